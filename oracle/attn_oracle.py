@@ -1,0 +1,178 @@
+"""Float64 CPU oracle for causal self-attention with rotary positions and shared K/V heads.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct reference that the
+GPU path is checked against.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it; the product path never calls it and shares no code with it.
+
+Everything is computed in numpy float64 and follows the plain definition, step by step:
+
+  1. rotary embedding (half-split "rotate_half" form) on q and k, never on v;
+  2. scores = q_rot . k_rot^T / sqrt(head_dim);
+  3. causal mask: a key later than the query gets -inf added to its score;
+  4. softmax over keys with the row maximum subtracted first;
+  5. out = softmax(scores) . v;
+  6. lse = row max + ln(sum of exp(score - row max))  (natural log of the softmax denominator).
+
+Sources (the pages this oracle follows):
+  * Picotron page "Picotron model implementation: Llama architecture and Flash Attention
+    integration", section 1 "embedding layer and positional encoding" -- apply_rotary_pos_emb
+    with rotate_half = cat(-x2, x1) over the two halves of head_dim, x*cos + rotate_half*sin;
+    section 2 "attention implementations" -- flash_attn_func(q, k, v, causal) on (B, S, H, D).
+  * PaLM page "PaLM teaching implementation in ColossalAI", section 2.3 RotaryEmbedding --
+    inv_freq = 1 / base^(arange(0, dim, 2) / dim), freqs = positions (outer) inv_freq,
+    cat(freqs, freqs); applied to q and k only.  Section 2.5 Attention -- multi-query
+    attention (one shared K/V head), causal mask on the upper triangle, row max subtracted
+    before the softmax.
+  * llama3-from-scratch page "parallel computing architecture": "attention score matrix"
+    (q_rot @ k_rot.T / head_dim**0.5), "causal mask" (full(-inf) then triu(diagonal=1),
+    added to the scores), "softmax" (over the key axis), "key-value sharing" (n_kv_heads=8
+    for n_heads=32: every 4 query heads share one K/V head).
+
+Readings where the pages are silent or disagree (each also listed in the design notes):
+  * RoPE pairing: half-split (Picotron and PaLM pages); the llama3 page's adjacent-pair
+    complex form is the same rotation under a fixed permutation of head_dim and is used
+    only as a cross-check in the tests.
+  * Positions are 0..S-1 for every batch row.
+  * GQA grouping is contiguous: query head h reads K/V head h // (Hq // Hkv).
+  * lse is the natural-log logsumexp of the scaled scores over the visible keys.
+"""
+
+import numpy as np
+
+__all__ = [
+    "rope_frequencies",
+    "rope_angles",
+    "rotate_half",
+    "apply_rope",
+    "causal_mask",
+    "softmax_rows",
+    "kv_head_of",
+    "attention_weights",
+    "attention",
+]
+
+
+def rope_frequencies(head_dim, rope_theta):
+    """Per-pair angular frequency theta_i = rope_theta ** (-2i / head_dim), i < head_dim/2.
+
+    PaLM page, section 2.3 RotaryEmbedding: 1 / base ** (arange(0, dim, 2) / dim).
+    The llama3 page builds the same numbers as 1 / rope_theta ** (arange(64) / 64) for
+    head_dim 128.
+    """
+    i2 = np.arange(0, head_dim, 2, dtype=np.float64)
+    return 1.0 / (np.float64(rope_theta) ** (i2 / np.float64(head_dim)))
+
+
+def rope_angles(positions, head_dim, rope_theta):
+    """Angle table (len(positions), head_dim): outer(positions, freqs) duplicated over both halves.
+
+    PaLM page, section 2.3: freqs = positions x inv_freq, then cat((freqs, freqs), -1), so
+    element c and element c + head_dim/2 share the angle of pair c.
+    """
+    freqs = np.outer(np.asarray(positions, dtype=np.float64), rope_frequencies(head_dim, rope_theta))
+    return np.concatenate([freqs, freqs], axis=-1)
+
+
+def rotate_half(x):
+    """cat(-x2, x1) where x1, x2 are the first and second halves of the last axis.
+
+    Picotron page, section 1 (apply_rotary_pos_emb).
+    """
+    half = x.shape[-1] // 2
+    return np.concatenate([-x[..., half:], x[..., :half]], axis=-1)
+
+
+def apply_rope(x, positions, rope_theta):
+    """Rotate x of shape (B, len(positions), H, head_dim) by the angles of `positions`.
+
+    Picotron page, section 1: x * cos + rotate_half(x) * sin, with cos/sin of the angle
+    table broadcast over batch and heads.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ang = rope_angles(positions, x.shape[-1], rope_theta)
+    cos = np.cos(ang)[None, :, None, :]
+    sin = np.sin(ang)[None, :, None, :]
+    return x * cos + rotate_half(x) * sin
+
+
+def causal_mask(query_positions, n_keys):
+    """Additive mask (len(query_positions), n_keys): 0 where key j <= query i, -inf where j > i.
+
+    llama3 page, "causal mask": full(-inf) followed by triu(diagonal=1), added to the scores.
+    Written for an arbitrary set of query positions so single rows can be evaluated alone.
+    """
+    j = np.arange(n_keys)
+    i = np.asarray(query_positions)
+    return np.where(j[None, :] > i[:, None], -np.inf, 0.0)
+
+
+def softmax_rows(scores):
+    """Numerically stable softmax along the last axis; also returns the row max and row sum.
+
+    PaLM page, section 2.5: subtract the row maximum, then softmax.
+    Returns (P, m, l) with P = exp(scores - m) / l, m = row max, l = sum exp(scores - m).
+    """
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, m[..., 0], l[..., 0]
+
+
+def kv_head_of(h, n_q_heads, n_kv_heads):
+    """K/V head read by query head h: contiguous groups of Hq/Hkv query heads.
+
+    llama3 page, "key-value sharing": every 4 query heads share one K/V head (32 over 8);
+    PaLM page, section 2.5: a single K/V head shared by every query head.
+    """
+    if n_q_heads % n_kv_heads != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    return h // (n_q_heads // n_kv_heads)
+
+
+def attention_weights(q_rot, k_rot, query_positions, causal):
+    """Softmax weights for one (batch, head): q_rot (R, d) at query_positions, k_rot (S, d).
+
+    llama3 page, "attention score matrix": scores = q_rot @ k_rot.T / head_dim ** 0.5;
+    "causal mask": add the mask; "softmax": over the key axis.
+    Returns (P, m, l) as softmax_rows does.
+    """
+    d = q_rot.shape[-1]
+    scores = (q_rot @ k_rot.T) / np.sqrt(np.float64(d))
+    if causal:
+        scores = scores + causal_mask(query_positions, k_rot.shape[0])
+    return softmax_rows(scores)
+
+
+def attention(q, k, v, rope_theta, causal=True, rows=None):
+    """Causal (or full) RoPE attention with shared K/V heads, in float64.
+
+    q: (B, S, Hq, d); k, v: (B, S, Hkv, d); Hq a multiple of Hkv; d even.
+    rows: optional 1-D array of query positions to evaluate (default: all S rows).  Each
+    output row depends only on its own query and the keys, so evaluating a subset is the
+    same definition restricted to those rows.
+
+    Returns (out, lse): out (B, R, Hq, d) float64 and lse (B, Hq, R) float64, R = len(rows).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be (B, S, Hkv, d) with q's B, S and d")
+    if d % 2 != 0:
+        raise ValueError("head_dim must be even for the half-split rotation")
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+
+    q_rot = apply_rope(q[:, rows], rows, rope_theta)
+    k_rot = apply_rope(k, np.arange(S), rope_theta)
+
+    out = np.empty((B, len(rows), Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, len(rows)), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            P, m, l = attention_weights(q_rot[b, :, h, :], k_rot[b, :, g, :], rows, causal)
+            out[b, :, h, :] = P @ v[b, :, g, :]
+            lse[b, h, :] = m + np.log(l)
+    return out, lse

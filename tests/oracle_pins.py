@@ -1,0 +1,367 @@
+"""Pins that tie the float64 oracle to facts outside itself.
+
+Each pin raises AssertionError on failure.  They are plain functions so that the mutation
+test can run the whole set against deliberately broken copies of the oracle and show that
+every plausible slip is caught by at least one of them.
+
+What each pin rests on:
+  * brute force      -- an independent pure-Python evaluation on tiny shapes (bruteforce.py);
+  * softmax facts    -- rows of the weights sum to 1; weights of future keys are exactly 0;
+  * closed forms     -- row 0 sees only key 0 (out = v_0, lse = q_0.k_0/sqrt(d) since the
+                        rotation at position 0 is the identity); q = 0 gives uniform weights
+                        (out_i = mean of v_0..v_i, lse_i = ln(i+1)); constant v gives that
+                        constant; a strongly dominant diagonal gives out_i = v_i;
+  * GQA              -- equals plain MHA on K/V heads repeated G times (contiguous groups);
+  * rotation facts   -- norm preserved, dot products depend only on the position difference,
+                        identity at position 0, d=2 is the textbook 2x2 rotation by p radians,
+                        frequencies agree with the llama3 page's 1/theta**(arange(64)/64);
+  * library routines -- torch's scaled_dot_product_attention (float64, CPU) on rotated q/k,
+                        scipy's logsumexp for lse;
+  * other page form  -- the llama3 page's adjacent-pair complex rotation equals the
+                        half-split rotation after a fixed permutation of head_dim;
+  * lse meaning      -- two disjoint key sets merged by logaddexp reproduce the full result;
+  * golden fixtures  -- hand-derived closed-form cases in tests/golden/.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+import bruteforce
+from oracle import attn_oracle as O
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- brute force
+BRUTE_CASES = [
+    # (B, S, Hq, Hkv, d, causal, rope_theta)
+    (1, 1, 1, 1, 2, True, 10000.0),
+    (1, 5, 2, 1, 4, True, 10000.0),
+    (2, 6, 4, 2, 8, True, 100.0),
+    (1, 7, 3, 3, 4, False, 10000.0),
+    (1, 8, 4, 1, 8, False, 500000.0),
+    (1, 6, 4, 4, 2, True, 3.0),
+    (1, 8, 2, 2, 6, True, 50.0),
+]
+
+
+def pin_bruteforce():
+    rng = np.random.default_rng(11)
+    for (B, S, Hq, Hkv, d, causal, theta) in BRUTE_CASES:
+        q = _rand(rng, B, S, Hq, d, scale=0.7)
+        k = _rand(rng, B, S, Hkv, d, scale=0.7)
+        v = _rand(rng, B, S, Hkv, d)
+        out_b, lse_b = bruteforce.brute_attention(q.tolist(), k.tolist(), v.tolist(), theta, causal)
+        out_o, lse_o = O.attention(q, k, v, theta, causal=causal)
+        case = f"brute force {(B, S, Hq, Hkv, d, causal, theta)}"
+        _close(out_o, out_b, 1e-12, case + " out")
+        _close(lse_o, lse_b, 1e-12, case + " lse")
+
+
+# ---------------------------------------------------------------- softmax facts
+def _rotated(rng, B=1, S=48, Hq=4, Hkv=2, d=16, theta=10000.0):
+    q = _rand(rng, B, S, Hq, d)
+    k = _rand(rng, B, S, Hkv, d)
+    pos = np.arange(S)
+    return O.apply_rope(q, pos, theta), O.apply_rope(k, pos, theta)
+
+
+def pin_rows_sum_to_one():
+    rng = np.random.default_rng(12)
+    qr, kr = _rotated(rng)
+    S = qr.shape[1]
+    for causal in (True, False):
+        P, _, _ = O.attention_weights(qr[0, :, 0], kr[0, :, 0], np.arange(S), causal)
+        _close(P.sum(axis=-1), np.ones(S), 1e-12, f"row sums (causal={causal})")
+        assert np.all(P >= 0.0), "negative softmax weight"
+
+
+def pin_masked_exact_zero():
+    rng = np.random.default_rng(13)
+    qr, kr = _rotated(rng)
+    S = qr.shape[1]
+    P, _, _ = O.attention_weights(qr[0, :, 1], kr[0, :, 0], np.arange(S), True)
+    future = np.triu(np.ones((S, S), dtype=bool), k=1)
+    assert np.all(P[future] == 0.0), "a future key got non-zero weight"
+    assert np.all(P[~future] > 0.0), "a visible key got zero weight"
+    # Evaluating a subset of rows gives the same weights as the full matrix.
+    rows = np.array([0, 5, S - 1])
+    Pr, _, _ = O.attention_weights(qr[0, rows, 1], kr[0, :, 0], rows, True)
+    _close(Pr, P[rows], 1e-15, "row subset of weights")
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_row0_closed_form():
+    rng = np.random.default_rng(14)
+    B, S, Hq, Hkv, d = 2, 9, 4, 2, 8
+    q = _rand(rng, B, S, Hq, d)
+    k = _rand(rng, B, S, Hkv, d)
+    v = _rand(rng, B, S, Hkv, d)
+    out, lse = O.attention(q, k, v, 10000.0, causal=True)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        _close(out[:, 0, h], v[:, 0, g], 1e-14, "row 0 out = v_0")
+        _close(lse[:, h, 0], np.sum(q[:, 0, h] * k[:, 0, g], axis=-1) / math.sqrt(d), 1e-13,
+               "row 0 lse = q_0.k_0/sqrt(d)")
+
+
+def pin_zero_query():
+    rng = np.random.default_rng(15)
+    B, S, Hq, Hkv, d = 1, 12, 2, 1, 8
+    q = np.zeros((B, S, Hq, d))
+    k = _rand(rng, B, S, Hkv, d)
+    v = _rand(rng, B, S, Hkv, d)
+    out, lse = O.attention(q, k, v, 10000.0, causal=True)
+    cummean = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, S + 1)[:, None]
+    for h in range(Hq):
+        _close(out[0, :, h], cummean, 1e-13, "q=0 causal out = running mean of v")
+        _close(lse[0, h], np.log(np.arange(1, S + 1)), 1e-13, "q=0 causal lse = ln(i+1)")
+    out, lse = O.attention(q, k, v, 10000.0, causal=False)
+    _close(out[0, :, 0], np.broadcast_to(v[0, :, 0].mean(axis=0), (S, d)), 1e-13, "q=0 full out = mean v")
+    _close(lse[0, 0], np.full(S, math.log(S)), 1e-13, "q=0 full lse = ln S")
+
+
+def pin_constant_v():
+    rng = np.random.default_rng(16)
+    B, S, Hq, Hkv, d = 2, 10, 4, 2, 8
+    q = _rand(rng, B, S, Hq, d)
+    k = _rand(rng, B, S, Hkv, d)
+    c = _rand(rng, B, 1, Hkv, d)
+    v = np.broadcast_to(c, (B, S, Hkv, d)).copy()
+    out, _ = O.attention(q, k, v, 10000.0, causal=True)
+    G = Hq // Hkv
+    for h in range(Hq):
+        _close(out[:, :, h], np.broadcast_to(c[:, :, h // G], (B, S, d)), 1e-13, "constant v")
+
+
+def pin_diagonal_dominance():
+    rng = np.random.default_rng(17)
+    B, S, H, d = 1, 16, 1, 8
+    u = _rand(rng, B, S, H, d)
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    q = 40.0 * u
+    k = 40.0 * u
+    v = _rand(rng, B, S, H, d)
+    out, _ = O.attention(q, k, v, 10000.0, causal=True)
+    _close(out, v, 1e-9, "dominant diagonal picks v_i")
+
+
+# ---------------------------------------------------------------- GQA
+def pin_gqa_repeat():
+    rng = np.random.default_rng(18)
+    B, S, d = 1, 14, 8
+    for (Hq, Hkv) in ((6, 2), (4, 1), (4, 4), (8, 2)):
+        q = _rand(rng, B, S, Hq, d)
+        k = _rand(rng, B, S, Hkv, d)
+        v = _rand(rng, B, S, Hkv, d)
+        G = Hq // Hkv
+        out, lse = O.attention(q, k, v, 10000.0, causal=True)
+        out_m, lse_m = O.attention(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), 10000.0, causal=True)
+        _close(out, out_m, 1e-14, f"GQA {Hq}/{Hkv} vs repeated-head MHA out")
+        _close(lse, lse_m, 1e-14, f"GQA {Hq}/{Hkv} vs repeated-head MHA lse")
+
+
+# ---------------------------------------------------------------- rotation facts
+def pin_rope_norm():
+    rng = np.random.default_rng(19)
+    x = _rand(rng, 2, 33, 3, 16)
+    for theta in (10000.0, 500000.0):
+        xr = O.apply_rope(x, np.arange(33), theta)
+        _close(np.linalg.norm(xr, axis=-1), np.linalg.norm(x, axis=-1), 1e-12, "rotation keeps norm")
+        xr = O.apply_rope(x[:, :1], np.array([32767]), theta)
+        _close(np.linalg.norm(xr, axis=-1), np.linalg.norm(x[:, :1], axis=-1), 1e-12, "norm at p=32767")
+
+
+def pin_rope_relative():
+    rng = np.random.default_rng(20)
+    d = 16
+    q = _rand(rng, 1, 1, 1, d)
+    k = _rand(rng, 1, 1, 1, d)
+    for theta in (10000.0, 500000.0):
+        for (p, pk) in ((3, 1), (0, 7), (100, 100), (2047, 5)):
+            ref = np.sum(O.apply_rope(q, [p], theta) * O.apply_rope(k, [pk], theta))
+            for t in (1, 17, 1000, 30000):
+                got = np.sum(O.apply_rope(q, [p + t], theta) * O.apply_rope(k, [pk + t], theta))
+                assert abs(got - ref) <= 1e-10 * (1 + abs(ref)), "q.k depends on more than p - p'"
+            # and it does depend on the difference
+            other = np.sum(O.apply_rope(q, [p + 1], theta) * O.apply_rope(k, [pk], theta))
+            assert abs(other - ref) > 1e-9, "rotation had no effect on q.k"
+
+
+def pin_rope_identity():
+    rng = np.random.default_rng(21)
+    x = _rand(rng, 2, 1, 3, 8)
+    assert np.array_equal(O.apply_rope(x, [0], 10000.0), x), "rotation at position 0 is not the identity"
+
+
+def pin_rope_d2_textbook():
+    # For head_dim 2 the single frequency is theta**0 = 1, so position p rotates by p radians.
+    rng = np.random.default_rng(22)
+    x = _rand(rng, 1, 1, 1, 2)
+    for p in (1, 2, 5, 1000):
+        R = np.array([[math.cos(p), -math.sin(p)], [math.sin(p), math.cos(p)]])
+        got = O.apply_rope(x, [p], 12345.0)[0, 0, 0]
+        _close(got, R @ x[0, 0, 0], 1e-12, f"d=2 textbook rotation at p={p}")
+
+
+def pin_rope_frequencies_llama3():
+    # llama3 page, "RoPE principle": 1/rope_theta**(arange(64)/64) for head_dim 128.
+    for theta in (10000.0, 500000.0):
+        ref = np.array([1.0 / theta ** (i / 64.0) for i in range(64)])
+        _close(O.rope_frequencies(128, theta), ref, 1e-15, "frequencies vs the llama3 page")
+
+
+# ---------------------------------------------------------------- library routines
+def pin_sdpa():
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(23)
+    B, S, Hq, Hkv, d = 2, 37, 6, 2, 16
+    q = _rand(rng, B, S, Hq, d)
+    k = _rand(rng, B, S, Hkv, d)
+    v = _rand(rng, B, S, Hkv, d)
+    G = Hq // Hkv
+    pos = np.arange(S)
+    qr = torch.from_numpy(O.apply_rope(q, pos, 500000.0)).permute(0, 2, 1, 3)
+    kr = torch.from_numpy(O.apply_rope(k, pos, 500000.0)).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    for causal in (True, False):
+        ref = F.scaled_dot_product_attention(qr, kr, vt, is_causal=causal).permute(0, 2, 1, 3).numpy()
+        out, _ = O.attention(q, k, v, 500000.0, causal=causal)
+        _close(out, ref, 1e-12, f"SDPA float64 (causal={causal})")
+
+
+def pin_lse_scipy():
+    from scipy.special import logsumexp
+
+    rng = np.random.default_rng(24)
+    B, S, Hq, Hkv, d = 1, 29, 4, 1, 8
+    q = _rand(rng, B, S, Hq, d, scale=2.0)
+    k = _rand(rng, B, S, Hkv, d, scale=2.0)
+    v = _rand(rng, B, S, Hkv, d)
+    pos = np.arange(S)
+    qr = O.apply_rope(q, pos, 10000.0)
+    kr = O.apply_rope(k, pos, 10000.0)
+    for causal in (True, False):
+        _, lse = O.attention(q, k, v, 10000.0, causal=causal)
+        for h in range(Hq):
+            sc = np.einsum("ic,jc->ij", qr[0, :, h], kr[0, :, 0]) / math.sqrt(d)
+            if causal:
+                sc = np.where(np.tril(np.ones((S, S), dtype=bool)), sc, -np.inf)
+            _close(lse[0, h], logsumexp(sc, axis=-1), 1e-12, f"lse vs scipy (causal={causal})")
+
+
+# ---------------------------------------------------------------- other page's form
+def _llama3_complex_rotate(x, positions, rope_theta):
+    # llama3 page, "parallel rotation of queries and keys": adjacent pairs viewed as complex
+    # numbers times polar(1, p * freq), freq = 1/rope_theta**(arange(d/2)/(d/2)).
+    d = x.shape[-1]
+    freqs = 1.0 / rope_theta ** (np.arange(d // 2) / (d // 2))
+    ang = np.outer(positions, freqs)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * ang)[None, :, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+def pin_interleaved_equivalence():
+    rng = np.random.default_rng(25)
+    B, S, Hq, Hkv, d = 1, 20, 4, 2, 16
+    q = _rand(rng, B, S, Hq, d)
+    k = _rand(rng, B, S, Hkv, d)
+    v = _rand(rng, B, S, Hkv, d)
+    theta = 500000.0
+    pos = np.arange(S)
+    qi = _llama3_complex_rotate(q, pos, theta)
+    ki = _llama3_complex_rotate(k, pos, theta)
+    G = Hq // Hkv
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    out_h, lse_h = O.attention(q[..., perm], k[..., perm], v, theta, causal=True)
+    for h in range(Hq):
+        g = h // G
+        sc = qi[0, :, h] @ ki[0, :, g].T / math.sqrt(d)
+        sc = np.where(np.tril(np.ones((S, S), dtype=bool)), sc, -np.inf)
+        m = sc.max(axis=-1, keepdims=True)
+        e = np.exp(sc - m)
+        _close(out_h[0, :, h], (e / e.sum(-1, keepdims=True)) @ v[0, :, g], 1e-12,
+               "interleaved complex form vs permuted half-split (out)")
+        _close(lse_h[0, h], (m[:, 0] + np.log(e.sum(-1))), 1e-12,
+               "interleaved complex form vs permuted half-split (lse)")
+
+
+# ---------------------------------------------------------------- lse meaning
+def pin_lse_merge():
+    rng = np.random.default_rng(26)
+    S, d = 40, 8
+    qr, kr = _rotated(rng, S=S, d=d)
+    v = _rand(rng, S, d)
+    rows = np.arange(S)
+    P, m, l = O.attention_weights(qr[0, :, 0], kr[0, :, 0], rows, False)
+    full_out = P @ v
+    full_lse = m + np.log(l)
+    split = rng.permutation(S)
+    a, b = split[:17], split[17:]
+    Pa, ma, la = O.attention_weights(qr[0, :, 0], kr[0, a, 0], rows, False)
+    Pb, mb, lb = O.attention_weights(qr[0, :, 0], kr[0, b, 0], rows, False)
+    lse_a, lse_b = ma + np.log(la), mb + np.log(lb)
+    lse = np.logaddexp(lse_a, lse_b)
+    out = np.exp(lse_a - lse)[:, None] * (Pa @ v[a]) + np.exp(lse_b - lse)[:, None] * (Pb @ v[b])
+    _close(lse, full_lse, 1e-12, "merged lse")
+    _close(out, full_out, 1e-12, "merged out")
+
+
+# ---------------------------------------------------------------- golden fixtures
+def pin_golden():
+    path = os.path.join(GOLDEN_DIR, "closed_form_cases.json")
+    with open(path, "r", encoding="utf-8") as f:
+        cases = json.load(f)["cases"]
+    assert cases, "no golden cases"
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float64)
+        k = np.array(c["k"], dtype=np.float64)
+        v = np.array(c["v"], dtype=np.float64)
+        out, lse = O.attention(q, k, v, c["rope_theta"], causal=c["causal"])
+        _close(out, np.array(c["out"]), 1e-14, f"golden {c['name']} out")
+        _close(lse, np.array(c["lse"]), 1e-14, f"golden {c['name']} lse")
+
+
+ALL_PINS = [
+    pin_bruteforce,
+    pin_rows_sum_to_one,
+    pin_masked_exact_zero,
+    pin_row0_closed_form,
+    pin_zero_query,
+    pin_constant_v,
+    pin_diagonal_dominance,
+    pin_gqa_repeat,
+    pin_rope_norm,
+    pin_rope_relative,
+    pin_rope_identity,
+    pin_rope_d2_textbook,
+    pin_rope_frequencies_llama3,
+    pin_sdpa,
+    pin_lse_scipy,
+    pin_interleaved_equivalence,
+    pin_lse_merge,
+    pin_golden,
+]

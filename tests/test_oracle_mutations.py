@@ -1,0 +1,180 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins catch every one.
+
+Each mutation replaces one oracle function by a subtly wrong version -- a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one -- and the test asserts that at
+least one pin in oracle_pins fails.  This is what shows the pins constrain the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import attn_oracle as O
+
+
+def _rotate_half_wrong_sign(x):
+    half = x.shape[-1] // 2
+    return np.concatenate([x[..., half:], -x[..., :half]], axis=-1)
+
+
+def _rotate_half_swapped_halves(x):
+    half = x.shape[-1] // 2
+    return np.concatenate([-x[..., :half], x[..., half:]], axis=-1)
+
+
+def _freq_missing_two(head_dim, rope_theta):
+    i = np.arange(0, head_dim // 2, dtype=np.float64)
+    return 1.0 / (np.float64(rope_theta) ** (i / head_dim))
+
+
+def _freq_wrong_sign(head_dim, rope_theta):
+    i2 = np.arange(0, head_dim, 2, dtype=np.float64)
+    return np.float64(rope_theta) ** (i2 / head_dim)
+
+
+def _angles_interleaved_dup(positions, head_dim, rope_theta):
+    freqs = np.outer(np.asarray(positions, dtype=np.float64), O.rope_frequencies(head_dim, rope_theta))
+    return np.repeat(freqs, 2, axis=-1)
+
+
+def _apply_rope_cos_sin_swapped(x, positions, rope_theta):
+    x = np.asarray(x, dtype=np.float64)
+    ang = O.rope_angles(positions, x.shape[-1], rope_theta)
+    return x * np.sin(ang)[None, :, None, :] + O.rotate_half(x) * np.cos(ang)[None, :, None, :]
+
+
+def _apply_rope_positions_plus_one(x, positions, rope_theta):
+    x = np.asarray(x, dtype=np.float64)
+    ang = O.rope_angles(np.asarray(positions) + 1, x.shape[-1], rope_theta)
+    return x * np.cos(ang)[None, :, None, :] + O.rotate_half(x) * np.sin(ang)[None, :, None, :]
+
+
+def _mask_includes_diagonal(query_positions, n_keys):
+    j = np.arange(n_keys)
+    i = np.asarray(query_positions)
+    return np.where(j[None, :] >= i[:, None], -np.inf, 0.0)
+
+
+def _mask_reversed(query_positions, n_keys):
+    j = np.arange(n_keys)
+    i = np.asarray(query_positions)
+    return np.where(j[None, :] < i[:, None], -np.inf, 0.0)
+
+
+def _mask_off_by_one(query_positions, n_keys):
+    j = np.arange(n_keys)
+    i = np.asarray(query_positions)
+    return np.where(j[None, :] > i[:, None] + 1, -np.inf, 0.0)
+
+
+def _softmax_wrong_axis(scores):
+    m = scores.max(axis=0, keepdims=True)
+    e = np.exp(scores - m)
+    l = e.sum(axis=0, keepdims=True)
+    P = e / l
+    mm = scores.max(axis=-1)
+    return P, mm, np.exp(scores - mm[:, None]).sum(-1)
+
+
+def _softmax_no_normalise(scores):
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e, m[..., 0], l[..., 0]
+
+
+def _kv_head_modulo(h, n_q_heads, n_kv_heads):
+    return h % n_kv_heads
+
+
+def _weights_scale_by_d(q_rot, k_rot, query_positions, causal):
+    d = q_rot.shape[-1]
+    scores = (q_rot @ k_rot.T) / np.float64(d)
+    if causal:
+        scores = scores + O.causal_mask(query_positions, k_rot.shape[0])
+    return O.softmax_rows(scores)
+
+
+def _weights_no_scale(q_rot, k_rot, query_positions, causal):
+    scores = q_rot @ k_rot.T
+    if causal:
+        scores = scores + O.causal_mask(query_positions, k_rot.shape[0])
+    return O.softmax_rows(scores)
+
+
+def _weights_ignore_causal(q_rot, k_rot, query_positions, causal):
+    d = q_rot.shape[-1]
+    return O.softmax_rows((q_rot @ k_rot.T) / np.sqrt(np.float64(d)))
+
+
+def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, unrotated_k=False):
+    def attention(q, k, v, rope_theta, causal=True, rows=None):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        B, S, Hq, d = q.shape
+        Hkv = k.shape[2]
+        rows = np.arange(S) if rows is None else np.asarray(rows)
+        q_rot = O.apply_rope(q[:, rows], rows, rope_theta)
+        k_rot = k if unrotated_k else O.apply_rope(k, np.arange(S), rope_theta)
+        vv = O.apply_rope(v, np.arange(S), rope_theta) if rope_v else v
+        out = np.empty((B, len(rows), Hq, d))
+        lse = np.empty((B, Hq, len(rows)))
+        for b in range(B):
+            for h in range(Hq):
+                g = O.kv_head_of(h, Hq, Hkv)
+                P, m, l = O.attention_weights(q_rot[b, :, h], k_rot[b, :, g], rows, causal)
+                if transpose_p and P.shape[0] == P.shape[1]:
+                    P = P.T
+                out[b, :, h] = P @ vv[b, :, g]
+                lse[b, h] = np.log(l) if lse_drops_max else m + np.log(l)
+        return out, lse
+
+    return attention
+
+
+MUTATIONS = {
+    "rotate_half_wrong_sign": ("rotate_half", _rotate_half_wrong_sign),
+    "rotate_half_swapped_halves": ("rotate_half", _rotate_half_swapped_halves),
+    "frequencies_missing_factor_two": ("rope_frequencies", _freq_missing_two),
+    "frequencies_wrong_sign": ("rope_frequencies", _freq_wrong_sign),
+    "angles_interleaved_duplication": ("rope_angles", _angles_interleaved_dup),
+    "rope_cos_sin_swapped": ("apply_rope", _apply_rope_cos_sin_swapped),
+    "rope_positions_off_by_one": ("apply_rope", _apply_rope_positions_plus_one),
+    "mask_includes_diagonal": ("causal_mask", _mask_includes_diagonal),
+    "mask_reversed": ("causal_mask", _mask_reversed),
+    "mask_off_by_one": ("causal_mask", _mask_off_by_one),
+    "softmax_wrong_axis": ("softmax_rows", _softmax_wrong_axis),
+    "softmax_not_normalised": ("softmax_rows", _softmax_no_normalise),
+    "gqa_modulo_grouping": ("kv_head_of", _kv_head_modulo),
+    "scale_one_over_d": ("attention_weights", _weights_scale_by_d),
+    "scale_dropped": ("attention_weights", _weights_no_scale),
+    "causal_flag_ignored": ("attention_weights", _weights_ignore_causal),
+    "lse_drops_row_max": ("attention", _attention_variant(lse_drops_max=True)),
+    "rope_applied_to_v": ("attention", _attention_variant(rope_v=True)),
+    "weights_transposed": ("attention", _attention_variant(transpose_p=True)),
+    "k_left_unrotated": ("attention", _attention_variant(unrotated_k=True)),
+}
+
+
+def _failing_pins():
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception:  # AssertionError, or a crash the slip causes
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = _failing_pins()
+    assert failed, f"mutation {name} passed every pin"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failing_pins() == []
