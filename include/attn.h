@@ -1,0 +1,115 @@
+/*
+ * attn.h -- C ABI of a fused causal self-attention forward for AMD MI355X (gfx950).
+ *
+ * One call computes, for every batch row b, query head h and query position i:
+ *
+ *   q' = RoPE(q[b,i,h,:], i),  k'_j = RoPE(k[b,j,g,:], j),  g = h / (Hq / Hkv)
+ *   s_j = q' . k'_j / sqrt(d)           for the visible keys j (j <= i when causal)
+ *   out[b,i,h,:] = sum_j softmax(s)_j * v[b,j,g,:]
+ *   lse[b,h,i]   = ln sum_j exp(s_j)    (natural log, float32)
+ *
+ * Definitions followed:
+ *   - rotary embedding, half-split form: x*cos + rotate_half(x)*sin with
+ *     rotate_half(x) = cat(-x2, x1) over the two halves of head_dim
+ *     (Picotron page "Llama architecture and Flash Attention integration", section 1),
+ *     frequencies rope_theta^(-2i/d), i < d/2, angle = position * frequency, applied to q
+ *     and k only (PaLM-in-ColossalAI page, section 2.3 RotaryEmbedding);
+ *   - scores scaled by 1/sqrt(head_dim), causal mask on keys later than the query, row
+ *     softmax (llama3-from-scratch page: "attention score matrix", "causal mask",
+ *     "softmax"); the row maximum is subtracted before exponentiating (PaLM page, 2.5);
+ *   - grouped K/V heads: contiguous groups of Hq/Hkv query heads share one K/V head
+ *     (llama3 page, "key-value sharing": 32 query heads over 8 K/V heads); Hkv = 1 is
+ *     multi-query attention (PaLM page, section 2.5);
+ *   - the (B, S, H, D) tensor layout that flash_attn_func receives (Picotron page,
+ *     section 2); lse per (head, row) so sequence shards can be merged ring-attention
+ *     style (Picotron page, "context parallelism and ring attention").
+ *
+ * Threading and ownership: every buffer is allocated and owned by the caller; the library
+ * allocates no device memory and keeps no mutable global state, so concurrent calls on
+ * different streams are safe as long as their output and workspace buffers do not overlap.
+ * Calls are asynchronous: they enqueue work on `stream` and return without synchronising.
+ * Every argument is validated on the host before any HIP runtime call; on an error code
+ * nothing has been enqueued.  No C++ exception crosses this interface.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Element types of q, k, v and out. */
+#define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
+#define ATTN_DTYPE_FP32 1 /* float32 inputs/outputs; float32 arithmetic throughout */
+
+/* Return codes. */
+#define ATTN_OK 0
+#define ATTN_EINVAL (-1)       /* null or misaligned pointer, B/S/Hq/Hkv < 1, Hq % Hkv != 0,
+                                  rope_theta not finite or <= 0, causal not 0/1 */
+#define ATTN_EUNSUPPORTED (-2) /* head_dim not 64 or 128, unknown dtype, sizes too large */
+#define ATTN_EHIP (-3)         /* the HIP runtime rejected an event record or kernel launch */
+#define ATTN_EWORKSPACE (-4)   /* workspace pointer null while needed, or workspace too small */
+
+/* Version of this interface (ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* Static, human-readable text for a return code; never NULL. */
+const char *attn_strerror(int code);
+
+/*
+ * Bytes of device workspace attn_fwd needs for these sizes (0 when none is needed).
+ * For bf16 it holds the rotated keys, laid out (B, Hkv, S rounded up to 64, d) bf16.
+ * Returns 0 as well for arguments attn_fwd would reject.
+ */
+size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
+
+/*
+ * Fused RoPE + causal (or full) attention forward with grouped K/V heads.
+ *
+ *   q          device, (B, S, Hq, head_dim) contiguous, element type `dtype`, 16-byte aligned
+ *   k, v       device, (B, S, Hkv, head_dim) contiguous, same type, 16-byte aligned
+ *   B, S       batch rows and sequence length (>= 1); positions are 0 .. S-1 in every row
+ *   Hq, Hkv    query heads and K/V heads; Hq must be a multiple of Hkv
+ *   head_dim   64 or 128 (even, split into two rotation halves)
+ *   rope_theta rotary base (> 0, finite); frequencies rope_theta^(-2i/head_dim)
+ *   causal     1: key j is visible to query i iff j <= i;  0: every key is visible
+ *   dtype      ATTN_DTYPE_BF16 or ATTN_DTYPE_FP32
+ *   out        device, (B, S, Hq, head_dim) contiguous, type `dtype`, 16-byte aligned;
+ *              fully overwritten; must not overlap the inputs
+ *   lse        device, (B, Hq, S) float32; fully overwritten
+ *   workspace  device scratch of at least attn_fwd_workspace_bytes(...) bytes, 16-byte
+ *              aligned (may be NULL when that size is 0); its contents on entry are
+ *              ignored and on return are unspecified
+ *   stream     hipStream_t to enqueue on; NULL means the default stream
+ *
+ * Returns ATTN_OK or one of the error codes above.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+             int head_dim, double rope_theta, int causal, int dtype, void *out, float *lse,
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same as attn_fwd, and additionally records `ev_start` on `stream` immediately before the
+ * attention kernel and `ev_stop` immediately after it (the key-rotation pre-pass, when there
+ * is one, runs before ev_start).  Events come from attn_event_create.  For benchmarking.
+ */
+int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                   int head_dim, double rope_theta, int causal, int dtype, void *out,
+                   float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                   void *ev_start, void *ev_stop);
+
+/* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */
+void *attn_event_create(void);
+int attn_event_destroy(void *ev);
+/* Milliseconds between two recorded events; waits for `stop` to complete. */
+int attn_event_elapsed_ms(void *start, void *stop, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

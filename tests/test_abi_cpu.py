@@ -1,0 +1,102 @@
+"""The C ABI library on a machine without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented codes before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_causal_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_strerror", "attn_abi_version", "attn_fwd_workspace_bytes"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_version_and_strerror():
+    assert _lib.abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert len(_lib.strerror(code)) > 5
+    assert "unknown" in _lib.strerror(12345)
+
+
+def test_workspace_bytes():
+    # bf16: rotated keys (B, Hkv, S rounded up to 64, D) in bf16
+    assert _lib.workspace_bytes(1, 2048, 8, 128, 0) == 1 * 8 * 2048 * 128 * 2
+    assert _lib.workspace_bytes(2, 100, 3, 64, 0) == 2 * 3 * 128 * 64 * 2
+    assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 64 * 64 * 2
+    assert _lib.workspace_bytes(1, 64, 1, 64, 1) == 0  # fp32 needs none
+    assert _lib.workspace_bytes(1, 64, 1, 96, 0) == 0  # unsupported -> 0
+    assert _lib.workspace_bytes(0, 64, 1, 64, 0) == 0
+
+
+# Fake, aligned, non-null "device pointers": every call below must be rejected on the host
+# before any HIP call, so they are never dereferenced.
+P = 0x10000
+
+
+def call(**over):
+    a = dict(q=P, k=P, v=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=10000.0, causal=1, dtype=0,
+             out=P, lse=P, ws=P, wsb=1 << 30, stream=None)
+    a.update(over)
+    return _lib.fwd_raw(a["q"], a["k"], a["v"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"],
+                        a["causal"], a["dtype"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(q=None), dict(k=None), dict(v=None), dict(out=None), dict(lse=None),
+    dict(q=P + 8), dict(k=P + 2), dict(v=P + 4), dict(out=P + 1), dict(lse=P + 2),
+    dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(B=-3), dict(S=-1),
+    dict(Hq=6, Hkv=4), dict(Hq=3, Hkv=2),
+    dict(theta=0.0), dict(theta=-1.0), dict(theta=float("nan")), dict(theta=float("inf")),
+    dict(causal=2), dict(causal=-1),
+])
+def test_invalid_arguments(over):
+    assert call(**over) == _lib.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("over", [
+    dict(d=96), dict(d=256), dict(d=32), dict(d=0), dict(dtype=2), dict(dtype=-1),
+    dict(S=(1 << 28) + 1),
+])
+def test_unsupported(over):
+    assert call(**over) == _lib.ATTN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("over", [dict(ws=None), dict(wsb=1024), dict(ws=P + 8)])
+def test_workspace_rejected(over):
+    assert call(**over) == _lib.ATTN_EWORKSPACE
+
+
+def test_timed_variant_validates_too():
+    lib = _lib.load()
+    rc = lib.attn_fwd_timed(P, P, P, 1, 64, 4, 1, 96, 1e4, 1, 0, P, P, P, 1 << 30, None, None, None)
+    assert rc == _lib.ATTN_EUNSUPPORTED
+
+
+def test_event_helpers_reject_null():
+    lib = _lib.load()
+    assert lib.attn_event_destroy(None) == _lib.ATTN_EINVAL
+    ms = ctypes.c_float()
+    assert lib.attn_event_elapsed_ms(None, None, ctypes.byref(ms)) == _lib.ATTN_EINVAL

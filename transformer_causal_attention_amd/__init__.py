@@ -1,0 +1,23 @@
+"""Fused causal RoPE + grouped-query attention forward for AMD MI355X (gfx950).
+
+    out, lse = attn_fwd(q, k, v, rope_theta, causal=True)
+
+q: (B, S, Hq, D), k/v: (B, S, Hkv, D) contiguous CUDA (HIP) tensors, bfloat16 or float32,
+D in {64, 128}, Hq a multiple of Hkv.  Returns out (B, S, Hq, D) in the input dtype and
+lse (B, Hq, S) float32 (natural-log logsumexp of the scaled scores of each row).
+
+PyTorch only provides device memory and the stream; the computation runs in the HIP
+kernels behind the C ABI of libattn.so (include/attn.h).
+"""
+
+from ._lib import (  # noqa: F401
+    ATTN_DTYPE_BF16,
+    ATTN_DTYPE_FP32,
+    AttnError,
+    Event,
+    abi_version,
+    load,
+    strerror,
+    workspace_bytes,
+)
+from .api import attn_fwd, attn_fwd_into  # noqa: F401

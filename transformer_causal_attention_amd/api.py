@@ -1,0 +1,64 @@
+"""PyTorch-facing wrapper of attn_fwd: checks tensors, allocates outputs, passes pointers."""
+
+import torch
+
+from . import _lib
+
+_DTYPE_CODE = {torch.bfloat16: _lib.ATTN_DTYPE_BF16, torch.float32: _lib.ATTN_DTYPE_FP32}
+
+
+def _shapes(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D tensor (B, S, H, D)")
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype: bfloat16 or float32")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError(f"k and v must be (B, S, Hkv, D) = ({B}, {S}, Hkv, {D}); got {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    return B, S, Hq, Hkv, D
+
+
+def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=None, events=None):
+    """attn_fwd writing into caller-provided out (like q) and lse (B, Hq, S) float32.
+
+    workspace: optional uint8 GPU tensor of at least workspace_bytes(...) bytes.
+    stream: torch.cuda.Stream to enqueue on (default: the current stream).
+    events: optional (start, stop) pair of Event recorded around the attention kernel.
+    """
+    B, S, Hq, Hkv, D = _shapes(q, k, v)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, S)")
+    code = _DTYPE_CODE[q.dtype]
+    need = _lib.workspace_bytes(B, S, Hkv, D, code)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if stream is not None:
+            workspace.record_stream(st)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ev0, ev1 = (events[0].ptr, events[1].ptr) if events is not None else (None, None)
+    rc = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
+                      1 if causal else 0, code, out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
+                      st.cuda_stream, ev0, ev1)
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, events=None):
+    """Fused RoPE + causal GQA attention forward.  Returns (out, lse)."""
+    B, S, Hq, Hkv, D = _shapes(q, k, v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events)

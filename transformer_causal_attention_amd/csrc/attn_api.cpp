@@ -1,0 +1,192 @@
+// C ABI of the attention forward (declared in include/attn.h): host-side validation,
+// kernel selection and launch.  Every argument is checked before the first HIP runtime
+// call, so a rejected call enqueues nothing.
+
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_launch.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kTileKeys = 64;  // key tile of the bf16 kernel; rotated keys are padded to it
+
+size_t padded_len(int S) { return ((size_t)S + kTileKeys - 1) / kTileKeys * kTileKeys; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Query heads per workgroup: the largest of 4, 2, 1 dividing G (4 waves per workgroup).
+int heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
+int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int causal, int dtype) {
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP32) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  // index arithmetic in the kernels: row/key positions in int, offsets in size_t,
+  // workgroup counts below 2^31
+  if (S > (1 << 28)) return ATTN_EUNSUPPORTED;
+  const double elems = (double)B * S * Hq * d;
+  if (elems > 4.0e15) return ATTN_EUNSUPPORTED;
+  const double wgs = (double)B * Hq * ((double)S / 32.0 + 1.0) + (double)B * Hkv * (padded_len(S) / 256.0 + 1.0) * (d / 16);
+  if (wgs >= 2147483647.0) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn::RopeTable rope_table(int d, double rope_theta) {
+  attn::RopeTable t{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d / 2; ++i) t.rev[i] = std::pow(rope_theta, -(2.0 * i) / d) / two_pi;
+  return t;
+}
+
+float q_scale(int d) { return (float)(1.4426950408889634073599246810019 / std::sqrt((double)d)); }
+
+template <int D>
+hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                    const attn::RopeTable &tab, int causal, void *out, float *lse, void *ws,
+                    hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  attn::RopeKParams rp;
+  rp.k = static_cast<const __bf16 *>(k);
+  rp.kr = static_cast<__bf16 *>(ws);
+  rp.B = B;
+  rp.S = S;
+  rp.Hkv = Hkv;
+  rp.S_pad = (int)padded_len(S);
+  hipError_t err = attn::launch_rope_k<D>(rp, tab, st);
+  if (err != hipSuccess) return err;
+
+  attn::FwdParams p;
+  p.q = static_cast<const __bf16 *>(q);
+  p.kr = rp.kr;
+  p.v = static_cast<const __bf16 *>(v);
+  p.out = static_cast<__bf16 *>(out);
+  p.lse = lse;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.S_pad = rp.S_pad;
+  p.hpw = heads_per_wg(p.G);
+  p.n_units = B * Hkv * (p.G / p.hpw);
+  const int rows_per_wg = 32 * (4 / p.hpw);
+  p.n_row_blocks = (S + rows_per_wg - 1) / rows_per_wg;
+  p.q_scale = q_scale(D);
+
+  if (e0 && (err = hipEventRecord(e0, st)) != hipSuccess) return err;
+  err = causal ? attn::launch_attn_bf16<D, true>(p, tab, st) : attn::launch_attn_bf16<D, false>(p, tab, st);
+  if (err != hipSuccess) return err;
+  if (e1 && (err = hipEventRecord(e1, st)) != hipSuccess) return err;
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t run_f32(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                   const attn::RopeTable &tab, int causal, void *out, float *lse, hipStream_t st,
+                   hipEvent_t e0, hipEvent_t e1) {
+  attn::F32Params p;
+  p.q = static_cast<const float *>(q);
+  p.k = static_cast<const float *>(k);
+  p.v = static_cast<const float *>(v);
+  p.out = static_cast<float *>(out);
+  p.lse = lse;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.n_row_blocks = (S + 63) / 64;
+  p.q_scale = q_scale(D);
+  hipError_t err;
+  if (e0 && (err = hipEventRecord(e0, st)) != hipSuccess) return err;
+  err = causal ? attn::launch_attn_f32<D, true>(p, tab, st) : attn::launch_attn_f32<D, false>(p, tab, st);
+  if (err != hipSuccess) return err;
+  if (e1 && (err = hipEventRecord(e1, st)) != hipSuccess) return err;
+  return hipSuccess;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv, int d,
+             double rope_theta, int causal, int dtype, void *out, float *lse, void *workspace,
+             size_t workspace_bytes, void *stream, void *ev_start, void *ev_stop) {
+  if (!q || !k || !v || !out || !lse) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return ATTN_EINVAL;
+  const int rc = check_shape(B, S, Hq, Hkv, d, rope_theta, causal, dtype);
+  if (rc != ATTN_OK) return rc;
+  const size_t need = attn_fwd_workspace_bytes(B, S, Hkv, d, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_EWORKSPACE;
+
+  const attn::RopeTable tab = rope_table(d, rope_theta);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+  hipError_t err;
+  if (dtype == ATTN_DTYPE_BF16)
+    err = d == 64 ? run_bf16<64>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, workspace, st, e0, e1)
+                  : run_bf16<128>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, workspace, st, e0, e1);
+  else
+    err = d == 64 ? run_f32<64>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, st, e0, e1)
+                  : run_f32<128>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, st, e0, e1);
+  return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+ATTN_EXPORT const char *attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size, Hq not a multiple of Hkv, bad rope_theta or causal flag)";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, dtype bf16 or fp32, sizes within limits)";
+    case ATTN_EHIP: return "HIP runtime error while recording an event or launching a kernel";
+    case ATTN_EWORKSPACE: return "workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()";
+    default: return "unknown error code";
+  }
+}
+
+ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype) {
+  if (dtype != ATTN_DTYPE_BF16) return 0;
+  if (B < 1 || S < 1 || Hkv < 1 || (head_dim != 64 && head_dim != 128) || S > (1 << 28)) return 0;
+  return (size_t)B * Hkv * padded_len(S) * head_dim * 2;
+}
+
+ATTN_EXPORT int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                         int head_dim, double rope_theta, int causal, int dtype, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, workspace,
+                  workspace_bytes, stream, nullptr, nullptr);
+}
+
+ATTN_EXPORT int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                               int head_dim, double rope_theta, int causal, int dtype, void *out,
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                               void *ev_start, void *ev_stop) {
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, workspace,
+                  workspace_bytes, stream, ev_start, ev_stop);
+}
+
+ATTN_EXPORT void *attn_event_create(void) {
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+ATTN_EXPORT int attn_event_destroy(void *ev) {
+  if (!ev) return ATTN_EINVAL;
+  return hipEventDestroy(static_cast<hipEvent_t>(ev)) == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+ATTN_EXPORT int attn_event_elapsed_ms(void *start, void *stop, float *ms) {
+  if (!start || !stop || !ms) return ATTN_EINVAL;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return ATTN_EHIP;
+  return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) == hipSuccess
+             ? ATTN_OK
+             : ATTN_EHIP;
+}

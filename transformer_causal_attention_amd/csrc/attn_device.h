@@ -1,0 +1,77 @@
+// Device-side types and helpers shared by the attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace attn {
+
+constexpr int kMaxHalfDim = 64;  // head_dim <= 128
+
+// Rotary frequencies in revolutions per position: rope_theta^(-2i/d) / (2*pi), i < d/2.
+// Computed on the host in double precision and passed by value, so every index used by
+// the kernels is a compile-time constant or wave-uniform (scalar loads, no scratch).
+struct RopeTable {
+  double rev[kMaxHalfDim];
+};
+
+// Everything the bf16 attention kernel needs besides the rotation table.
+struct FwdParams {
+  const __bf16 *q;   // (B, S, Hq, D)
+  const __bf16 *kr;  // rotated keys (B, Hkv, S_pad, D), zero rows past S
+  const __bf16 *v;   // (B, S, Hkv, D)
+  __bf16 *out;       // (B, S, Hq, D)
+  float *lse;        // (B, Hq, S)
+  int B, S, Hq, Hkv, G, S_pad;
+  int hpw;           // query heads per workgroup (1, 2 or 4)
+  int n_units;       // B * Hkv * (G / hpw)
+  int n_row_blocks;  // ceil(S / rows per workgroup)
+  float q_scale;     // log2(e) / sqrt(D): scores come out in the base-2 domain
+};
+
+struct F32Params {
+  const float *q, *k, *v;
+  float *out;
+  float *lse;
+  int B, S, Hq, Hkv, G;
+  int n_row_blocks;
+  float q_scale;
+};
+
+struct RopeKParams {
+  const __bf16 *k;  // (B, S, Hkv, D)
+  __bf16 *kr;       // (B, Hkv, S_pad, D)
+  int B, S, Hkv, S_pad;
+};
+
+// Fraction of a turn for position p and frequency f (revolutions per position):
+// p * f is formed in double precision and reduced to [-0.5, 0.5], so the angle stays
+// accurate to ~1e-12 turns even at p = 32767, where a float product would be off by
+// ~1e-3 rad.
+__device__ __forceinline__ float turn_fraction(int p, double f) {
+  double r = (double)p * f;
+  return (float)(r - __builtin_rint(r));
+}
+
+// Accurate sin/cos of 2*pi*t for t in [-0.5, 0.5] (library sincospi).
+__device__ __forceinline__ void sincos_turns(float t, float *s, float *c) {
+  sincospif(2.0f * t, s, c);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace attn
