@@ -19,8 +19,8 @@ size_t padded_len(int S) { return ((size_t)S + kTileKeys - 1) / kTileKeys * kTil
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Query heads per workgroup: the largest of 4, 2, 1 dividing G (4 waves per workgroup).
-int heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+// Query heads per 4-wave group: the largest of 4, 2, 1 dividing G.
+int heads_per_group(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int causal, int dtype) {
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return ATTN_EINVAL;
@@ -74,10 +74,11 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
   p.S_pad = rp.S_pad;
-  p.hpw = heads_per_wg(p.G);
+  p.hpw = heads_per_group(p.G);
+  p.rows_per_blk = 32 * (4 / p.hpw);
   p.n_units = B * Hkv * (p.G / p.hpw);
-  const int rows_per_wg = 32 * (4 / p.hpw);
-  p.n_row_blocks = (S + rows_per_wg - 1) / rows_per_wg;
+  p.n_row_blocks = (S + p.rows_per_blk - 1) / p.rows_per_blk;
+  p.n_pairs = (p.n_row_blocks + 1) / 2;
   p.q_scale = q_scale(D);
 
   if (e0 && (err = hipEventRecord(e0, st)) != hipSuccess) return err;

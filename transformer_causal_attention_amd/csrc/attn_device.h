@@ -29,9 +29,11 @@ struct FwdParams {
   __bf16 *out;       // (B, S, Hq, D)
   float *lse;        // (B, Hq, S)
   int B, S, Hq, Hkv, G, S_pad;
-  int hpw;           // query heads per workgroup (1, 2 or 4)
+  int hpw;           // query heads per wave group (1, 2 or 4)
+  int rows_per_blk;  // query rows per row block: 32 * (4 / hpw)
   int n_units;       // B * Hkv * (G / hpw)
-  int n_row_blocks;  // ceil(S / rows per workgroup)
+  int n_row_blocks;  // ceil(S / rows_per_blk)
+  int n_pairs;       // ceil(n_row_blocks / 2): workgroups per unit
   float q_scale;     // log2(e) / sqrt(D): scores come out in the base-2 domain
 };
 
