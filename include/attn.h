@@ -62,7 +62,9 @@ const char *attn_strerror(int code);
 
 /*
  * Bytes of device workspace attn_fwd needs for these sizes (0 when none is needed).
- * For bf16 it holds the rotated keys, laid out (B, Hkv, S rounded up to 64, d) bf16.
+ * For bf16 it holds two equal halves of B * Hkv * (S rounded up to 64) * d bf16 elements: the
+ * rotated keys, then the values transposed per 64-key tile (a private layout, rewritten on
+ * every call).
  * Returns 0 as well for arguments attn_fwd would reject.
  */
 size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
@@ -94,8 +96,8 @@ int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, 
 
 /*
  * Same as attn_fwd, and additionally records `ev_start` on `stream` immediately before the
- * attention kernel and `ev_stop` immediately after it (the key-rotation pre-pass, when there
- * is one, runs before ev_start).  Events come from attn_event_create.  For benchmarking.
+ * attention kernel and `ev_stop` immediately after it (the key/value preparation pass, when
+ * there is one, runs before ev_start).  Events come from attn_event_create.  For benchmarking.
  */
 int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
                    int head_dim, double rope_theta, int causal, int dtype, void *out,

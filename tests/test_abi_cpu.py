@@ -42,10 +42,10 @@ def test_version_and_strerror():
 
 
 def test_workspace_bytes():
-    # bf16: rotated keys (B, Hkv, S rounded up to 64, D) in bf16
-    assert _lib.workspace_bytes(1, 2048, 8, 128, 0) == 1 * 8 * 2048 * 128 * 2
-    assert _lib.workspace_bytes(2, 100, 3, 64, 0) == 2 * 3 * 128 * 64 * 2
-    assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 64 * 64 * 2
+    # bf16: rotated keys and transposed values, each (B, Hkv, S rounded up to 64, D) bf16
+    assert _lib.workspace_bytes(1, 2048, 8, 128, 0) == 2 * 1 * 8 * 2048 * 128 * 2
+    assert _lib.workspace_bytes(2, 100, 3, 64, 0) == 2 * 2 * 3 * 128 * 64 * 2
+    assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 2 * 64 * 64 * 2
     assert _lib.workspace_bytes(1, 64, 1, 64, 1) == 0  # fp32 needs none
     assert _lib.workspace_bytes(1, 64, 1, 96, 0) == 0  # unsupported -> 0
     assert _lib.workspace_bytes(0, 64, 1, 64, 0) == 0

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kTileKeys = 64;  // key tile of the bf16 kernel; rotated keys are padded to it
+constexpr int kTileKeys = 64;  // key tile of the bf16 kernel; prepared K and V are padded to it
 
 size_t padded_len(int S) { return ((size_t)S + kTileKeys - 1) / kTileKeys * kTileKeys; }
 
@@ -32,6 +32,7 @@ int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int cau
   // index arithmetic in the kernels: row/key positions in int, offsets in size_t,
   // workgroup counts below 2^31
   if (S > (1 << 28)) return ATTN_EUNSUPPORTED;
+  if ((double)Hkv * d > (double)(1 << 24)) return ATTN_EUNSUPPORTED;  // 32-bit offsets within a 64-key tile
   const double elems = (double)B * S * Hq * d;
   if (elems > 4.0e15) return ATTN_EUNSUPPORTED;
   const double wgs = (double)B * Hq * ((double)S / 32.0 + 1.0) + (double)B * Hkv * (padded_len(S) / 256.0 + 1.0) * (d / 16);
@@ -52,20 +53,23 @@ template <int D>
 hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
                     const attn::RopeTable &tab, int causal, void *out, float *lse, void *ws,
                     hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  attn::RopeKParams rp;
-  rp.k = static_cast<const __bf16 *>(k);
-  rp.kr = static_cast<__bf16 *>(ws);
-  rp.B = B;
-  rp.S = S;
-  rp.Hkv = Hkv;
-  rp.S_pad = (int)padded_len(S);
-  hipError_t err = attn::launch_rope_k<D>(rp, tab, st);
+  const size_t s_pad = padded_len(S);
+  attn::PrepParams pp;
+  pp.k = static_cast<const __bf16 *>(k);
+  pp.v = static_cast<const __bf16 *>(v);
+  pp.kr = static_cast<__bf16 *>(ws);
+  pp.vt = pp.kr + (size_t)B * Hkv * s_pad * D;
+  pp.B = B;
+  pp.S = S;
+  pp.Hkv = Hkv;
+  pp.S_pad = (int)s_pad;
+  hipError_t err = attn::launch_prep_kv<D>(pp, tab, st);
   if (err != hipSuccess) return err;
 
   attn::FwdParams p;
   p.q = static_cast<const __bf16 *>(q);
-  p.kr = rp.kr;
-  p.v = static_cast<const __bf16 *>(v);
+  p.kr = pp.kr;
+  p.vt = pp.vt;
   p.out = static_cast<__bf16 *>(out);
   p.lse = lse;
   p.B = B;
@@ -73,7 +77,7 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
-  p.S_pad = rp.S_pad;
+  p.S_pad = pp.S_pad;
   p.hpw = heads_per_group(p.G);
   p.rows_per_blk = 32 * (4 / p.hpw);
   p.n_units = B * Hkv * (p.G / p.hpw);
@@ -155,7 +159,7 @@ ATTN_EXPORT const char *attn_strerror(int code) {
 ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype) {
   if (dtype != ATTN_DTYPE_BF16) return 0;
   if (B < 1 || S < 1 || Hkv < 1 || (head_dim != 64 && head_dim != 128) || S > (1 << 28)) return 0;
-  return (size_t)B * Hkv * padded_len(S) * head_dim * 2;
+  return 2 * (size_t)B * Hkv * padded_len(S) * head_dim * 2;  // rotated K and transposed V
 }
 
 ATTN_EXPORT int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,

@@ -24,8 +24,8 @@ struct RopeTable {
 // Everything the bf16 attention kernel needs besides the rotation table.
 struct FwdParams {
   const __bf16 *q;   // (B, S, Hq, D)
-  const __bf16 *kr;  // rotated keys (B, Hkv, S_pad, D), zero rows past S
-  const __bf16 *v;   // (B, S, Hkv, D)
+  const __bf16 *kr;  // rotated keys, 64-key tiles (B, Hkv, S_pad/64) x [D/8][64][8]
+  const __bf16 *vt;  // transposed values, 64-key tiles (B, Hkv, S_pad/64) x [8][D][8]
   __bf16 *out;       // (B, S, Hq, D)
   float *lse;        // (B, Hq, S)
   int B, S, Hq, Hkv, G, S_pad;
@@ -46,9 +46,11 @@ struct F32Params {
   float q_scale;
 };
 
-struct RopeKParams {
+struct PrepParams {
   const __bf16 *k;  // (B, S, Hkv, D)
-  __bf16 *kr;       // (B, Hkv, S_pad, D)
+  const __bf16 *v;  // (B, S, Hkv, D)
+  __bf16 *kr;       // 64-key tiles (B, Hkv, S_pad/64) x [D/8][64][8]
+  __bf16 *vt;       // 64-key tiles (B, Hkv, S_pad/64) x [8][D][8]
   int B, S, Hkv, S_pad;
 };
 

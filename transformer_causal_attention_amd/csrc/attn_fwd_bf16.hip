@@ -2,14 +2,15 @@
 //
 // What is computed (per batch row b, query head h, query position i, K/V head g = h / G):
 //   q' = RoPE(q_i) * log2(e)/sqrt(D)        (in registers, once per row block)
-//   s_j = q' . k'_j                          (k' = RoPE(k), produced by the pre-pass)
-//   online softmax over j <= i in base 2, out_i = sum_j p_j v_j / sum_j p_j,
-//   lse_i = ln(2) * (max_j s_j + log2 sum_j 2^(s_j - max))
+//   s_j = q' . k'_j                          (k' = RoPE(k), produced by the preparation pass)
+//   softmax over j <= i in base 2, evaluated online:  out_i = sum_j p_j v_j / sum_j p_j,
+//   p_j = 2^(s_j - m), lse_i = ln(2) * (m + log2 sum_j p_j)
 // Definitions: scores / sqrt(head_dim), mask of later keys, softmax over keys (llama3-from-
-// scratch page: "attention score matrix", "causal mask", "softmax"); row max subtracted
-// first (PaLM page, section 2.5); grouped K/V heads (llama3 page, "key-value sharing"); the
-// IO-aware, tiled evaluation that never stores the score matrix is what the Picotron page
-// calls flash attention ("Flash Attention integration and optimisation").
+// scratch page: "attention score matrix", "causal mask", "softmax"); the row maximum is
+// subtracted before exponentiating (PaLM page, section 2.5); grouped K/V heads (llama3 page,
+// "key-value sharing"); the IO-aware, tiled evaluation that never stores the score matrix is
+// what the Picotron page calls flash attention ("Flash Attention integration and
+// optimisation").
 //
 // Work decomposition.  A workgroup has 8 waves in two groups of 4 (wave w runs on SIMD w%4,
 // so every SIMD holds one wave of each group).  In a group each wave owns 32 query rows of
@@ -20,23 +21,37 @@
 // the remaining key tiles of block n-1-r, with x chosen so both groups run the same number of
 // tiles; A then hands its partial (max, sum, accumulator) for block n-1-r to B through LDS and
 // B merges the two (the same logsumexp merge that joins sequence shards).  Every workgroup
-// therefore does the same work, and consecutive workgroup ids walk the (batch, K/V head)
-// units so one K/V head stays on one XCD's L2 when the unit count is a multiple of 8.
+// therefore does the same work, and consecutive workgroup ids walk the (batch, K/V head, head
+// group) units so one K/V head stays on one XCD's L2 when the unit count is a multiple of 8.
 //
-// Data movement.  K' and V tiles (64 keys) go from HBM straight into LDS (global_load_lds,
-// 16 bytes per lane, no registers), double buffered per group, with XOR swizzles of the
-// 16-byte chunks so the MFMA operand reads below are free of bank conflicts.
+// Data movement.  The preparation pass stores K' and V^T as 64-key tiles in chunk-major order
+// ([dimension chunk][key][8] and [key chunk][column][8]).  A tile is copied from HBM straight
+// into LDS (global_load_lds, 16 bytes per lane, no registers) as one contiguous run, double
+// buffered per group, and every MFMA operand is then one 16-byte LDS read at a per-lane base
+// plus a constant offset, with 8 consecutive lanes reading 128 consecutive bytes (no bank
+// conflicts, no address arithmetic in the loop).  The two buffers are separate LDS arrays and
+// the loop is unrolled by two, so the compiler can see that operand reads of one buffer never
+// depend on the copies filling the other and inserts no wait for them.
 //
 // Matrix layout.  With A = K tile (32 keys x 16 dims) and B = Q^T (16 dims x 32 rows), the
 // 32x32x16 bf16 MFMA yields S^T: lane l holds query row l%32 and, in its 16 accumulators,
-// keys 8*(v/4) + 4*(l/32) + v%4.  Row max and row sum are thus in-lane plus one exchange
-// between the lane halves.  O^T = V^T P^T takes those accumulators (packed to bf16) as its B
-// operand unchanged; the matching A operand (V^T, keys along k in that order) is fetched from
-// the row-major V tile with the transposing LDS read ds_read_tr16_b64.  Keys above the
+// keys 8*(v/4) + 4*(l/32) + v%4.  Row sums are thus in-lane plus one exchange between the lane
+// halves at the end.  O^T = V^T P^T takes those accumulators (packed to bf16) as its B operand
+// unchanged; the matching A operand (V^T, 8 keys of one column in that order) is one 16-byte
+// read, because V^T stores each group of 16 keys in exactly that order.  Keys above the
 // diagonal are never loaded, and a wave skips the 32-key blocks entirely above its rows.
-// The accumulator is rescaled only when a row maximum grows by more than 2^8 (a wave-uniform
-// test): probabilities are then taken against a stale maximum and stay below 256, which
-// bf16 and fp32 hold exactly as well as values below 1.
+//
+// Softmax without a per-block maximum.  The running maximum m only needs to keep 2^(s - m)
+// finite: probabilities are taken against m as it stands, and a block is re-done with an
+// exact maximum (K fragments re-read, scores recomputed, accumulator and sum rescaled) only
+// if its probability sum exceeds 2^64.  The first block of a row block sets m exactly.  bf16
+// and fp32 hold values up to 2^64 with the same relative precision as values below 1, and the
+// result out = o / l, lse = m + log2 l does not depend on which m was used.  The common path
+// is branch-free, so a tile runs as  QK(b0) | QK(b1) with exp(b0) | PV(b0) with exp(b1) |
+// PV(b1), letting the in-order wave issue the exponentials of one block between the MFMAs of
+// the other.
+
+#include <type_traits>
 
 #include "attn_device.h"
 
@@ -45,8 +60,8 @@
 
 namespace attn {
 
-constexpr int BN = 64;  // keys per staged tile
-typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+constexpr int BN = 64;                      // keys per staged tile
+constexpr float kSumLimit = 1.8446744e19f;  // 2^64: above this a block is redone exactly
 
 __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -59,41 +74,32 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// 16-byte-chunk swizzles (chunk index XOR f(row)) of the staged tiles.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (row & 15) : ((row ^ (row >> 3)) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  const int a = row & 3;
-  return D == 128 ? (4 * a + 2 * (a >> 1)) : 2 * a;
-}
-
 // Each lane copies 16 bytes from `g` to lds_base + 16 * lane (lds_base is wave-uniform).
 __device__ __forceinline__ void lds_dma16(const void *g, char *lds_base) {
   __builtin_amdgcn_global_load_lds((GLB_AS void *)g, (LDS_AS void *)lds_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)p);
-  return __builtin_bit_cast(u32x2, r);
-}
-
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
-  constexpr int NKK = D / 16;      // MFMA steps over head_dim
-  constexpr int NCB = D / 32;      // 32-column blocks of the output
-  constexpr int TB = BN * D * 2;   // bytes of one staged K or V tile
-  constexpr int RB = 2 * D;        // bytes per tile row
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int DMA_PER_WAVE = TB / 4096;  // 1 KiB copies per wave per tile (4 waves per group)
-  // [group][buffer][K, V]
-  __shared__ __attribute__((aligned(1024))) char smem[8 * TB];
+  constexpr int NKK = D / 16;              // MFMA steps over head_dim
+  constexpr int NCB = D / 32;              // 32-column blocks of the output
+  constexpr int TB = BN * D * 2;           // bytes of one staged K or V^T tile
+  constexpr int DMA_PER_WAVE = TB / 4096;  // 1 KiB copies per wave, tile and operand
+  // one array per buffer parity, each [group][K, V^T]
+  __shared__ __attribute__((aligned(1024))) char lds0[4 * TB];
+  __shared__ __attribute__((aligned(1024))) char lds1[4 * TB];
+  // rotation frequencies, read per row block from LDS rather than held in registers (kept as
+  // loop-invariant values they would occupy 2*D VGPRs for the whole loop)
+  __shared__ double freq[D / 2];
 
   const int tid = threadIdx.x;
+  if (tid < D / 2) freq[tid] = tab.rev[tid];
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int grp = wave >> 2;
@@ -127,37 +133,33 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int head = g * p.G + hg * p.hpw + (gw % p.hpw);
   const int sub = gw / p.hpw;
 
-  const __bf16 *kr_base = p.kr + ((size_t)b * p.Hkv + g) * (size_t)p.S_pad * D;
-  const __bf16 *v_base = p.v + ((size_t)b * S * p.Hkv + g) * D;
-  const size_t v_rs = (size_t)p.Hkv * D;
+  const size_t n_tiles = (size_t)(p.S_pad / BN);
+  const char *kr_tiles = reinterpret_cast<const char *>(p.kr) + ((size_t)b * p.Hkv + g) * n_tiles * TB;
+  const char *vt_tiles = reinterpret_cast<const char *>(p.vt) + ((size_t)b * p.Hkv + g) * n_tiles * TB;
 
-  // per-lane operand offsets (loop invariant)
-  const int k_sw = k_swz<D>(l32);
-  const int sig = lane & 15;
-  const int v_row = 4 * hh + (sig >> 2);                       // + 32jb + 16t + 8e2
-  const int v_ch = 2 * ((lane >> 4) & 1) + ((sig & 3) >> 1);   // + 4cb
-  const int v_sw = v_swz<D>(sig >> 2);
-  const int v_half = 8 * (sig & 1);
+  // per-lane operand bases inside a staged tile (constant parts are immediates):
+  //   K of key block jb, step kk:   [chunk 2kk + hh][key 32jb + l32] -> k_lane + 2kk*1024 + jb*512
+  //   V^T of block jb, half t, cb:  [chunk 4jb + 2t + hh][column 32cb + l32]
+  //                                 -> v_lane + (4jb + 2t)*16*D + cb*512
+  const int k_lane = hh * 1024 + l32 * 16;
+  const int v_lane = hh * 16 * D + l32 * 16;
 
-  auto stage = [&](int i, int buf) {
+  auto stage = [&](int i, char *dst) {
     const int kt = i < len0 ? i : k1s + (i - len0);
-    char *kd = smem + ((grp * 2 + buf) * 2 + 0) * TB;
-    char *vd = smem + ((grp * 2 + buf) * 2 + 1) * TB;
-    const __bf16 *ks = kr_base + (size_t)kt * BN * D;
+    char *kd = dst + grp * 2 * TB;
+    const char *ks = kr_tiles + (size_t)kt * TB;
+    const char *vs = vt_tiles + (size_t)kt * TB;
 #pragma unroll
     for (int r = 0; r < DMA_PER_WAVE; ++r) {
       const int blk = gw * DMA_PER_WAVE + r;
-      const int L = blk * 64 + lane;  // 16-byte chunk of the tile this lane fills
-      const int row = L / CPR;
-      const int ch = L % CPR;
-      lds_dma16(ks + row * D + 8 * (ch ^ k_swz<D>(row)), kd + blk * 1024);
-      const int j = min(kt * BN + row, S - 1);  // rows past S are masked; any finite value works
-      lds_dma16(v_base + (size_t)j * v_rs + 8 * (ch ^ v_swz<D>(row)), vd + blk * 1024);
+      lds_dma16(ks + blk * 1024 + lane * 16, kd + blk * 1024);
+      lds_dma16(vs + blk * 1024 + lane * 16, kd + TB + blk * 1024);
     }
   };
 
+  // ---- state of this wave's 32 rows
   bf16x8 qf[NKK];
-  float m_run = -INFINITY;  // running row max (base-2 scores), stale by at most 8
+  float m_run = -INFINITY;  // running maximum used for the probabilities (base-2 scores)
   float l_run = 0.f;        // this lane half's share of the running row sum
   f32x16 o[NCB];
   int row0 = 0, kb_last = -1, cur_seg = -1;
@@ -186,7 +188,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
         for (int z = 0; z < 2; ++z) {
           const int e = 2 * w + z;
-          const double f = hh ? tab.rev[16 * kk + 8 + e] : tab.rev[16 * kk + e];
+          const double f = freq[16 * kk + 8 * hh + e];
           const float t = turn_fraction(my_row, f);
           const float sn = __builtin_amdgcn_sinf(t);  // argument in turns
           const float cs = __builtin_amdgcn_cosf(t);
@@ -228,85 +230,130 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
   };
 
-  auto compute_tile = [&](int kt, int buf) {
-    const char *kd = smem + ((grp * 2 + buf) * 2 + 0) * TB;
-    const char *vd = smem + ((grp * 2 + buf) * 2 + 1) * TB;
-    const int kbase = kt * BN;
-    f32x16 s[2];
+  // ---- block pieces (kd / vd: this group's K and V^T tile in the current buffer)
+  auto qk = [&](const char *kd, int jb) {
+    bf16x8 kf[NKK];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (2 * kt + jb <= kb_last) {
-        f32x16 acc = f32x16{};
-        const int row = 32 * jb + l32;
-        const int sw = D == 128 ? k_sw : k_swz<D>(row);
-        const char *ka = kd + row * RB;
+    for (int kk = 0; kk < NKK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kd + k_lane + 2 * kk * 1024 + jb * 512);
+    f32x16 sc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ka + 16 * ((2 * kk + hh) ^ sw));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], acc, 0, 0, 0);
-        }
-        s[jb] = acc;
-      }
-    }
+    for (int kk = 0; kk < NKK; ++kk) sc = mfma(kf[kk], qf[kk], sc);
+    return sc;
+  };
+  auto load_v = [&](const char *vd, int jb, bf16x8 (&vf)[2][NCB]) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      if (2 * kt + jb > kb_last) continue;  // wave-uniform
-      const int kb0 = kbase + 32 * jb;
-      if ((CAUSAL && kb0 + 31 > row0) || kb0 + 32 > S) {
-        const int my_row = row0 + l32;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if ((CAUSAL && j > my_row) || j >= S) s[jb][v] = -INFINITY;
-        }
-      }
-      float mx = s[jb][0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
-      mx = max_xor32(mx);
-      // every row of a processed block has a visible key, so mx is finite here
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-        m_run = m_new;
-      }
-      float rsum = 0.f;
+      for (int cb = 0; cb < NCB; ++cb)
+        vf[t][cb] = *reinterpret_cast<const bf16x8 *>(vd + v_lane + (4 * jb + 2 * t) * 16 * D + cb * 512);
+  };
+  // keys after the query (diagonal block) or past the sequence end get -inf
+  auto mask = [&](f32x16 &sc, int kb0) {
+    if ((CAUSAL && kb0 + 31 > row0) || kb0 + 32 > S) {  // wave-uniform
+      const int my_row = row0 + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(s[jb][v] - m_run);
-        s[jb][v] = e;
-        rsum += e;
-      }
-      l_run += rsum;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 pw;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(s[jb][8 * t + 2 * w], s[jb][8 * t + 2 * w + 1]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        const char *vr = vd + (32 * jb + 16 * t + v_row) * RB + v_half;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int ch = (4 * cb + v_ch) ^ v_sw;
-          const u32x2 a0 = lds_read_tr16(vr + 16 * ch);
-          const u32x2 a1 = lds_read_tr16(vr + 8 * RB + 16 * ch);
-          const u32x4 a4 = {a0[0], a0[1], a1[0], a1[1]};
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pb, o[cb], 0, 0, 0);
-        }
+        const int j = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if ((CAUSAL && j > my_row) || j >= S) sc[v] = -INFINITY;
       }
     }
   };
+  // exact maximum of a (masked) block; rescales the accumulated state to it.  Finite: every
+  // row of a processed block has a visible key.
+  auto take_max = [&](const f32x16 &sc) {
+    float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was unset
+    l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+    m_run = m_new;
+  };
+  // p = 2^(s - m_run) in place; returns this lane's sum of the block
+  auto expo = [&](f32x16 &sc) {
+    float rsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sc[v] = __builtin_amdgcn_exp2f(sc[v] - m_run);
+      rsum += sc[v];
+    }
+    return rsum;
+  };
+  auto needs_redo = [&](float rsum) {
+    return __builtin_amdgcn_ballot_w64(!(rsum <= kSumLimit)) != 0;  // also catches inf and NaN
+  };
+  // exact path for a block whose probability sum overflowed the limit: scores recomputed from
+  // the (still staged) K tile, maximum taken, state rescaled, probabilities recomputed
+  auto redo = [&](f32x16 &sc, float &rsum, const char *kd, int jb, int kb0) {
+    // re-read the fragments rather than keeping the first read's registers alive until here
+    asm volatile("" ::: "memory");
+    sc = qk(kd, jb);
+    mask(sc, kb0);
+    take_max(sc);
+    rsum = expo(sc);
+  };
+  auto pv = [&](const f32x16 &pr, const bf16x8 (&vf)[2][NCB]) {
+    bf16x8 pb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 pw;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(pr[8 * t + 2 * w], pr[8 * t + 2 * w + 1]);
+      pb[t] = __builtin_bit_cast(bf16x8, pw);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) o[cb] = mfma(vf[t][cb], pb[t], o[cb]);
+  };
 
-  // ---- main loop: both groups step through their tile lists in lockstep
-  if (n_mine > 0) stage(0, 0);
-  wait_vm_all();
-  __syncthreads();
-  for (int i = 0; i < n_iter; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < n_mine) stage(i + 1, buf ^ 1);
+  auto compute_tile = [&](int kt, const char *base) {
+    const char *kd = base + grp * 2 * TB;
+    const char *vd = kd + TB;
+    const int kb0 = kt * BN;
+    if (2 * kt > kb_last) return;  // the whole tile is above this wave's rows
+    f32x16 s0 = qk(kd, 0);
+    mask(s0, kb0);
+    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) take_max(s0);  // first block of the rows
+    if (2 * kt + 1 <= kb_last) {
+      // QK(b1) with exp(b0) | PV(b0) with exp(b1) | PV(b1); the fences keep each region's
+      // fragment loads inside it, which bounds the live registers
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s1 = qk(kd, 1);
+      float r0 = expo(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (needs_redo(r0)) redo(s0, r0, kd, 0, kb0);
+      l_run += r0;
+      mask(s1, kb0 + 32);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 vf[2][NCB];
+      load_v(vd, 0, vf);
+      pv(s0, vf);
+      float r1 = expo(s1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (needs_redo(r1)) redo(s1, r1, kd, 1, kb0 + 32);
+      l_run += r1;
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(vd, 1, vf);
+      pv(s1, vf);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      float r0 = expo(s0);
+      if (needs_redo(r0)) redo(s0, r0, kd, 0, kb0);
+      l_run += r0;
+      bf16x8 vf[2][NCB];
+      load_v(vd, 0, vf);
+      pv(s0, vf);
+    }
+  };
+
+  // ---- main loop: both groups step through their tile lists in lockstep; tile i sits in
+  // buffer i % 2 (unrolled by two so the buffer of every access is known at compile time)
+  auto step = [&](int i, const char *cur, char *nxt) {
+    if (i + 1 < n_mine) stage(i + 1, nxt);
     if (i < n_mine) {
       const int seg = i < len0 ? 0 : 1;
       if (seg != cur_seg) {
@@ -314,17 +361,24 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         begin_seg(seg);
         cur_seg = seg;
       }
-      compute_tile(i < len0 ? i : k1s + (i - len0), buf);
+      compute_tile(i < len0 ? i : k1s + (i - len0), cur);
     }
     wait_vm_all();
     __syncthreads();
+  };
+  if (n_mine > 0) stage(0, lds0);
+  wait_vm_all();
+  __syncthreads();
+  for (int i = 0; i < n_iter; i += 2) {
+    step(i, lds0, lds1);
+    if (i + 1 < n_iter) step(i + 1, lds1, lds0);
   }
 
   // ---- finish: A stores block r_lo if it still holds it; the split block is merged in B
   if (grp == 0 && cur_seg == 0) store_seg();
   if (x > 0) {
-    float *mo = reinterpret_cast<float *>(smem);  // tile buffers are free after the last barrier
-    float *mm = mo + 4 * NCB * 16 * 64;
+    float *mo = reinterpret_cast<float *>(lds0);  // tile buffers are free after the last barrier
+    float *mm = reinterpret_cast<float *>(lds1);
     if (grp == 0) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)

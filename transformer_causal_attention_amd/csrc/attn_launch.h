@@ -6,7 +6,7 @@
 namespace attn {
 
 template <int D>
-hipError_t launch_rope_k(const RopeKParams &p, const RopeTable &tab, hipStream_t stream);
+hipError_t launch_prep_kv(const PrepParams &p, const RopeTable &tab, hipStream_t stream);
 
 template <int D, bool CAUSAL>
 hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream);
