@@ -95,9 +95,10 @@ int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, 
              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Same as attn_fwd, and additionally records `ev_start` on `stream` immediately before the
- * attention kernel and `ev_stop` immediately after it (the key/value preparation pass, when
- * there is one, runs before ev_start).  Events come from attn_event_create.  For benchmarking.
+ * Same as attn_fwd, and additionally has the runtime record `ev_start` and `ev_stop` with the
+ * attention kernel's own dispatch (hipExtLaunchKernel), so the interval between them is that
+ * kernel's execution alone; the key/value preparation pass, when there is one, runs before
+ * it.  Either event may be NULL.  Events come from attn_event_create.  For benchmarking.
  */
 int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
                    int head_dim, double rope_theta, int causal, int dtype, void *out,

@@ -124,6 +124,78 @@ def test_zero_query_gives_running_mean():
         assert (lse[0, h].cpu().double() - torch.log(torch.arange(1, w.S + 1, dtype=torch.float64))).abs().max().item() <= 2e-2
 
 
+# Inputs with a wide score range, built in the lowest-frequency rotation pair (dimensions
+# d/2 - 1 and d - 1): at rope_theta 5e5 it turns by under 1e-3 rad over a few hundred
+# positions, so values placed there keep their size after rotation.  A kernel that takes
+# probabilities against a running maximum must rescale when a later block scores far above
+# the first one; these cases force that on every workgroup shape (1, 2 and 4 heads per
+# K/V tile), causal and not, at both head sizes.
+WIDE = [(d, Hq, Hkv, causal) for d in (64, 128) for (Hq, Hkv) in ((4, 1), (8, 2), (2, 2)) for causal in (True, False)]
+
+
+def wide_ids(c):
+    return f"d{c[0]}-H{c[1]}/{c[2]}-{'causal' if c[3] else 'full'}"
+
+
+@pytest.mark.parametrize("depth", [55.0, 96.0])
+@pytest.mark.parametrize("case", WIDE, ids=wide_ids)
+def test_sunken_first_tile(case, depth):
+    """Keys 0..63 score `depth` (natural units) below the later keys for rows >= 64.
+
+    At depth 55 the later blocks' probability sums against the first block's maximum are
+    about 2^79 (finite, above 2^64); at depth 96 they overflow float32.  Rows below 64 see
+    only the first tile, with moderate scores.  Tolerances are the bf16 ones: the sunken keys
+    carry weights of e^-55 or less, so their (larger) score rounding does not reach the result.
+    """
+    d, Hq, Hkv, causal = case
+    w = small("sunken", 1, 300, Hq, Hkv, d, "bf16", causal, theta=500000.0, seed=int(depth) + d)
+    q, k, v = (t.float() for t in make_inputs(w))
+    c, c2 = d // 2 - 1, d - 1
+    q, k = 0.5 * q, 0.5 * k
+    k[:, :64] = 0.0
+    k[:, :64, :, c] = -8.0
+    k[:, 64:, :, c] = 0.0
+    k[:, 64:, :, c2] = 0.0
+    q[:, :64, :, c] = 0.5
+    q[:, 64:, :, c] = depth * d ** 0.5 / 8.0
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    out, lse = gpu_run(w, q, k, v)
+    ref_out, ref_lse = oracle_run(w, q, k, v)
+    compare(w, out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("case", WIDE, ids=wide_ids)
+def test_staircase_scores(case):
+    """Every 64-key tile scores about 68 (natural units) above the one before it.
+
+    Each new tile's probabilities against the previous maximum sum past 2^97, so every tile is
+    rescaled.  out keeps the bf16 tolerance.  For lse the scaled query is rounded to bf16
+    (relative error up to 2^-9), which moves the top score of a row by up to 2^-9 * |s|;
+    scores reach ~300 here, so lse is checked to 2e-2 + 2^-8 * max|s| per row.
+    """
+    d, Hq, Hkv, causal = case
+    w = small("stairs", 1, 300, Hq, Hkv, d, "bf16", causal, theta=500000.0, seed=d + 3)
+    q, k, v = (t.float() for t in make_inputs(w))
+    c, c2 = d // 2 - 1, d - 1
+    q, k = 0.25 * q, 0.25 * k
+    q[..., c] = 68.0 * d ** 0.5 / 8.0
+    q[..., c2] = 0.0
+    k[..., c2] = 0.0
+    k[..., c] = 8.0 * (torch.arange(w.S) // 64).float()[None, :, None]
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    out, lse = gpu_run(w, q, k, v)
+    ref_out, ref_lse = oracle_run(w, q, k, v)
+    o = out.float().cpu().double().numpy()
+    assert np.all(np.isfinite(o))
+    eo = np.abs(o - ref_out).max()
+    # |s| of every row's top score, from the oracle's own lse (lse >= max score >= lse - ln S)
+    lse_tol = 2e-2 + 2.0 ** -8 * (np.abs(ref_lse) + np.log(w.S))
+    el = np.abs(lse.cpu().double().numpy() - ref_lse)
+    say(f"staircase {w}: out err {eo:.3e}, lse err {el.max():.3e} (tol up to {lse_tol.max():.3e})")
+    assert eo <= TOL["bf16"]
+    assert np.all(el <= lse_tol)
+
+
 def test_deterministic_and_overwrites_poisoned_outputs():
     w = small("det", 2, 300, 8, 2, 128, "bf16", True)
     q, k, v = (t.cuda() for t in make_inputs(w))

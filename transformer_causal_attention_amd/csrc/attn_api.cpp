@@ -85,11 +85,8 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.n_pairs = (p.n_row_blocks + 1) / 2;
   p.q_scale = q_scale(D);
 
-  if (e0 && (err = hipEventRecord(e0, st)) != hipSuccess) return err;
-  err = causal ? attn::launch_attn_bf16<D, true>(p, tab, st) : attn::launch_attn_bf16<D, false>(p, tab, st);
-  if (err != hipSuccess) return err;
-  if (e1 && (err = hipEventRecord(e1, st)) != hipSuccess) return err;
-  return hipSuccess;
+  return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
+                : attn::launch_attn_bf16<D, false>(p, tab, st, e0, e1);
 }
 
 template <int D>
@@ -109,12 +106,8 @@ hipError_t run_f32(const void *q, const void *k, const void *v, int B, int S, in
   p.G = Hq / Hkv;
   p.n_row_blocks = (S + 63) / 64;
   p.q_scale = q_scale(D);
-  hipError_t err;
-  if (e0 && (err = hipEventRecord(e0, st)) != hipSuccess) return err;
-  err = causal ? attn::launch_attn_f32<D, true>(p, tab, st) : attn::launch_attn_f32<D, false>(p, tab, st);
-  if (err != hipSuccess) return err;
-  if (e1 && (err = hipEventRecord(e1, st)) != hipSuccess) return err;
-  return hipSuccess;
+  return causal ? attn::launch_attn_f32<D, true>(p, tab, st, e0, e1)
+                : attn::launch_attn_f32<D, false>(p, tab, st, e0, e1);
 }
 
 int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv, int d,

@@ -53,6 +53,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "attn_device.h"
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -406,15 +408,21 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream) {
+hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
   const long long blocks = (long long)p.n_units * p.n_pairs;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0, stream, p, tab);
+  hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0, stream,
+                        ev_start, ev_stop, 0, p, tab);
   return hipGetLastError();
 }
 
-template hipError_t launch_attn_bf16<64, true>(const FwdParams &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_bf16<64, false>(const FwdParams &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_bf16<128, true>(const FwdParams &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_bf16<128, false>(const FwdParams &, const RopeTable &, hipStream_t);
+template hipError_t launch_attn_bf16<64, true>(const FwdParams &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_bf16<64, false>(const FwdParams &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_bf16<128, true>(const FwdParams &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_bf16<128, false>(const FwdParams &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
 
 }  // namespace attn

@@ -9,6 +9,8 @@
 // plain FMAs against key/value tiles staged in LDS, where every lane reads the same key
 // at the same time (LDS broadcast).  Keys are rotated while they are staged.
 
+#include <hip/hip_ext.h>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -124,15 +126,21 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream) {
+hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop) {
   const long long blocks = (long long)p.B * p.Hq * p.n_row_blocks;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64), 0, stream, p, tab);
+  hipExtLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64), 0, stream,
+                        ev_start, ev_stop, 0, p, tab);
   return hipGetLastError();
 }
 
-template hipError_t launch_attn_f32<64, true>(const F32Params &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_f32<64, false>(const F32Params &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_f32<128, true>(const F32Params &, const RopeTable &, hipStream_t);
-template hipError_t launch_attn_f32<128, false>(const F32Params &, const RopeTable &, hipStream_t);
+template hipError_t launch_attn_f32<64, true>(const F32Params &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_f32<64, false>(const F32Params &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_f32<128, true>(const F32Params &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
+template hipError_t launch_attn_f32<128, false>(const F32Params &, const RopeTable &, hipStream_t,
+                                                    hipEvent_t, hipEvent_t);
 
 }  // namespace attn

@@ -8,10 +8,14 @@ namespace attn {
 template <int D>
 hipError_t launch_prep_kv(const PrepParams &p, const RopeTable &tab, hipStream_t stream);
 
+// The attention launchers take optional start/stop events that the runtime records with the
+// kernel's own dispatch (hipExtLaunchKernel), so their interval is the kernel's execution.
 template <int D, bool CAUSAL>
-hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream);
+hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
+                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
 template <int D, bool CAUSAL>
-hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream);
+hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace attn
