@@ -26,12 +26,12 @@
 //
 // Data movement.  The preparation pass stores K' and V^T as 64-key tiles in chunk-major order
 // ([dimension chunk][key][8] and [key chunk][column][8]).  A tile is copied from HBM straight
-// into LDS (global_load_lds, 16 bytes per lane, no registers) as one contiguous run, double
-// buffered per group, and every MFMA operand is then one 16-byte LDS read at a per-lane base
-// plus a constant offset, with 8 consecutive lanes reading 128 consecutive bytes (no bank
-// conflicts, no address arithmetic in the loop).  The two buffers are separate LDS arrays and
-// the loop is unrolled by two, so the compiler can see that operand reads of one buffer never
-// depend on the copies filling the other and inserts no wait for them.
+// into LDS (global_load_lds, 16 bytes per lane, no registers) as one contiguous run, and every
+// MFMA operand is then one 16-byte LDS read at a per-lane base plus a constant offset, with 8
+// consecutive lanes reading 128 consecutive bytes (no bank conflicts, no address arithmetic in
+// the loop).  K and V^T have two buffers each, in four separate LDS arrays, and the loop is
+// unrolled by two, so the compiler can see that operand reads never depend on the copies in
+// flight and inserts no wait for them.
 //
 // Matrix layout.  With A = K tile (32 keys x 16 dims) and B = Q^T (16 dims x 32 rows), the
 // 32x32x16 bf16 MFMA yields S^T: lane l holds query row l%32 and, in its 16 accumulators,
@@ -41,29 +41,35 @@
 // read, because V^T stores each group of 16 keys in exactly that order.  Keys above the
 // diagonal are never loaded, and a wave skips the 32-key blocks entirely above its rows.
 //
+// Pipeline.  Step i of the loop computes the scores and probabilities of key tile i and the
+// P.V product of tile i-1 (whose V^T tile is kept one step longer), so every step has matrix
+// work to overlap with the exponentials: the two 32-key score blocks run as two interleaved
+// MFMA chains, then the P.V product of the previous tile carries the exponentials of both.
+// The probabilities of a tile wait in registers, packed to bf16, until the next step.
+//
 // Softmax without a per-block maximum.  The running maximum m only needs to keep 2^(s - m)
-// finite: probabilities are taken against m as it stands, and a block is re-done with an
-// exact maximum (K fragments re-read, scores recomputed, accumulator and sum rescaled) only
-// if its probability sum exceeds 2^64.  The first block of a row block sets m exactly.  bf16
-// and fp32 hold values up to 2^64 with the same relative precision as values below 1, and the
-// result out = o / l, lse = m + log2 l does not depend on which m was used.  The common path
-// is branch-free, so a tile runs as  QK(b0) | QK(b1) with exp(b0) | PV(b0) with exp(b1) |
-// PV(b1), letting the in-order wave issue the exponentials of one block between the MFMAs of
-// the other.
-
-#include <type_traits>
+// finite: interior tiles take probabilities against m as it stands (the QK accumulation starts
+// from -m, so the products come out already shifted), and a tile is re-done with an exact
+// maximum (scores recomputed from the still-staged K tile, accumulator and sum rescaled) only if
+// its probability sum exceeds 2^64.  The first tile of a row block, tiles on the diagonal and
+// the tile at the sequence end always take the exact maximum.  bf16 and fp32 hold values up to
+// 2^64 with the same relative precision as values below 1, and out = o / l,
+// lse = m + log2 l do not depend on which m was used.  The row sum adds the bf16-rounded
+// probabilities (the values the P.V product sees) with a two-term dot product.
 
 #include <hip/hip_ext.h>
 
 #include "attn_device.h"
 
 #define LDS_AS __attribute__((address_space(3)))
-#define GLB_AS __attribute__((address_space(1)))
 
 namespace attn {
 
 constexpr int BN = 64;                      // keys per staged tile
-constexpr float kSumLimit = 1.8446744e19f;  // 2^64: above this a block is redone exactly
+constexpr float kSumLimit = 1.8446744e19f;  // 2^64: above this a tile is redone exactly
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -76,9 +82,16 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Each lane copies 16 bytes from `g` to lds_base + 16 * lane (lds_base is wave-uniform).
-__device__ __forceinline__ void lds_dma16(const void *g, char *lds_base) {
-  __builtin_amdgcn_global_load_lds((GLB_AS void *)g, (LDS_AS void *)lds_base, 16, 0, 0);
+// Each lane copies the 16 bytes at byte soff + voff of buffer `rsrc` to lds_base + 16 * lane
+// (lds_base and soff wave-uniform, voff = 16 * lane).  Buffer addressing keeps the base in
+// scalar registers and the lane offset in one VGPR; reads past the buffer's size return zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)lds_base, 16, voff, soff, 0, 0);
+}
+
+// Raw (unformatted, byte-addressed) buffer resource over `bytes` bytes at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -87,17 +100,20 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+constexpr int kReadsAhead = 4;  // LDS operand reads kept in flight ahead of the MFMAs
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;              // MFMA steps over head_dim
   constexpr int NCB = D / 32;              // 32-column blocks of the output
   constexpr int TB = BN * D * 2;           // bytes of one staged K or V^T tile
-  constexpr int DMA_PER_WAVE = TB / 4096;  // 1 KiB copies per wave, tile and operand
-  // one array per buffer parity, each [group][K, V^T]
-  __shared__ __attribute__((aligned(1024))) char lds0[4 * TB];
-  __shared__ __attribute__((aligned(1024))) char lds1[4 * TB];
-  // rotation frequencies, read per row block from LDS rather than held in registers (kept as
-  // loop-invariant values they would occupy 2*D VGPRs for the whole loop)
+  constexpr int DMA_PER_WAVE = TB / 4096;  // 1 KiB copies per wave and tile
+  // K tiles of even / odd steps and V^T tiles of even / odd steps, each [group][tile]
+  __shared__ __attribute__((aligned(1024))) char ldsk0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char ldsk1[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char ldsv0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char ldsv1[2 * TB];
+  // rotation frequencies, read per row block from LDS rather than held in registers
   __shared__ double freq[D / 2];
 
   const int tid = threadIdx.x;
@@ -130,7 +146,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int len0 = (grp == 0 && two) ? t_lo : 0;
   const int k1s = grp == 0 ? 0 : x;
   const int n_mine = len0 + (grp == 0 ? x : t_hi - x);
-  const int n_iter = max((two ? t_lo : 0) + x, t_hi - x);
+  // group A issues the tile copies of both groups (it finishes its tiles first and would
+  // otherwise wait at the barrier); group B's tile list is x, x+1, ..., t_hi-1
+  const int len0_a = two ? t_lo : 0;
+  const int n_a = len0_a + x;
+  const int n_b = t_hi - x;
+  // one extra step drains the last tile's P.V product; rounded up to even (the loop body is
+  // two steps, and steps past a group's last tile only wait at the barrier)
+  const int n_iter = (max((two ? t_lo : 0) + x, t_hi - x) + 2) & ~1;
 
   const int head = g * p.G + hg * p.hpw + (gw % p.hpw);
   const int sub = gw / p.hpw;
@@ -138,6 +161,10 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const size_t n_tiles = (size_t)(p.S_pad / BN);
   const char *kr_tiles = reinterpret_cast<const char *>(p.kr) + ((size_t)b * p.Hkv + g) * n_tiles * TB;
   const char *vt_tiles = reinterpret_cast<const char *>(p.vt) + ((size_t)b * p.Hkv + g) * n_tiles * TB;
+  // the K and V^T tiles of this (batch row, K/V head) as buffers (S_pad * D * 2 bytes < 2^31)
+  const __amdgpu_buffer_rsrc_t kr_buf = raw_buffer(kr_tiles, (uint32_t)(n_tiles * TB));
+  const __amdgpu_buffer_rsrc_t vt_buf = raw_buffer(vt_tiles, (uint32_t)(n_tiles * TB));
+  const uint32_t dma_lane = 16u * (uint32_t)lane;
 
   // per-lane operand bases inside a staged tile (constant parts are immediates):
   //   K of key block jb, step kk:   [chunk 2kk + hh][key 32jb + l32] -> k_lane + 2kk*1024 + jb*512
@@ -146,16 +173,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int k_lane = hh * 1024 + l32 * 16;
   const int v_lane = hh * 16 * D + l32 * 16;
 
-  auto stage = [&](int i, char *dst) {
-    const int kt = i < len0 ? i : k1s + (i - len0);
-    char *kd = dst + grp * 2 * TB;
-    const char *ks = kr_tiles + (size_t)kt * TB;
-    const char *vs = vt_tiles + (size_t)kt * TB;
+  auto tile_of = [&](int i) { return i < len0 ? i : k1s + (i - len0); };
+  auto tile_a = [&](int i) { return i < len0_a ? i : i - len0_a; };
+  // this wave's share (DMA_PER_WAVE KiB) of copying tile kt of `buf` to dst
+  auto stage = [&](__amdgpu_buffer_rsrc_t buf, int kt, char *dst) {
 #pragma unroll
     for (int r = 0; r < DMA_PER_WAVE; ++r) {
       const int blk = gw * DMA_PER_WAVE + r;
-      lds_dma16(ks + blk * 1024 + lane * 16, kd + blk * 1024);
-      lds_dma16(vs + blk * 1024 + lane * 16, kd + TB + blk * 1024);
+      lds_dma16(buf, dma_lane, (uint32_t)kt * TB + blk * 1024, dst + blk * 1024);
     }
   };
 
@@ -164,7 +189,23 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   float m_run = -INFINITY;  // running maximum used for the probabilities (base-2 scores)
   float l_run = 0.f;        // this lane half's share of the running row sum
   f32x16 o[NCB];
+  bf16x8 pend[2][2];        // probabilities of the previous tile, [block][key half]; zero if none
   int row0 = 0, kb_last = -1, cur_seg = -1;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
+  // The P.V product of a step always runs; with zero probabilities it must read finite values,
+  // so the V^T buffers start out zeroed (later they only ever hold staged tiles).
+  {
+    u32x4 *z0 = reinterpret_cast<u32x4 *>(ldsv0);
+    u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
+#pragma unroll
+    for (int r = 0; r < 2 * TB / 16 / 512; ++r) {
+      z0[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
+      z1[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   auto begin_seg = [&](int seg) {
     const int R = seg == 0 ? r_lo : r_hi;
@@ -232,160 +273,255 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
   };
 
-  // ---- block pieces (kd / vd: this group's K and V^T tile in the current buffer)
+  // ---- block pieces (kd / vd: this group's K and V^T tile)
+  auto kfrag = [&](const char *kd, int jb, int kk) {
+    return *reinterpret_cast<const bf16x8 *>(kd + k_lane + 2 * kk * 1024 + jb * 512);
+  };
+  auto vfrag = [&](const char *vd, int jb, int t, int cb) {
+    return *reinterpret_cast<const bf16x8 *>(vd + v_lane + (4 * jb + 2 * t) * 16 * D + cb * 512);
+  };
   auto qk = [&](const char *kd, int jb) {
-    bf16x8 kf[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kd + k_lane + 2 * kk * 1024 + jb * 512);
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) sc = mfma(kf[kk], qf[kk], sc);
+    for (int kk = 0; kk < NKK; ++kk) sc = mfma(kfrag(kd, jb, kk), qf[kk], sc);
     return sc;
   };
-  auto load_v = [&](const char *vd, int jb, bf16x8 (&vf)[2][NCB]) {
+  // O += V^T(previous tile) P^T(previous tile)
+  auto pv_pending = [&](const char *vd) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        vf[t][cb] = *reinterpret_cast<const bf16x8 *>(vd + v_lane + (4 * jb + 2 * t) * 16 * D + cb * 512);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb] = mfma(vfrag(vd, jb, t, cb), pend[jb][t], o[cb]);
   };
-  // keys after the query (diagonal block) or past the sequence end get -inf
+  // keys after the query or past the sequence end get -inf (only called where some may be)
   auto mask = [&](f32x16 &sc, int kb0) {
-    if ((CAUSAL && kb0 + 31 > row0) || kb0 + 32 > S) {  // wave-uniform
-      const int my_row = row0 + l32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if ((CAUSAL && j > my_row) || j >= S) sc[v] = -INFINITY;
-      }
-    }
-  };
-  // exact maximum of a (masked) block; rescales the accumulated state to it.  Finite: every
-  // row of a processed block has a visible key.
-  auto take_max = [&](const f32x16 &sc) {
-    float mx = fmaxf(sc[0], sc[1]);
-#pragma unroll
-    for (int v = 2; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run was unset
-    l_run *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-    m_run = m_new;
-  };
-  // p = 2^(s - m_run) in place; returns this lane's sum of the block
-  auto expo = [&](f32x16 &sc) {
-    float rsum = 0.f;
+    const int my_row = row0 + l32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      sc[v] = __builtin_amdgcn_exp2f(sc[v] - m_run);
-      rsum += sc[v];
+      const int j = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if ((CAUSAL && j > my_row) || j >= S) sc[v] = -INFINITY;
     }
-    return rsum;
   };
-  auto needs_redo = [&](float rsum) {
-    return __builtin_amdgcn_ballot_w64(!(rsum <= kSumLimit)) != 0;  // also catches inf and NaN
-  };
-  // exact path for a block whose probability sum overflowed the limit: scores recomputed from
-  // the (still staged) K tile, maximum taken, state rescaled, probabilities recomputed
-  auto redo = [&](f32x16 &sc, float &rsum, const char *kd, int jb, int kb0) {
-    // re-read the fragments rather than keeping the first read's registers alive until here
-    asm volatile("" ::: "memory");
-    sc = qk(kd, jb);
-    mask(sc, kb0);
-    take_max(sc);
-    rsum = expo(sc);
-  };
-  auto pv = [&](const f32x16 &pr, const bf16x8 (&vf)[2][NCB]) {
-    bf16x8 pb[2];
+  // p = 2^(sc - m) packed to bf16; returns this lane's sum of the bf16-rounded probabilities
+  auto expo_pack = [&](f32x16 &sc, float m, bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(sc[v] - m);
+    float rs = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       u32x4 pw;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(pr[8 * t + 2 * w], pr[8 * t + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(sc[8 * t + 2 * w], sc[8 * t + 2 * w + 1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // through a scalar: a bit cast of the vector element itself reads element 0
+        const uint32_t pair = pw[w];
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                             __builtin_bit_cast(bf16x2, kOnesBf16x2), rs, false);
+      }
       pb[t] = __builtin_bit_cast(bf16x8, pw);
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) o[cb] = mfma(vf[t][cb], pb[t], o[cb]);
+    return rs;
+  };
+  auto needs_redo = [&](float rsum) {
+    return __builtin_amdgcn_ballot_w64(!(rsum <= kSumLimit)) != 0;  // also catches inf and NaN
   };
 
-  auto compute_tile = [&](int kt, const char *base) {
-    const char *kd = base + grp * 2 * TB;
-    const char *vd = kd + TB;
-    const int kb0 = kt * BN;
-    if (2 * kt > kb_last) return;  // the whole tile is above this wave's rows
-    f32x16 s0 = qk(kd, 0);
-    mask(s0, kb0);
-    if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY)) take_max(s0);  // first block of the rows
-    if (2 * kt + 1 <= kb_last) {
-      // QK(b1) with exp(b0) | PV(b0) with exp(b1) | PV(b1); the fences keep each region's
-      // fragment loads inside it, which bounds the live registers
+  // one probability pair: p = 2^(s - m) for elements 2w2, 2w2 + 1, packed to bf16 into
+  // pw[w2 / 4][w2 % 4], the bf16 values added to the row sum rs
+  auto exp_pair = [&](const f32x16 &sc, int w2, float m, u32x4 (&pw)[2], float &rs) {
+    const float e0 = __builtin_amdgcn_exp2f(sc[2 * w2] - m);
+    const float e1 = __builtin_amdgcn_exp2f(sc[2 * w2 + 1] - m);
+    const uint32_t pk = pack_bf16x2(e0, e1);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, kOnesBf16x2),
+                                         rs, false);
+    // consumed here, so the pair is computed in the unit that asks for it (the copy branches
+    // of group A would otherwise let the compiler sink it to the end of the phase)
+    asm volatile("" ::"v"(rs));
+    pw[w2 >> 2][w2 & 3] = pk;
+  };
+
+  // One key tile: QK(b0) and QK(b1) as two interleaved chains | PV(previous tile) with
+  // exp(b0), exp(b1), the probabilities taken against the running m.  The issue order is written out: each unit is
+  // one MFMA, the operand read kReadsAhead MFMAs ahead and a share of the exponentials, fenced
+  // so the compiler keeps it.  If any row's sum passed the limit, or m was not yet set (the
+  // first tile of a row block gives inf / NaN sums), the tile is redone with the exact maximum
+  // over both blocks: scores recomputed from the still-staged K tile, the state rescaled to the
+  // new maximum, probabilities recomputed.
+  constexpr int NPV = 4 * NCB;               // MFMAs of the P.V product of one tile
+  constexpr int NMF = 2 * NKK + NPV;         // MFMAs of one tile
+  constexpr int NDMA = 4 * DMA_PER_WAVE;     // copy instructions per step of a group-A wave
+  auto pv_of = [&](const char *vd, int r) {  // operand of the r-th P.V MFMA
+    const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
+    return vfrag(vd, jb, t, cb);
+  };
+  // The four tile copies of a step (next K tile and this V^T tile, of each group) as source /
+  // destination pairs; a group-A wave moves its share of each, one instruction every
+  // NMF / NDMA MFMAs, so the copies pass through the vector memory path while the tile's
+  // arithmetic runs instead of stalling every wave at the start of a step.
+  struct Copies {
+    int tile[4];  // K tile, V^T tile, K tile, V^T tile
+    char *dst[4];
+  };
+  auto copy_part = [&](const Copies &c, int r) {
+    const int q = r / DMA_PER_WAVE;
+    const int blk = gw * DMA_PER_WAVE + r % DMA_PER_WAVE;
+    lds_dma16((q & 1) ? vt_buf : kr_buf, dma_lane, (uint32_t)c.tile[q] * TB + blk * 1024, c.dst[q] + blk * 1024);
+  };
+  auto tile = [&](const char *kd, const char *vd, int kb0, bool msk, const Copies &cp) {
+    auto dma_at = [&](int g) {  // after the g-th MFMA of the tile (group A only)
+      if ((g * NDMA) % NMF == 0 && grp == 0) copy_part(cp, g * NDMA / NMF);
+    };
+    // operand reads: phase 1 reads K fragments in MFMA order (k0, k1 alternating blocks), the
+    // last ones of phase 1 fetch the first P.V operands
+    auto k_of = [&](int g) { return kfrag(kd, g & 1, g >> 1); };
+    bf16x8 fr[kReadsAhead];
+#pragma unroll
+    for (int r = 0; r < kReadsAhead; ++r) fr[r] = k_of(r);
+    // phase 1: QK(b0) and QK(b1) as two interleaved accumulation chains
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int g = 0; g < 2 * NKK; ++g) {
+      if (g & 1)
+        s1 = mfma(fr[g % kReadsAhead], qf[g >> 1], s1);
+      else
+        s0 = mfma(fr[g % kReadsAhead], qf[g >> 1], s0);
+      const int nx = g + kReadsAhead;
+      fr[g % kReadsAhead] = nx < 2 * NKK ? k_of(nx) : pv_of(vd, nx - 2 * NKK);
+      dma_at(g);
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s1 = qk(kd, 1);
-      float r0 = expo(s0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (needs_redo(r0)) redo(s0, r0, kd, 0, kb0);
-      l_run += r0;
+    }
+    if (msk) {
+      mask(s0, kb0);
       mask(s1, kb0 + 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 2: PV(previous tile) with exp(b0) and exp(b1)
+    u32x4 pw0[2], pw1[2];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < NPV; ++r) {
+      const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
+      o[cb] = mfma(fr[r % kReadsAhead], pend[jb][t], o[cb]);
+      if (r + kReadsAhead < NPV) fr[r % kReadsAhead] = pv_of(vd, r + kReadsAhead);
+      dma_at(2 * NKK + r);
+#pragma unroll
+      for (int w2 = r * 16 / NPV; w2 < (r + 1) * 16 / NPV; ++w2) {
+        if (w2 < 8)
+          exp_pair(s0, w2, m_run, pw0, rs0);
+        else
+          exp_pair(s1, w2 - 8, m_run, pw1, rs1);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 vf[2][NCB];
-      load_v(vd, 0, vf);
-      pv(s0, vf);
-      float r1 = expo(s1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (needs_redo(r1)) redo(s1, r1, kd, 1, kb0 + 32);
-      l_run += r1;
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(vd, 1, vf);
-      pv(s1, vf);
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      float r0 = expo(s0);
-      if (needs_redo(r0)) redo(s0, r0, kd, 0, kb0);
-      l_run += r0;
-      bf16x8 vf[2][NCB];
-      load_v(vd, 0, vf);
-      pv(s0, vf);
+    }
+    bf16x8 p0[2], p1[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      p0[t] = __builtin_bit_cast(bf16x8, pw0[t]);
+      p1[t] = __builtin_bit_cast(bf16x8, pw1[t]);
+    }
+    if (__builtin_expect(needs_redo(rs0 + rs1), 0)) {
+      asm volatile("" ::: "memory");  // re-read the K fragments from LDS
+      s0 = qk(kd, 0);
+      s1 = qk(kd, 1);
+      if (msk) {
+        mask(s0, kb0);
+        mask(s1, kb0 + 32);
+      }
+      float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+      const float m_new = fmaxf(m_run, max_xor32(mx));
+      // a row with no visible key so far keeps m = -inf and gets zero probabilities
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 when m was unset
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+      m_run = m_new;
+      rs0 = expo_pack(s0, m_use, p0);
+      rs1 = expo_pack(s1, m_use, p1);
+    }
+    l_run += rs0 + rs1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pend[0][t] = p0[t];
+      pend[1][t] = p1[t];
     }
   };
 
-  // ---- main loop: both groups step through their tile lists in lockstep; tile i sits in
-  // buffer i % 2 (unrolled by two so the buffer of every access is known at compile time)
-  auto step = [&](int i, const char *cur, char *nxt) {
-    if (i + 1 < n_mine) stage(i + 1, nxt);
-    if (i < n_mine) {
-      const int seg = i < len0 ? 0 : 1;
-      if (seg != cur_seg) {
-        if (cur_seg == 0) store_seg();
-        begin_seg(seg);
-        cur_seg = seg;
+  // ---- main loop.  Step i: K tile i in ldsk[i%2], V^T tile i-1 in ldsv[(i+1)%2]; copies of
+  // K tile i+1 into ldsk[(i+1)%2] and V^T tile i into ldsv[i%2], issued by the tile, run
+  // meanwhile.  Unrolled by
+  // two so the buffer of every access is known at compile time.  Step n_mine only finishes
+  // the last tile's P.V product; steps after it only wait.
+  auto step = [&](int i, const char *kcur, char *knxt, const char *vprev, char *vfill) {
+    const int go = grp * TB;
+    const int seg = i < n_mine ? (i < len0 ? 0 : 1) : -1;
+    if (seg != cur_seg) {  // new row block, or the end of this group's tiles
+      if (cur_seg >= 0) {
+        pv_pending(vprev + go);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
+        if (cur_seg == 0) store_seg();  // the r_hi block is stored (or merged) after the loop
       }
-      compute_tile(i < len0 ? i : k1s + (i - len0), cur);
+      if (seg >= 0) begin_seg(seg);
+      cur_seg = seg;
+    }
+    // copies of this step: K tile i+1 and V^T tile i of each group.  Indices past a group's
+    // last tile are clamped to it: the copy is then an in-bounds duplicate into a buffer that
+    // group no longer reads.
+    Copies cp;
+    {
+      const int ia = max(min(i, n_a - 1), 0), ia1 = max(min(i + 1, n_a - 1), 0);
+      const int ib = min(i, n_b - 1), ib1 = min(i + 1, n_b - 1);
+      cp.tile[0] = tile_a(ia1);
+      cp.dst[0] = knxt;
+      cp.tile[1] = tile_a(ia);
+      cp.dst[1] = vfill;
+      cp.tile[2] = x + ib1;
+      cp.dst[2] = knxt + TB;
+      cp.tile[3] = x + ib;
+      cp.dst[3] = vfill + TB;
+    }
+    if (seg >= 0) {
+      const int kt = tile_of(i);
+      const int kb0 = kt * BN;
+      const bool msk = (CAUSAL && kb0 + BN - 1 > row0) || kb0 + BN > S;
+      tile(kcur + go, vprev + go, kb0, msk, cp);
+    } else if (grp == 0 && i < n_b) {  // group A is done but B still needs its tiles
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) copy_part(cp, r);
     }
     wait_vm_all();
     __syncthreads();
   };
-  if (n_mine > 0) stage(0, lds0);
+  if (grp == 0) {  // first K tiles of both groups
+    stage(kr_buf, 0, ldsk0);
+    stage(kr_buf, x, ldsk0 + TB);
+  }
   wait_vm_all();
   __syncthreads();
   for (int i = 0; i < n_iter; i += 2) {
-    step(i, lds0, lds1);
-    if (i + 1 < n_iter) step(i + 1, lds1, lds0);
+    step(i, ldsk0, ldsk1, ldsv1, ldsv0);
+    step(i + 1, ldsk1, ldsk0, ldsv0, ldsv1);
   }
 
-  // ---- finish: A stores block r_lo if it still holds it; the split block is merged in B
-  if (grp == 0 && cur_seg == 0) store_seg();
+  // ---- finish: the split block r_hi is merged in B.  The tile buffers are free after the last
+  // barrier: per-wave accumulators of group A go to ldsk0 (waves 0, 1) and ldsk1 (waves 2, 3),
+  // maxima and sums to ldsv0.
   if (x > 0) {
-    float *mo = reinterpret_cast<float *>(lds0);  // tile buffers are free after the last barrier
-    float *mm = reinterpret_cast<float *>(lds1);
+    float *mo = reinterpret_cast<float *>(gw < 2 ? ldsk0 : ldsk1) + (gw & 1) * NCB * 16 * 64;
+    float *mm = reinterpret_cast<float *>(ldsv0);
     if (grp == 0) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mo[((gw * NCB + cb) * 16 + v) * 64 + lane] = o[cb][v];
+        for (int v = 0; v < 16; ++v) mo[(cb * 16 + v) * 64 + lane] = o[cb][v];
       mm[gw * 64 + lane] = m_run;
       mm[256 + gw * 64 + lane] = l_run;
     }
@@ -400,7 +536,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[cb][v] = mo[((gw * NCB + cb) * 16 + v) * 64 + lane] * ca + o[cb][v] * cb_;
+        for (int v = 0; v < 16; ++v) o[cb][v] = mo[(cb * 16 + v) * 64 + lane] * ca + o[cb][v] * cb_;
       m_run = m_new;
     }
   }
