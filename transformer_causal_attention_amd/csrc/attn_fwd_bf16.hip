@@ -43,8 +43,8 @@
 //
 // Pipeline.  Step i of the loop computes the scores and probabilities of key tile i and the
 // P.V product of tile i-1 (whose V^T tile is kept one step longer), so every step has matrix
-// work to overlap with the exponentials: the two 32-key score blocks run as two interleaved
-// MFMA chains, then the P.V product of the previous tile carries the exponentials of both.
+// work to overlap with the exponentials: QK(b0) | QK(b1) with the exponentials of block 0 |
+// the P.V product of the previous tile with the exponentials of block 1.
 // The probabilities of a tile wait in registers, packed to bf16, until the next step.
 //
 // Softmax without a per-block maximum.  The running maximum m only needs to keep 2^(s - m)
@@ -54,8 +54,7 @@
 // its probability sum exceeds 2^64.  The first tile of a row block, tiles on the diagonal and
 // the tile at the sequence end always take the exact maximum.  bf16 and fp32 hold values up to
 // 2^64 with the same relative precision as values below 1, and out = o / l,
-// lse = m + log2 l do not depend on which m was used.  The row sum adds the bf16-rounded
-// probabilities (the values the P.V product sees) with a two-term dot product.
+// lse = m + log2 l do not depend on which m was used.
 
 #include <hip/hip_ext.h>
 
@@ -67,9 +66,7 @@ namespace attn {
 
 constexpr int BN = 64;                      // keys per staged tile
 constexpr float kSumLimit = 1.8446744e19f;  // 2^64: above this a tile is redone exactly
-constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -100,7 +97,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kReadsAhead = 4;  // LDS operand reads kept in flight ahead of the MFMAs
+constexpr int kReadsAhead = 6;  // LDS operand reads kept in flight ahead of the MFMAs
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
@@ -173,10 +170,10 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int k_lane = hh * 1024 + l32 * 16;
   const int v_lane = hh * 16 * D + l32 * 16;
 
-  auto tile_of = [&](int i) { return i < len0 ? i : k1s + (i - len0); };
-  auto tile_a = [&](int i) { return i < len0_a ? i : i - len0_a; };
+  auto tile_of = [&](int i) __attribute__((always_inline)) { return i < len0 ? i : k1s + (i - len0); };
+  auto tile_a = [&](int i) __attribute__((always_inline)) { return i < len0_a ? i : i - len0_a; };
   // this wave's share (DMA_PER_WAVE KiB) of copying tile kt of `buf` to dst
-  auto stage = [&](__amdgpu_buffer_rsrc_t buf, int kt, char *dst) {
+  auto stage = [&](__amdgpu_buffer_rsrc_t buf, int kt, char *dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < DMA_PER_WAVE; ++r) {
       const int blk = gw * DMA_PER_WAVE + r;
@@ -186,9 +183,10 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 
   // ---- state of this wave's 32 rows
   bf16x8 qf[NKK];
-  float m_run = -INFINITY;  // running maximum used for the probabilities (base-2 scores)
+  float m_run = 0.f;        // reference the probabilities are taken against (base-2 scores)
   float l_run = 0.f;        // this lane half's share of the running row sum
   f32x16 o[NCB];
+  f32x16 sc0, sc1;          // scores of the tile awaiting its softmax half
   bf16x8 pend[2][2];        // probabilities of the previous tile, [block][key half]; zero if none
   int row0 = 0, kb_last = -1, cur_seg = -1;
 #pragma unroll
@@ -207,7 +205,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
   }
 
-  auto begin_seg = [&](int seg) {
+  auto begin_seg = [&](int seg) __attribute__((always_inline)) {
     const int R = seg == 0 ? r_lo : r_hi;
     row0 = R * RPB + sub * 32;
     kb_last = row0 >= S ? -1 : (CAUSAL ? min(row0 + 31, S - 1) : S - 1) / 32;
@@ -247,13 +245,15 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       qf[kk] = __builtin_bit_cast(bf16x8, olo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
     }
-    m_run = -INFINITY;
+    // the first tile of a row block always takes the exact maximum, which replaces this
+    // provisional reference before any probability is kept
+    m_run = 0.f;
     l_run = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
   };
 
-  auto store_seg = [&]() {
+  auto store_seg = [&]() __attribute__((always_inline)) {
     const float l_tot = l_run + xor32(l_run);
     const int my_row = row0 + l32;
     if (my_row < S) {
@@ -274,29 +274,21 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   };
 
   // ---- block pieces (kd / vd: this group's K and V^T tile)
-  auto kfrag = [&](const char *kd, int jb, int kk) {
+  auto kfrag = [&](const char *kd, int jb, int kk) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8 *>(kd + k_lane + 2 * kk * 1024 + jb * 512);
   };
-  auto vfrag = [&](const char *vd, int jb, int t, int cb) {
+  auto vfrag = [&](const char *vd, int jb, int t, int cb) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8 *>(vd + v_lane + (4 * jb + 2 * t) * 16 * D + cb * 512);
   };
-  auto qk = [&](const char *kd, int jb) {
-    f32x16 sc = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) sc = mfma(kfrag(kd, jb, kk), qf[kk], sc);
-    return sc;
-  };
-  // O += V^T(previous tile) P^T(previous tile)
-  auto pv_pending = [&](const char *vd) {
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) o[cb] = mfma(vfrag(vd, jb, t, cb), pend[jb][t], o[cb]);
+  constexpr int NPV = 4 * NCB;            // MFMAs of the P.V product of one tile
+  constexpr int NMF = 2 * NKK + NPV;      // MFMAs of one tile
+  constexpr int NDMA = 2 * DMA_PER_WAVE;  // copy instructions per step of a wave (its group's two tiles)
+  auto pv_of = [&](const char *vd, int r) __attribute__((always_inline)) {  // operand of the r-th P.V MFMA
+    const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
+    return vfrag(vd, jb, t, cb);
   };
   // keys after the query or past the sequence end get -inf (only called where some may be)
-  auto mask = [&](f32x16 &sc, int kb0) {
+  auto mask = [&](f32x16 &sc, int kb0) __attribute__((always_inline)) {
     const int my_row = row0 + l32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -304,206 +296,196 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       if ((CAUSAL && j > my_row) || j >= S) sc[v] = -INFINITY;
     }
   };
-  // p = 2^(sc - m) packed to bf16; returns this lane's sum of the bf16-rounded probabilities
-  auto expo_pack = [&](f32x16 &sc, float m, bf16x8 (&pb)[2]) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(sc[v] - m);
-    float rs = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4 pw;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16x2(sc[8 * t + 2 * w], sc[8 * t + 2 * w + 1]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // through a scalar: a bit cast of the vector element itself reads element 0
-        const uint32_t pair = pw[w];
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
-                                             __builtin_bit_cast(bf16x2, kOnesBf16x2), rs, false);
-      }
-      pb[t] = __builtin_bit_cast(bf16x8, pw);
-    }
-    return rs;
-  };
-  auto needs_redo = [&](float rsum) {
+  auto needs_redo = [&](float rsum) __attribute__((always_inline)) {
     return __builtin_amdgcn_ballot_w64(!(rsum <= kSumLimit)) != 0;  // also catches inf and NaN
   };
-
-  // one probability pair: p = 2^(s - m) for elements 2w2, 2w2 + 1, packed to bf16 into
-  // pw[w2 / 4][w2 % 4], the bf16 values added to the row sum rs
-  auto exp_pair = [&](const f32x16 &sc, int w2, float m, u32x4 (&pw)[2], float &rs) {
-    const float e0 = __builtin_amdgcn_exp2f(sc[2 * w2] - m);
-    const float e1 = __builtin_amdgcn_exp2f(sc[2 * w2 + 1] - m);
-    const uint32_t pk = pack_bf16x2(e0, e1);
-    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, kOnesBf16x2),
-                                         rs, false);
-    // consumed here, so the pair is computed in the unit that asks for it (the copy branches
-    // of group A would otherwise let the compiler sink it to the end of the phase)
-    asm volatile("" ::"v"(rs));
-    pw[w2 >> 2][w2 & 3] = pk;
+  auto clear_pend = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
+  };
+  // O += V^T(previous tile) P^T(previous tile) on its own (row-block switches and the drain)
+  auto pv_only = [&](const char *vd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < NPV; ++r) {
+      const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
+      o[cb] = mfma(vfrag(vd, jb, t, cb), pend[jb][t], o[cb]);
+    }
   };
 
-  // One key tile: QK(b0) and QK(b1) as two interleaved chains | PV(previous tile) with
-  // exp(b0), exp(b1), the probabilities taken against the running m.  The issue order is written out: each unit is
-  // one MFMA, the operand read kReadsAhead MFMAs ahead and a share of the exponentials, fenced
-  // so the compiler keeps it.  If any row's sum passed the limit, or m was not yet set (the
-  // first tile of a row block gives inf / NaN sums), the tile is redone with the exact maximum
-  // over both blocks: scores recomputed from the still-staged K tile, the state rescaled to the
-  // new maximum, probabilities recomputed.
-  constexpr int NPV = 4 * NCB;               // MFMAs of the P.V product of one tile
-  constexpr int NMF = 2 * NKK + NPV;         // MFMAs of one tile
-  constexpr int NDMA = 4 * DMA_PER_WAVE;     // copy instructions per step of a group-A wave
-  auto pv_of = [&](const char *vd, int r) {  // operand of the r-th P.V MFMA
-    const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
-    return vfrag(vd, jb, t, cb);
-  };
-  // The four tile copies of a step (next K tile and this V^T tile, of each group) as source /
-  // destination pairs; a group-A wave moves its share of each, one instruction every
-  // NMF / NDMA MFMAs, so the copies pass through the vector memory path while the tile's
-  // arithmetic runs instead of stalling every wave at the start of a step.
+  // The two tile copies of a step for a group (its next K tile and this step's V^T tile); the
+  // group's waves move their share of each, one instruction at a time between softmax work.
   struct Copies {
-    int tile[4];  // K tile, V^T tile, K tile, V^T tile
-    char *dst[4];
+    int tile[2];  // K tile, V^T tile
+    char *dst[2];
   };
-  auto copy_part = [&](const Copies &c, int r) {
+  auto copy_part = [&](const Copies &c, int r) __attribute__((always_inline)) {
     const int q = r / DMA_PER_WAVE;
     const int blk = gw * DMA_PER_WAVE + r % DMA_PER_WAVE;
     lds_dma16((q & 1) ? vt_buf : kr_buf, dma_lane, (uint32_t)c.tile[q] * TB + blk * 1024, c.dst[q] + blk * 1024);
   };
-  auto tile = [&](const char *kd, const char *vd, int kb0, bool msk, const Copies &cp) {
-    auto dma_at = [&](int g) {  // after the g-th MFMA of the tile (group A only)
-      if ((g * NDMA) % NMF == 0 && grp == 0) copy_part(cp, g * NDMA / NMF);
+
+  // ---- one key tile per step: QK(b0) | QK(b1) with the probabilities of block 0 | P.V of the
+  // previous tile with the probabilities of block 1, operand reads kReadsAhead MFMAs ahead, one
+  // fenced unit per MFMA so the issue order is the one written here.  The probabilities are
+  // taken against m as it stands; the 16 pairs of scores (8 per block) go through two stages a
+  // pair apart (exponentials of pair w; packing of pair w-1 to bf16 and its addition to the row
+  // sums), so no instruction waits on the one before it.  Row sums use plain VALU adds: the
+  // bf16 dot-product instruction would queue behind MFMAs.  Each wave also issues its share
+  // of its group's copies for the step (the next K tile, this step's V^T tile), one every
+  // NMF / NDMA MFMAs.  Afterwards the tile is redone against its exact maximum when it is the
+  // first of its row block or a row's sum passed the limit, from the scores still in registers.
+  auto tile = [&](const char *kd, const char *vd, int kb0, bool msk, bool first, bool issue,
+                  const Copies &cp) __attribute__((always_inline)) {
+    auto op_of = [&](int g) __attribute__((always_inline)) {
+      return g < NKK ? kfrag(kd, 0, g) : g < 2 * NKK ? kfrag(kd, 1, g - NKK) : pv_of(vd, g - 2 * NKK);
     };
-    // operand reads: phase 1 reads K fragments in MFMA order (k0, k1 alternating blocks), the
-    // last ones of phase 1 fetch the first P.V operands
-    auto k_of = [&](int g) { return kfrag(kd, g & 1, g >> 1); };
     bf16x8 fr[kReadsAhead];
 #pragma unroll
-    for (int r = 0; r < kReadsAhead; ++r) fr[r] = k_of(r);
-    // phase 1: QK(b0) and QK(b1) as two interleaved accumulation chains
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    for (int r = 0; r < kReadsAhead; ++r) fr[r] = op_of(r);
+    auto unit_tail = [&](int g) __attribute__((always_inline)) {
+      if (g + kReadsAhead < NMF) fr[g % kReadsAhead] = op_of(g + kReadsAhead);
+      if ((g * NDMA) % NMF == NMF - NDMA && issue) copy_part(cp, g * NDMA / NMF);
+    };
+    u32x4 pw0[2], pw1[2];
+    float rsum[4];
+    float ex0 = 0.f, ex1 = 0.f;  // exponentials of the pair in flight
+    float rs0 = 0.f, rs1 = 0.f;
+    auto sc_of = [&](int w, int e) __attribute__((always_inline)) {
+      return w < 8 ? sc0[2 * w + e] : sc1[2 * (w - 8) + e];
+    };
+    auto pair_stage = [&](int w, float sh) __attribute__((always_inline)) {  // w = 0 .. 16
+      if (w >= 1) {  // pair w-1: packed to bf16, added to its row sums
+        const int c = w - 1;
+        const uint32_t pk = pack_bf16x2(ex0, ex1);
+        if (c < 8)
+          pw0[c >> 2][c & 3] = pk;
+        else
+          pw1[(c - 8) >> 2][(c - 8) & 3] = pk;
+        rsum[2 * (c >> 3)] += ex0;
+        rsum[2 * (c >> 3) + 1] += ex1;
+      }
+      if (w <= 15) {  // pair w: exponentials
+        ex0 = __builtin_amdgcn_exp2f(sc_of(w, 0) - sh);
+        ex1 = __builtin_amdgcn_exp2f(sc_of(w, 1) - sh);
+      }
+    };
+    auto pin = [&]() __attribute__((always_inline)) {
+      // consumed here, so each unit's share of the pipeline stays in its place
+      asm volatile("" ::"v"(ex0), "v"(ex1), "v"(rsum[0]), "v"(rsum[1]), "v"(rsum[2]), "v"(rsum[3]));
+    };
 #pragma unroll
-    for (int g = 0; g < 2 * NKK; ++g) {
-      if (g & 1)
-        s1 = mfma(fr[g % kReadsAhead], qf[g >> 1], s1);
-      else
-        s0 = mfma(fr[g % kReadsAhead], qf[g >> 1], s0);
-      const int nx = g + kReadsAhead;
-      fr[g % kReadsAhead] = nx < 2 * NKK ? k_of(nx) : pv_of(vd, nx - 2 * NKK);
-      dma_at(g);
+    for (int r = 0; r < 4; ++r) rsum[r] = 0.f;
+    const float sh = m_run;
+    // phase 1: QK(b0)
+    sc0 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      sc0 = mfma(fr[kk % kReadsAhead], qf[kk], sc0);
+      unit_tail(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (msk) {
-      mask(s0, kb0);
-      mask(s1, kb0 + 32);
-    }
+    if (msk) mask(sc0, kb0);
     __builtin_amdgcn_sched_barrier(0);
-    // phase 2: PV(previous tile) with exp(b0) and exp(b1)
-    u32x4 pw0[2], pw1[2];
-    float rs0 = 0.f, rs1 = 0.f;
+    // phase 2: QK(b1) with the probabilities of block 0
+    sc1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int g = NKK + kk;
+      sc1 = mfma(fr[g % kReadsAhead], qf[kk], sc1);
+      unit_tail(g);
+#pragma unroll
+      for (int w = kk * 8 / NKK; w < (kk + 1) * 8 / NKK; ++w) pair_stage(w, sh);
+      pin();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (msk) mask(sc1, kb0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 3: P.V of the previous tile with the probabilities of block 1
 #pragma unroll
     for (int r = 0; r < NPV; ++r) {
+      const int g = 2 * NKK + r;
       const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
-      o[cb] = mfma(fr[r % kReadsAhead], pend[jb][t], o[cb]);
-      if (r + kReadsAhead < NPV) fr[r % kReadsAhead] = pv_of(vd, r + kReadsAhead);
-      dma_at(2 * NKK + r);
+      o[cb] = mfma(fr[g % kReadsAhead], pend[jb][t], o[cb]);
+      unit_tail(g);
 #pragma unroll
-      for (int w2 = r * 16 / NPV; w2 < (r + 1) * 16 / NPV; ++w2) {
-        if (w2 < 8)
-          exp_pair(s0, w2, m_run, pw0, rs0);
-        else
-          exp_pair(s1, w2 - 8, m_run, pw1, rs1);
-      }
+      for (int w = 8 + r * 9 / NPV; w < 8 + (r + 1) * 9 / NPV; ++w) pair_stage(w, sh);
+      pin();
       __builtin_amdgcn_sched_barrier(0);
     }
-    bf16x8 p0[2], p1[2];
+    rs0 = rsum[0] + rsum[1];
+    rs1 = rsum[2] + rsum[3];
+    if (first || needs_redo(rs0 + rs1)) {
+      float mx = fmaxf(sc0[0], sc1[0]);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      p0[t] = __builtin_bit_cast(bf16x8, pw0[t]);
-      p1[t] = __builtin_bit_cast(bf16x8, pw1[t]);
-    }
-    if (__builtin_expect(needs_redo(rs0 + rs1), 0)) {
-      asm volatile("" ::: "memory");  // re-read the K fragments from LDS
-      s0 = qk(kd, 0);
-      s1 = qk(kd, 1);
-      if (msk) {
-        mask(s0, kb0);
-        mask(s1, kb0 + 32);
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sc0[v], sc1[v]));
+      mx = max_xor32(mx);
+      // The first tile of a row block replaces the provisional reference (its state is still
+      // empty, so nothing is rescaled); later the reference only grows, so every rescale factor
+      // is at most 1.  A row with no visible key keeps its reference.
+      float shift, alpha;
+      if (first) {
+        shift = mx == -INFINITY ? m_run : mx;
+        alpha = 0.f;
+      } else {
+        shift = fmaxf(m_run, mx);
+        alpha = __builtin_amdgcn_exp2f(m_run - shift);
       }
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-      const float m_new = fmaxf(m_run, max_xor32(mx));
-      // a row with no visible key so far keeps m = -inf and gets zero probabilities
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 when m was unset
       l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-      m_run = m_new;
-      rs0 = expo_pack(s0, m_use, p0);
-      rs1 = expo_pack(s1, m_use, p1);
+      m_run = shift;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rsum[r] = 0.f;
+#pragma unroll
+      for (int w = 0; w <= 16; ++w) pair_stage(w, shift);
+      rs0 = rsum[0] + rsum[1];
+      rs1 = rsum[2] + rsum[3];
     }
     l_run += rs0 + rs1;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      pend[0][t] = p0[t];
-      pend[1][t] = p1[t];
+      pend[0][t] = __builtin_bit_cast(bf16x8, pw0[t]);
+      pend[1][t] = __builtin_bit_cast(bf16x8, pw1[t]);
     }
   };
 
-  // ---- main loop.  Step i: K tile i in ldsk[i%2], V^T tile i-1 in ldsv[(i+1)%2]; copies of
-  // K tile i+1 into ldsk[(i+1)%2] and V^T tile i into ldsv[i%2], issued by the tile, run
-  // meanwhile.  Unrolled by
-  // two so the buffer of every access is known at compile time.  Step n_mine only finishes
-  // the last tile's P.V product; steps after it only wait.
-  auto step = [&](int i, const char *kcur, char *knxt, const char *vprev, char *vfill) {
+  // ---- main loop.  Step i: K tile i in ldsk[i%2], V^T tile i-1 in ldsv[(i+1)%2]; the copies
+  // of K tile i+1 into ldsk[(i+1)%2] and V^T tile i into ldsv[i%2], issued by the tile, run
+  // meanwhile.  Unrolled by two so the buffer of every access is known at compile time.
+  auto step = [&](int i, const char *kcur, char *knxt, const char *vprev, char *vfill) __attribute__((always_inline)) {
     const int go = grp * TB;
-    const int seg = i < n_mine ? (i < len0 ? 0 : 1) : -1;
-    if (seg != cur_seg) {  // new row block, or the end of this group's tiles
-      if (cur_seg >= 0) {
-        pv_pending(vprev + go);
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
-        if (cur_seg == 0) store_seg();  // the r_hi block is stored (or merged) after the loop
-      }
-      if (seg >= 0) begin_seg(seg);
-      cur_seg = seg;
-    }
-    // copies of this step: K tile i+1 and V^T tile i of each group.  Indices past a group's
-    // last tile are clamped to it: the copy is then an in-bounds duplicate into a buffer that
-    // group no longer reads.
+    // this group's copies: K tile i+1 and V^T tile i (an index past the group's last tile is
+    // clamped to it: an in-bounds duplicate into a buffer the group no longer reads)
     Copies cp;
-    {
-      const int ia = max(min(i, n_a - 1), 0), ia1 = max(min(i + 1, n_a - 1), 0);
-      const int ib = min(i, n_b - 1), ib1 = min(i + 1, n_b - 1);
-      cp.tile[0] = tile_a(ia1);
-      cp.dst[0] = knxt;
-      cp.tile[1] = tile_a(ia);
-      cp.dst[1] = vfill;
-      cp.tile[2] = x + ib1;
-      cp.dst[2] = knxt + TB;
-      cp.tile[3] = x + ib;
-      cp.dst[3] = vfill + TB;
-    }
-    if (seg >= 0) {
-      const int kt = tile_of(i);
-      const int kb0 = kt * BN;
+    cp.tile[0] = tile_of(max(min(i + 1, n_mine - 1), 0));
+    cp.dst[0] = knxt + go;
+    cp.tile[1] = tile_of(max(min(i, n_mine - 1), 0));
+    cp.dst[1] = vfill + go;
+    if (i < n_mine) {
+      const int seg = i < len0 ? 0 : 1;
+      if (seg != cur_seg) {  // new row block: finish the previous one, load the new one
+        if (cur_seg >= 0) {
+          pv_only(vprev + go);
+          clear_pend();
+          store_seg();
+        }
+        begin_seg(seg);
+        cur_seg = seg;
+      }
+      const int kb0 = tile_of(i) * BN;
       const bool msk = (CAUSAL && kb0 + BN - 1 > row0) || kb0 + BN > S;
-      tile(kcur + go, vprev + go, kb0, msk, cp);
-    } else if (grp == 0 && i < n_b) {  // group A is done but B still needs its tiles
-#pragma unroll
-      for (int r = 0; r < NDMA; ++r) copy_part(cp, r);
+      tile(kcur + go, vprev + go, kb0, msk, i == 0 || i == len0, true, cp);
+    } else if (i == n_mine && cur_seg >= 0) {  // the last tile's P.V product
+      pv_only(vprev + go);
+      clear_pend();
+      if (cur_seg == 0) store_seg();  // r_lo was group A's only block (r_hi is merged after)
     }
     wait_vm_all();
     __syncthreads();
   };
-  if (grp == 0) {  // first K tiles of both groups
-    stage(kr_buf, 0, ldsk0);
-    stage(kr_buf, x, ldsk0 + TB);
-  }
+  if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
   wait_vm_all();
   __syncthreads();
   for (int i = 0; i < n_iter; i += 2) {
