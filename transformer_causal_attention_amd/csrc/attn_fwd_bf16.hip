@@ -47,14 +47,13 @@
 // the P.V product of the previous tile with the exponentials of block 1.
 // The probabilities of a tile wait in registers, packed to bf16, until the next step.
 //
-// Softmax without a per-block maximum.  The running maximum m only needs to keep 2^(s - m)
-// finite: interior tiles take probabilities against m as it stands (the QK accumulation starts
-// from -m, so the products come out already shifted), and a tile is re-done with an exact
-// maximum (scores recomputed from the still-staged K tile, accumulator and sum rescaled) only if
-// its probability sum exceeds 2^64.  The first tile of a row block, tiles on the diagonal and
-// the tile at the sequence end always take the exact maximum.  bf16 and fp32 hold values up to
-// 2^64 with the same relative precision as values below 1, and out = o / l,
-// lse = m + log2 l do not depend on which m was used.
+// Softmax without a per-tile maximum.  The reference m that probabilities are taken against
+// only needs to keep 2^(s - m) finite: the first tile of a row block sets m to its exact row
+// maximum, later tiles take their probabilities against m as it stands, and a tile is redone
+// (from its scores, still in registers) against max(m, its row maximum), with the accumulator
+// and sum rescaled by 2^(m_old - m_new) <= 1, only if some row's probability sum passed 2^64 or
+// is not finite.  bf16 and fp32 hold values up to 2^64 with the same relative precision as
+// values below 1, and out = o / l, lse = m + log2 l do not depend on which m was used.
 
 #include <hip/hip_ext.h>
 

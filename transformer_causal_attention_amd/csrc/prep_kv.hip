@@ -30,7 +30,6 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
   __shared__ double freq[D / 2];
   __shared__ __attribute__((aligned(16))) uint16_t vs[64 * VSTR];
   const int tid = threadIdx.x;
-  if (tid < D / 2) freq[tid] = tab.rev[tid];
 
   const int n_tiles = p.S_pad / 64;
   const int unit = blockIdx.x / n_tiles;  // (b, g)
@@ -41,45 +40,60 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
   const __bf16 *ksrc = p.k + ((size_t)b * p.S * p.Hkv + g) * D;
   const __bf16 *vsrc = p.v + ((size_t)b * p.S * p.Hkv + g) * D;
 
+  // Every load of the tile is issued before any of them is used, so the block waits for memory
+  // once.  Rows past S load row S-1 (in bounds) and are replaced by zeros afterwards.
+  // Keys: 64 keys x D/16 pairs of 8-dimension chunks (c, c + D/2); lanes walk keys, so each
+  // chunk row of the tile is written contiguously.
+  constexpr int NKI = D / 64;  // key items per thread
+  constexpr int NVI = D / 32;  // value items per thread: 64 rows x D/8 chunks
+  u32x4 kl[NKI], kh[NKI], vv[NVI];
+#pragma unroll
+  for (int it = 0; it < NKI; ++it) {
+    const int item = tid + 256 * it;
+    const int j = min(j0 + item % 64, p.S - 1);
+    const __bf16 *src = ksrc + (size_t)j * src_rs + 8 * (item / 64);
+    kl[it] = *reinterpret_cast<const u32x4 *>(src);
+    kh[it] = *reinterpret_cast<const u32x4 *>(src + D / 2);
+  }
+#pragma unroll
+  for (int it = 0; it < NVI; ++it) {
+    const int item = tid + 256 * it;
+    const int j = min(j0 + item / (D / 8), p.S - 1);
+    vv[it] = *reinterpret_cast<const u32x4 *>(vsrc + (size_t)j * src_rs + 8 * (item % (D / 8)));
+  }
+  if (tid < D / 2) freq[tid] = tab.rev[tid];
   // values -> LDS (zeros past S)
 #pragma unroll
-  for (int it = 0; it < D / 32; ++it) {
-    const int item = tid + 256 * it;  // 64 rows x D/8 chunks
+  for (int it = 0; it < NVI; ++it) {
+    const int item = tid + 256 * it;
     const int row = item / (D / 8);
-    const int cc = item % (D / 8);
-    const int j = j0 + row;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (j < p.S) w = *reinterpret_cast<const u32x4 *>(vsrc + (size_t)j * src_rs + 8 * cc);
-    *reinterpret_cast<u32x4 *>(vs + row * VSTR + 8 * cc) = w;
+    const u32x4 w = j0 + row < p.S ? vv[it] : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(vs + row * VSTR + 8 * (item % (D / 8))) = w;
   }
-  __syncthreads();
+  __syncthreads();  // frequencies and staged values visible to every thread
 
   const size_t tile = ((size_t)b * p.Hkv + g) * n_tiles + (size_t)(j0 / 64);
   char *kdst = reinterpret_cast<char *>(p.kr) + tile * (64 * D * 2);
   char *vdst = reinterpret_cast<char *>(p.vt) + tile * (64 * D * 2);
 
-  // rotated keys: 64 keys x D/16 pairs of 8-dimension chunks (c, c + D/2); lanes walk keys so
-  // each chunk row of the tile is written contiguously
+  // rotated keys
 #pragma unroll
-  for (int it = 0; it < D / 64; ++it) {
+  for (int it = 0; it < NKI; ++it) {
     const int item = tid + 256 * it;
     const int row = item % 64;
     const int cp = item / 64;  // chunk of the first half: dims 8cp .. 8cp+7
     const int c0 = 8 * cp;
     const int j = j0 + row;
     u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (j < p.S) {
-      const __bf16 *src = ksrc + (size_t)j * src_rs;
-      const u32x4 xl = *reinterpret_cast<const u32x4 *>(src + c0);
-      const u32x4 xh = *reinterpret_cast<const u32x4 *>(src + c0 + D / 2);
+    if (j < p.S) {  // keys past S stay zero
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float t0 = turn_fraction(j, freq[c0 + 2 * w]);
         const float t1 = turn_fraction(j, freq[c0 + 2 * w + 1]);
         const float s0 = __builtin_amdgcn_sinf(t0), cs0 = __builtin_amdgcn_cosf(t0);
         const float s1 = __builtin_amdgcn_sinf(t1), cs1 = __builtin_amdgcn_cosf(t1);
-        const float x0 = bf16_lo(xl[w]), x1 = bf16_hi(xl[w]);
-        const float y0 = bf16_lo(xh[w]), y1 = bf16_hi(xh[w]);
+        const float x0 = bf16_lo(kl[it][w]), x1 = bf16_hi(kl[it][w]);
+        const float y0 = bf16_lo(kh[it][w]), y1 = bf16_hi(kh[it][w]);
         lo[w] = pack_bf16x2(x0 * cs0 - y0 * s0, x1 * cs1 - y1 * s1);
         hi[w] = pack_bf16x2(y0 * cs0 + x0 * s0, y1 * cs1 + x1 * s1);
       }
