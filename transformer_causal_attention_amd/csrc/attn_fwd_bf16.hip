@@ -96,7 +96,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kReadsAhead = 6;  // LDS operand reads kept in flight ahead of the MFMAs
+constexpr int kReadsAhead = 5;  // LDS operand reads kept in flight ahead of the MFMAs
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
@@ -109,11 +109,12 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   __shared__ __attribute__((aligned(1024))) char ldsk1[2 * TB];
   __shared__ __attribute__((aligned(1024))) char ldsv0[2 * TB];
   __shared__ __attribute__((aligned(1024))) char ldsv1[2 * TB];
-  // rotation frequencies, read per row block from LDS rather than held in registers
-  __shared__ double freq[D / 2];
+  // Rotated queries of group B's row block, handed to group A when A moves on to that block
+  // (same rows and heads, wave for wave); before that, the rotation frequencies.
+  __shared__ __attribute__((aligned(1024))) char ldsq[4 * NKK * 1024];
+  double *freq = reinterpret_cast<double *>(ldsq);
 
   const int tid = threadIdx.x;
-  if (tid < D / 2) freq[tid] = tab.rev[tid];
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int grp = wave >> 2;
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   f32x16 o[NCB];
   f32x16 sc0, sc1;          // scores of the tile awaiting its softmax half
   bf16x8 pend[2][2];        // probabilities of the previous tile, [block][key half]; zero if none
-  int row0 = 0, kb_last = -1, cur_seg = -1;
+  int row0 = 0, cur_seg = -1;
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
@@ -204,12 +205,12 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
   }
 
-  auto begin_seg = [&](int seg) __attribute__((always_inline)) {
-    const int R = seg == 0 ? r_lo : r_hi;
-    row0 = R * RPB + sub * 32;
-    kb_last = row0 >= S ? -1 : (CAUSAL ? min(row0 + 31, S - 1) : S - 1) / 32;
+  // ---- row blocks: rows, raw query loads, rotation, fresh state
+  auto seg_rows = [&](int seg) __attribute__((always_inline)) {
+    row0 = (seg == 0 ? r_lo : r_hi) * RPB + sub * 32;
+  };
+  auto load_q = [&](u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
     const int my_row = row0 + l32;
-    u32x4 raw[NKK];
     if (my_row < S) {
       const __bf16 *src = p.q + (((size_t)b * S + my_row) * p.Hq + head) * D + 8 * hh;
 #pragma unroll
@@ -218,6 +219,9 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) raw[kk] = u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto rotate_q = [&](const u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
+    const int my_row = row0 + l32;
     // rotate pairs (c, c + D/2): lane holds columns 16kk + 8hh + e in raw[kk], kk < NKK/2
 #pragma unroll
     for (int kk = 0; kk < NKK / 2; ++kk) {
@@ -244,6 +248,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       qf[kk] = __builtin_bit_cast(bf16x8, olo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
     }
+  };
+  auto reset_seg = [&]() __attribute__((always_inline)) {
     // the first tile of a row block always takes the exact maximum, which replaces this
     // provisional reference before any probability is kept
     m_run = 0.f;
@@ -251,13 +257,23 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
   };
+  // the hand-off slot of wave gw: NKK rows of 64 lanes x 16 bytes (the lane offset is made
+  // opaque where it is used, so no address is kept live across the loop)
+  auto q_slot = [&]() __attribute__((always_inline)) {
+    uint32_t lo = dma_lane;
+    asm volatile("" : "+v"(lo));
+    return ldsq + gw * NKK * 1024 + lo;
+  };
 
   auto store_seg = [&]() __attribute__((always_inline)) {
     const float l_tot = l_run + xor32(l_run);
-    const int my_row = row0 + l32;
+    // lane indices made opaque, so no per-lane part of the addresses is kept live across the loop
+    int lr = l32, lh = hh;
+    asm volatile("" : "+v"(lr), "+v"(lh));
+    const int my_row = row0 + lr;
     if (my_row < S) {
       const float inv = 1.0f / l_tot;
-      __bf16 *dst = p.out + (((size_t)b * S + my_row) * p.Hq + head) * D + 4 * hh;
+      __bf16 *dst = p.out + (((size_t)b * S + my_row) * p.Hq + head) * D + 4 * lh;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -267,7 +283,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
           w2[1] = pack_bf16x2(o[cb][4 * a + 2] * inv, o[cb][4 * a + 3] * inv);
           *reinterpret_cast<u32x2 *>(dst + 32 * cb + 8 * a) = w2;
         }
-      if (hh == 0)
+      if (lh == 0)
         p.lse[((size_t)b * p.Hq + head) * S + my_row] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     }
   };
@@ -463,15 +479,15 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     cp.tile[1] = tile_of(max(min(i, n_mine - 1), 0));
     cp.dst[1] = vfill + go;
     if (i < n_mine) {
-      const int seg = i < len0 ? 0 : 1;
-      if (seg != cur_seg) {  // new row block: finish the previous one, load the new one
-        if (cur_seg >= 0) {
-          pv_only(vprev + go);
-          clear_pend();
-          store_seg();
-        }
-        begin_seg(seg);
-        cur_seg = seg;
+      if (i == len0 && len0 > 0) {  // group A: block r_lo is done, continue with block r_hi
+        pv_only(vprev + go);
+        clear_pend();
+        store_seg();
+        seg_rows(1);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(q_slot() + kk * 1024);
+        reset_seg();
+        cur_seg = 1;
       }
       const int kb0 = tile_of(i) * BN;
       const bool msk = (CAUSAL && kb0 + BN - 1 > row0) || kb0 + BN > S;
@@ -484,9 +500,26 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     wait_vm_all();
     __syncthreads();
   };
-  if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
-  wait_vm_all();
-  __syncthreads();
+  // ---- prologue: the first row block's queries are loaded while the first K tile is copied;
+  // then rotated, and group B leaves its rotated queries in its hand-off slot for group A
+  // (read at A's switch to block r_hi, at step len0 >= 1, so after at least one barrier).
+  {
+    seg_rows(len0 > 0 ? 0 : 1);
+    cur_seg = n_mine > 0 ? (len0 > 0 ? 0 : 1) : -1;
+    u32x4 raw[NKK];
+    load_q(raw);
+    if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
+    if (tid < D / 2) freq[tid] = tab.rev[tid];
+    wait_vm_all();
+    __syncthreads();
+    rotate_q(raw);
+    reset_seg();
+    __syncthreads();  // the frequencies are no longer read: the slots may be written
+    if (grp == 1) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) *reinterpret_cast<bf16x8 *>(q_slot() + kk * 1024) = qf[kk];
+    }
+  }
   for (int i = 0; i < n_iter; i += 2) {
     step(i, ldsk0, ldsk1, ldsv1, ldsv0);
     step(i + 1, ldsk1, ldsk0, ldsv0, ldsv1);
