@@ -36,10 +36,10 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "72332a7d63ffd23b", "FETCH_SIZE_KiB": 12484.7, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "72332a7d63ffd23b", "FETCH_SIZE_KiB": 6272.25, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "72332a7d63ffd23b", "FETCH_SIZE_KiB": 33786.16, "WRITE_SIZE_KiB": 16896.22},
-    "long_shard": {"sources_sha256": "72332a7d63ffd23b", "FETCH_SIZE_KiB": 1149646.73, "WRITE_SIZE_KiB": 266240.22},
+    "llama3_8b": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 12466.14, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 6271.14, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 33153.75, "WRITE_SIZE_KiB": 16899.43},
+    "long_shard": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 1080735.17, "WRITE_SIZE_KiB": 266240.0},
 }
 
 

@@ -96,7 +96,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kReadsAhead = 5;  // LDS operand reads kept in flight ahead of the MFMAs
+constexpr int kReadsAhead = 6;  // LDS operand reads kept in flight ahead of the MFMAs
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
@@ -137,20 +137,19 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int t_lo = ((CAUSAL ? min(S, (r_lo + 1) * RPB) : S) + BN - 1) / BN;
   const int t_hi = ((CAUSAL ? min(S, (r_hi + 1) * RPB) : S) + BN - 1) / BN;
   const bool two = r_lo != r_hi;
-  const int x = two ? (t_hi - t_lo) / 2 : t_hi / 2;  // key tiles of block r_hi run by group A
-  // group A: segment 0 = (r_lo, tiles [0, t_lo)) when two, then segment 1 = (r_hi, [0, x));
-  // group B: segment 1 = (r_hi, [x, t_hi)).
+  // Steps of a group.  Group A: the t_lo tiles of block r_lo (when two), then tiles [0, x) of
+  // block r_hi; group B: tiles [x, t_hi) of block r_hi, with x balancing the two.  Inside the
+  // loop every update of the accumulators goes through the one tile body (a second one makes
+  // the compiler copy them every step): at A's switch the tile of block r_hi's first key tile
+  // also adds the P.V product of block r_lo's last one, and the last tile's P.V product is
+  // added after the loop.
+  const int x = two ? (t_hi - t_lo) / 2 : t_hi / 2;  // tiles of block r_hi run by group A
   const int len0 = (grp == 0 && two) ? t_lo : 0;
   const int k1s = grp == 0 ? 0 : x;
   const int n_mine = len0 + (grp == 0 ? x : t_hi - x);
-  // group A issues the tile copies of both groups (it finishes its tiles first and would
-  // otherwise wait at the barrier); group B's tile list is x, x+1, ..., t_hi-1
-  const int len0_a = two ? t_lo : 0;
-  const int n_a = len0_a + x;
-  const int n_b = t_hi - x;
-  // one extra step drains the last tile's P.V product; rounded up to even (the loop body is
-  // two steps, and steps past a group's last tile only wait at the barrier)
-  const int n_iter = (max((two ? t_lo : 0) + x, t_hi - x) + 2) & ~1;
+  // rounded up to even (the loop body is two steps; steps after a group's last tile only wait
+  // at the barrier)
+  const int n_iter = (max((two ? t_lo : 0) + x, t_hi - x) + 1) & ~1;
 
   const int head = g * p.G + hg * p.hpw + (gw % p.hpw);
   const int sub = gw / p.hpw;
@@ -171,7 +170,6 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int v_lane = hh * 16 * D + l32 * 16;
 
   auto tile_of = [&](int i) __attribute__((always_inline)) { return i < len0 ? i : k1s + (i - len0); };
-  auto tile_a = [&](int i) __attribute__((always_inline)) { return i < len0_a ? i : i - len0_a; };
   // this wave's share (DMA_PER_WAVE KiB) of copying tile kt of `buf` to dst
   auto stage = [&](__amdgpu_buffer_rsrc_t buf, int kt, char *dst) __attribute__((always_inline)) {
 #pragma unroll
@@ -265,12 +263,13 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     return ldsq + gw * NKK * 1024 + lo;
   };
 
-  auto store_seg = [&]() __attribute__((always_inline)) {
-    const float l_tot = l_run + xor32(l_run);
+  // out and lse of the rows starting at r0 from o, this lane half's sum l_half and reference m
+  auto store_seg = [&](int r0, float l_half, float m) __attribute__((always_inline)) {
+    const float l_tot = l_half + xor32(l_half);
     // lane indices made opaque, so no per-lane part of the addresses is kept live across the loop
     int lr = l32, lh = hh;
     asm volatile("" : "+v"(lr), "+v"(lh));
-    const int my_row = row0 + lr;
+    const int my_row = r0 + lr;
     if (my_row < S) {
       const float inv = 1.0f / l_tot;
       __bf16 *dst = p.out + (((size_t)b * S + my_row) * p.Hq + head) * D + 4 * lh;
@@ -284,7 +283,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
           *reinterpret_cast<u32x2 *>(dst + 32 * cb + 8 * a) = w2;
         }
       if (lh == 0)
-        p.lse[((size_t)b * p.Hq + head) * S + my_row] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+        p.lse[((size_t)b * p.Hq + head) * S + my_row] = (m + __log2f(l_tot)) * 0.69314718055994531f;
     }
   };
 
@@ -314,21 +313,6 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   auto needs_redo = [&](float rsum) __attribute__((always_inline)) {
     return __builtin_amdgcn_ballot_w64(!(rsum <= kSumLimit)) != 0;  // also catches inf and NaN
   };
-  auto clear_pend = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
-  };
-  // O += V^T(previous tile) P^T(previous tile) on its own (row-block switches and the drain)
-  auto pv_only = [&](const char *vd) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < NPV; ++r) {
-      const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
-      o[cb] = mfma(vfrag(vd, jb, t, cb), pend[jb][t], o[cb]);
-    }
-  };
-
   // The two tile copies of a step for a group (its next K tile and this step's V^T tile); the
   // group's waves move their share of each, one instruction at a time between softmax work.
   struct Copies {
@@ -440,9 +424,9 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       // empty, so nothing is rescaled); later the reference only grows, so every rescale factor
       // is at most 1.  A row with no visible key keeps its reference.
       float shift, alpha;
-      if (first) {
+      if (first) {  // o is zero, or at group A's switch block r_lo's accumulator: kept as is
         shift = mx == -INFINITY ? m_run : mx;
-        alpha = 0.f;
+        alpha = 1.f;
       } else {
         shift = fmaxf(m_run, mx);
         alpha = __builtin_amdgcn_exp2f(m_run - shift);
@@ -479,23 +463,28 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     cp.tile[1] = tile_of(max(min(i, n_mine - 1), 0));
     cp.dst[1] = vfill + go;
     if (i < n_mine) {
-      if (i == len0 && len0 > 0) {  // group A: block r_lo is done, continue with block r_hi
-        pv_only(vprev + go);
-        clear_pend();
-        store_seg();
+      // group A's switch: this tile is block r_hi's first, its P.V product block r_lo's last;
+      // r_lo's sum and reference are kept aside until that product is in o
+      const bool sw_now = i == len0 && len0 > 0;
+      float l_lo = 0.f, m_lo = 0.f;
+      if (sw_now) {
+        l_lo = l_run;
+        m_lo = m_run;
         seg_rows(1);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(q_slot() + kk * 1024);
-        reset_seg();
+        l_run = 0.f;
+        m_run = 0.f;  // provisional, replaced by the first tile's exact maximum
         cur_seg = 1;
       }
       const int kb0 = tile_of(i) * BN;
       const bool msk = (CAUSAL && kb0 + BN - 1 > row0) || kb0 + BN > S;
       tile(kcur + go, vprev + go, kb0, msk, i == 0 || i == len0, true, cp);
-    } else if (i == n_mine && cur_seg >= 0) {  // the last tile's P.V product
-      pv_only(vprev + go);
-      clear_pend();
-      if (cur_seg == 0) store_seg();  // r_lo was group A's only block (r_hi is merged after)
+      if (sw_now) {
+        store_seg(r_lo * RPB + sub * 32, l_lo, m_lo);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
+      }
     }
     wait_vm_all();
     __syncthreads();
@@ -523,6 +512,16 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   for (int i = 0; i < n_iter; i += 2) {
     step(i, ldsk0, ldsk1, ldsv1, ldsv0);
     step(i + 1, ldsk1, ldsk0, ldsv0, ldsv1);
+  }
+  // the last tile's P.V product (its V^T tile went to ldsv[(n_mine - 1) % 2])
+  if (n_mine > 0) {
+    const char *vd = (((n_mine - 1) & 1) ? ldsv1 : ldsv0) + grp * TB;
+#pragma unroll
+    for (int r = 0; r < NPV; ++r) {
+      const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
+      o[cb] = mfma(vfrag(vd, jb, t, cb), pend[jb][t], o[cb]);
+    }
+    if (cur_seg == 0) store_seg(row0, l_run, m_run);  // r_lo was group A's only block (r_hi is merged below)
   }
 
   // ---- finish: the split block r_hi is merged in B.  The tile buffers are free after the last
@@ -554,7 +553,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       m_run = m_new;
     }
   }
-  if (grp == 1) store_seg();
+  if (grp == 1) store_seg(row0, l_run, m_run);
 }
 
 template <int D, bool CAUSAL>
