@@ -36,10 +36,10 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 12466.14, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 6271.14, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 33153.75, "WRITE_SIZE_KiB": 16899.43},
-    "long_shard": {"sources_sha256": "3a9a8eab1e21b8bc", "FETCH_SIZE_KiB": 1080735.17, "WRITE_SIZE_KiB": 266240.0},
+    "llama3_8b": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 12445.57, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 6259.14, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 33586.35, "WRITE_SIZE_KiB": 16901.95},
+    "long_shard": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 1082347.19, "WRITE_SIZE_KiB": 266240.04},
 }
 
 
