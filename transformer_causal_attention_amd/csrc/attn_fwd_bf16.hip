@@ -191,18 +191,6 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) pend[jb][t] = bf16x8{};
-  // The P.V product of a step always runs; with zero probabilities it must read finite values,
-  // so the V^T buffers start out zeroed (later they only ever hold staged tiles).
-  {
-    u32x4 *z0 = reinterpret_cast<u32x4 *>(ldsv0);
-    u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
-#pragma unroll
-    for (int r = 0; r < 2 * TB / 16 / 512; ++r) {
-      z0[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
-      z1[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
   // ---- row blocks: rows, raw query loads, rotation, fresh state
   auto seg_rows = [&](int seg) __attribute__((always_inline)) {
     row0 = (seg == 0 ? r_lo : r_hi) * RPB + sub * 32;
@@ -239,6 +227,53 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
           const float yv = z ? bf16_hi(hi) : bf16_lo(hi);
           r[0][z] = (xv * cs - yv * sn) * p.q_scale;
           r[1][z] = (yv * cs + xv * sn) * p.q_scale;
+        }
+        olo[w] = pack_bf16x2(r[0][0], r[0][1]);
+        ohi[w] = pack_bf16x2(r[1][0], r[1][1]);
+      }
+      qf[kk] = __builtin_bit_cast(bf16x8, olo);
+      qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
+    }
+  };
+  // With four heads per group every wave of a group has the same 32 rows, so the workgroup
+  // forms each (row, frequency) angle once: a table of (cos, sin) * q_scale for the 32 rows of
+  // both row blocks, laid out [block][kk][hh][pair of e][row] x 16 bytes so that a lane's read
+  // of its two entries is one 16-byte read and a wave's reads are consecutive.
+  char *const rot_tab = ldsv1;  // free until the prologue ends (2 * TB >= 4096 * D / 16 bytes)
+  auto build_rot_tab = [&]() __attribute__((always_inline)) {
+    constexpr int SLOTS = 2 * (NKK / 2) * 2 * 4 * 32;
+#pragma unroll
+    for (int j = 0; j < SLOTS / 512; ++j) {
+      const int id = tid + 512 * j;
+      const int r = id % 32, c = (id / 32) % 4, h2 = (id / 128) % 2, kk = (id / 256) % (NKK / 2);
+      const int s = id / (256 * (NKK / 2));
+      const int pos = (s == 0 ? r_lo : r_hi) * RPB + r;
+      f32x4 v;
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float t = turn_fraction(pos, freq[16 * kk + 8 * h2 + 2 * c + z]);
+        v[2 * z] = __builtin_amdgcn_cosf(t) * p.q_scale;  // argument in turns
+        v[2 * z + 1] = __builtin_amdgcn_sinf(t) * p.q_scale;
+      }
+      *reinterpret_cast<f32x4 *>(rot_tab + id * 16) = v;
+    }
+  };
+  auto rotate_q_tab = [&](const u32x4 (&raw)[NKK], int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < NKK / 2; ++kk) {
+      u32x4 olo, ohi;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x4 cs = *reinterpret_cast<const f32x4 *>(
+            rot_tab + ((((s * (NKK / 2) + kk) * 2 + hh) * 4 + w) * 32 + l32) * 16);
+        float r[2][2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const uint32_t lo = raw[kk][w], hi = raw[kk + NKK / 2][w];
+          const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
+          const float yv = z ? bf16_hi(hi) : bf16_lo(hi);
+          r[0][z] = xv * cs[2 * z] - yv * cs[2 * z + 1];
+          r[1][z] = yv * cs[2 * z] + xv * cs[2 * z + 1];
         }
         olo[w] = pack_bf16x2(r[0][0], r[0][1]);
         ohi[w] = pack_bf16x2(r[1][0], r[1][1]);
@@ -501,13 +536,28 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     if (tid < D / 2) freq[tid] = tab.rev[tid];
     wait_vm_all();
     __syncthreads();
-    rotate_q(raw);
+    if (p.hpw == 4) {
+      build_rot_tab();
+      __syncthreads();
+      rotate_q_tab(raw, len0 > 0 ? 0 : 1);
+    } else {
+      rotate_q(raw);
+    }
     reset_seg();
-    __syncthreads();  // the frequencies are no longer read: the slots may be written
+    __syncthreads();  // frequencies and table are no longer read
+    // The P.V product of a step always runs; with zero probabilities it must read finite
+    // values, so the V^T buffer that step 0 reads starts out zeroed (later the V^T buffers only
+    // ever hold staged tiles).  Group B leaves its rotated queries in its slot.
+    {
+      u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
+#pragma unroll
+      for (int r = 0; r < 2 * TB / 16 / 512; ++r) z1[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (grp == 1) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) *reinterpret_cast<bf16x8 *>(q_slot() + kk * 1024) = qf[kk];
     }
+    __syncthreads();
   }
   for (int i = 0; i < n_iter; i += 2) {
     step(i, ldsk0, ldsk1, ldsv1, ldsv0);
