@@ -209,6 +209,27 @@ def test_deterministic_and_overwrites_poisoned_outputs():
         assert torch.equal(out, out0) and torch.equal(lse, lse0)
 
 
+# Many workgroups, several row-block pairs per (batch row, K/V head), every heads-per-group
+# shape: a race between the waves of a workgroup shows up as runs that differ or overflow.
+REPEAT = [small("rep", 4, 1024, Hq, Hkv, d, "bf16", True, sigma=0.5, seed=11)
+          for d in (64, 128) for (Hq, Hkv) in ((16, 16), (16, 8), (32, 8))]
+
+
+@pytest.mark.parametrize("w", REPEAT, ids=lambda w: f"B{w.B}S{w.S}H{w.Hq}/{w.Hkv}d{w.d}")
+def test_repeated_runs_bit_identical(w):
+    q, k, v = (t.cuda() for t in make_inputs(w))
+    say(w)
+    out0, lse0 = attn_fwd(q, k, v, w.rope_theta, True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out0).all() and torch.isfinite(lse0).all()
+    # each output is a convex combination of value rows (bf16 rounding aside)
+    assert out0.float().abs().max().item() <= 1.01 * v.float().abs().max().item()
+    for _ in range(5):
+        out, lse = attn_fwd(q, k, v, w.rope_theta, True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out0) and torch.equal(lse, lse0)
+
+
 def test_canary_tails_untouched():
     for dtype in ("bf16", "fp32"):
         w = small("canary", 1, 77, 4, 2, 64, dtype, True)

@@ -574,12 +574,13 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     if (cur_seg == 0) store_seg(row0, l_run, m_run);  // r_lo was group A's only block (r_hi is merged below)
   }
 
-  // ---- finish: the split block r_hi is merged in B.  The tile buffers are free after the last
-  // barrier: per-wave accumulators of group A go to ldsk0 (waves 0, 1) and ldsk1 (waves 2, 3),
-  // maxima and sums to ldsv0.
+  // ---- finish: the split block r_hi is merged in B.  Once every wave's last P.V product is
+  // done the tile buffers are free: per-wave accumulators of group A go to ldsk0 (waves 0, 1)
+  // and ldsk1 (waves 2, 3), maxima and sums to ldsv0.
   if (x > 0) {
     float *mo = reinterpret_cast<float *>(gw < 2 ? ldsk0 : ldsk1) + (gw & 1) * NCB * 16 * 64;
     float *mm = reinterpret_cast<float *>(ldsv0);
+    __syncthreads();  // every wave's last P.V product has read its V^T tile (ldsv0 may hold one)
     if (grp == 0) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
