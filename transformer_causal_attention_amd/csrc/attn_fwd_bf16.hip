@@ -581,11 +581,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     float *mo = reinterpret_cast<float *>(gw < 2 ? ldsk0 : ldsk1) + (gw & 1) * NCB * 16 * 64;
     float *mm = reinterpret_cast<float *>(ldsv0);
     __syncthreads();  // every wave's last P.V product has read its V^T tile (ldsv0 may hold one)
+    // accumulators as [cb][v / 4][lane][v % 4]: one 16-byte access per lane and 4 registers
+    f32x4 *mo4 = reinterpret_cast<f32x4 *>(mo);
     if (grp == 0) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mo[(cb * 16 + v) * 64 + lane] = o[cb][v];
+        for (int v4 = 0; v4 < 4; ++v4)
+          mo4[(cb * 4 + v4) * 64 + lane] = f32x4{o[cb][4 * v4], o[cb][4 * v4 + 1], o[cb][4 * v4 + 2], o[cb][4 * v4 + 3]};
       mm[gw * 64 + lane] = m_run;
       mm[256 + gw * 64 + lane] = l_run;
     }
@@ -600,7 +603,11 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[cb][v] = mo[(cb * 16 + v) * 64 + lane] * ca + o[cb][v] * cb_;
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 a4 = mo4[(cb * 4 + v4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[cb][4 * v4 + e] = a4[e] * ca + o[cb][4 * v4 + e] * cb_;
+        }
       m_run = m_new;
     }
   }
