@@ -49,11 +49,13 @@
 //
 // Softmax without a per-tile maximum.  The reference m that probabilities are taken against
 // only needs to keep 2^(s - m) finite: the first tile of a row block sets m to its exact row
-// maximum, later tiles take their probabilities against m as it stands, and a tile is redone
-// (from its scores, still in registers) against max(m, its row maximum), with the accumulator
-// and sum rescaled by 2^(m_old - m_new) <= 1, only if some row's probability sum passed 2^64 or
-// is not finite.  bf16 and fp32 hold values up to 2^64 with the same relative precision as
-// values below 1, and out = o / l, lse = m + log2 l do not depend on which m was used.
+// maximum (rounded up to a bf16 value), later tiles take their probabilities against m as it
+// stands, and a tile is redone (from its scores, still in registers) against max(m, its row
+// maximum), with the accumulator and sum rescaled by 2^(m_old - m_new) <= 1, only if some row's
+// probability sum passed 2^64 or is not finite.  bf16 and fp32 hold values up to 2^64 with the
+// same relative precision as values below 1, and out = o / l, lse = m + log2 l do not depend on
+// which m was used.  Because m is a bf16 value, the score product subtracts it itself: one more
+// MFMA k-step multiplies a key operand of ones by a query operand of -m.
 
 #include <hip/hip_ext.h>
 
@@ -181,7 +183,13 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 
   // ---- state of this wave's 32 rows
   bf16x8 qf[NKK];
-  float m_run = 0.f;        // reference the probabilities are taken against (base-2 scores)
+  float m_run = 0.f;        // reference the probabilities are taken against (base-2 scores,
+                            // always a bf16 value, so that the MFMA below subtracts it exactly)
+  // One more k-step of the score product subtracts the reference: row k = 0 of the key operand
+  // is 1 and of the query operand -m, so the scores come out as s - m and the exponentials need
+  // no subtraction.  Lanes 0-31 hold k = 0..7 of these operands, lanes 32-63 k = 8..15.
+  const bf16x8 kaug = __builtin_bit_cast(bf16x8, u32x4{hh ? 0u : 0x3F80u, 0u, 0u, 0u});
+  bf16x8 qaug = bf16x8{};
   float l_run = 0.f;        // this lane half's share of the running row sum
   f32x16 o[NCB];
   f32x16 sc0, sc1;          // scores of the tile awaiting its softmax half
@@ -282,10 +290,15 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
     }
   };
+  auto set_ref = [&](float m) __attribute__((always_inline)) {  // m: a bf16 value
+    m_run = m;
+    const uint32_t nm = __float_as_uint(-m) >> 16;
+    qaug = __builtin_bit_cast(bf16x8, u32x4{hh ? 0u : nm, 0u, 0u, 0u});
+  };
   auto reset_seg = [&]() __attribute__((always_inline)) {
     // the first tile of a row block always takes the exact maximum, which replaces this
     // provisional reference before any probability is kept
-    m_run = 0.f;
+    set_ref(0.f);
     l_run = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{};
@@ -389,7 +402,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     auto sc_of = [&](int w, int e) __attribute__((always_inline)) {
       return w < 8 ? sc0[2 * w + e] : sc1[2 * (w - 8) + e];
     };
-    auto pair_stage = [&](int w, float sh) __attribute__((always_inline)) {  // w = 0 .. 16
+    // scores are s - m already; the exact path subtracts the change of reference sh
+    auto pair_stage = [&](int w, float sh, bool shifted) __attribute__((always_inline)) {  // w = 0 .. 16
       if (w >= 1) {  // pair w-1: packed to bf16, added to its row sums
         const int c = w - 1;
         const uint32_t pk = pack_bf16x2(ex0, ex1);
@@ -401,8 +415,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         rsum[2 * (c >> 3) + 1] += ex1;
       }
       if (w <= 15) {  // pair w: exponentials
-        ex0 = __builtin_amdgcn_exp2f(sc_of(w, 0) - sh);
-        ex1 = __builtin_amdgcn_exp2f(sc_of(w, 1) - sh);
+        ex0 = __builtin_amdgcn_exp2f(shifted ? sc_of(w, 0) - sh : sc_of(w, 0));
+        ex1 = __builtin_amdgcn_exp2f(shifted ? sc_of(w, 1) - sh : sc_of(w, 1));
       }
     };
     auto pin = [&]() __attribute__((always_inline)) {
@@ -411,9 +425,9 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     };
 #pragma unroll
     for (int r = 0; r < 4; ++r) rsum[r] = 0.f;
-    const float sh = m_run;
-    // phase 1: QK(b0)
-    sc0 = f32x16{};
+    // phase 1: QK(b0), starting from -m
+    sc0 = mfma(kaug, qaug, f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       sc0 = mfma(fr[kk % kReadsAhead], qf[kk], sc0);
@@ -422,15 +436,16 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
     if (msk) mask(sc0, kb0);
     __builtin_amdgcn_sched_barrier(0);
-    // phase 2: QK(b1) with the probabilities of block 0
-    sc1 = f32x16{};
+    // phase 2: QK(b1), starting from -m, with the probabilities of block 0
+    sc1 = mfma(kaug, qaug, f32x16{});
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int g = NKK + kk;
       sc1 = mfma(fr[g % kReadsAhead], qf[kk], sc1);
       unit_tail(g);
 #pragma unroll
-      for (int w = kk * 8 / NKK; w < (kk + 1) * 8 / NKK; ++w) pair_stage(w, sh);
+      for (int w = kk * 8 / NKK; w < (kk + 1) * 8 / NKK; ++w) pair_stage(w, 0.f, false);
       pin();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -444,7 +459,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       o[cb] = mfma(fr[g % kReadsAhead], pend[jb][t], o[cb]);
       unit_tail(g);
 #pragma unroll
-      for (int w = 8 + r * 9 / NPV; w < 8 + (r + 1) * 9 / NPV; ++w) pair_stage(w, sh);
+      for (int w = 8 + r * 9 / NPV; w < 8 + (r + 1) * 9 / NPV; ++w) pair_stage(w, 0.f, false);
       pin();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -455,25 +470,26 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sc0[v], sc1[v]));
       mx = max_xor32(mx);
-      // The first tile of a row block replaces the provisional reference (its state is still
-      // empty, so nothing is rescaled); later the reference only grows, so every rescale factor
-      // is at most 1.  A row with no visible key keeps its reference.
-      float shift, alpha;
-      if (first) {  // o is zero, or at group A's switch block r_lo's accumulator: kept as is
-        shift = mx == -INFINITY ? m_run : mx;
-        alpha = 1.f;
-      } else {
-        shift = fmaxf(m_run, mx);
-        alpha = __builtin_amdgcn_exp2f(m_run - shift);
-      }
+      // mx is the row maximum of s - m.  The first tile of a row block replaces the provisional
+      // reference (its state is still empty, so nothing is rescaled); later the reference only
+      // grows, so every rescale factor is at most 1.  A row with no visible key keeps its
+      // reference.  The new reference is rounded up to a bf16 value, so every probability is at
+      // most 1 and the largest ones keep bf16's finest relative spacing below 1.
+      const float m_abs = first ? (mx == -INFINITY ? m_run : m_run + mx) : m_run + fmaxf(0.f, mx);
+      const uint32_t mb = __float_as_uint(m_abs);
+      const float m_new = __uint_as_float(m_abs > 0.f ? (mb + 0xFFFFu) & 0xFFFF0000u : mb & 0xFFFF0000u);
+      const float d = m_new - m_run;  // the change of reference (>= 0 unless first)
+      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-d);
+      // (o is zero at a row block's first tile, or at group A's switch block r_lo's
+      // accumulator, which is kept as is)
       l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-      m_run = shift;
+      set_ref(m_new);
 #pragma unroll
       for (int r = 0; r < 4; ++r) rsum[r] = 0.f;
 #pragma unroll
-      for (int w = 0; w <= 16; ++w) pair_stage(w, shift);
+      for (int w = 0; w <= 16; ++w) pair_stage(w, d, true);
       rs0 = rsum[0] + rsum[1];
       rs1 = rsum[2] + rsum[3];
     }
@@ -509,7 +525,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(q_slot() + kk * 1024);
         l_run = 0.f;
-        m_run = 0.f;  // provisional, replaced by the first tile's exact maximum
+        set_ref(0.f);  // provisional, replaced by the first tile's exact maximum
         cur_seg = 1;
       }
       const int kb0 = tile_of(i) * BN;
