@@ -36,10 +36,10 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 12445.57, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 6259.14, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 33586.35, "WRITE_SIZE_KiB": 16901.95},
-    "long_shard": {"sources_sha256": "bbeb320946845b26", "FETCH_SIZE_KiB": 1082347.19, "WRITE_SIZE_KiB": 266240.04},
+    "llama3_8b": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 12447.16, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 6263.14, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 33663.26, "WRITE_SIZE_KiB": 16896.09},
+    "long_shard": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 1081772.29, "WRITE_SIZE_KiB": 266240.0},
 }
 
 
