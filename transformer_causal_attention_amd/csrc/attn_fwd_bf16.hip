@@ -345,6 +345,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   constexpr int NPV = 4 * NCB;            // MFMAs of the P.V product of one tile
   constexpr int NMF = 2 * NKK + NPV;      // MFMAs of one tile
   constexpr int NDMA = 2 * DMA_PER_WAVE;  // copy instructions per step of a wave (its group's two tiles)
+  static_assert(3 * (NDMA - 1) < NMF, "every copy is issued inside the tile");
   auto pv_of = [&](const char *vd, int r) __attribute__((always_inline)) {  // operand of the r-th P.V MFMA
     const int jb = r / (2 * NCB), t = (r / NCB) % 2, cb = r % NCB;
     return vfrag(vd, jb, t, cb);
@@ -380,9 +381,10 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   // pair apart (exponentials of pair w; packing of pair w-1 to bf16 and its addition to the row
   // sums), so no instruction waits on the one before it.  Row sums use plain VALU adds: the
   // bf16 dot-product instruction would queue behind MFMAs.  Each wave also issues its share
-  // of its group's copies for the step (the next K tile, this step's V^T tile), one every
-  // NMF / NDMA MFMAs.  Afterwards the tile is redone against its exact maximum when it is the
-  // first of its row block or a row's sum passed the limit, from the scores still in registers.
+  // of its group's copies for the step (the next K tile, this step's V^T tile), one every third
+  // MFMA from the first, so the last copy has a third of the tile to land before the step's
+  // wait.  Afterwards the tile is redone against its exact maximum when it is the first of its
+  // row block or a row's sum passed the limit, from the scores still in registers.
   auto tile = [&](const char *kd, const char *vd, int kb0, bool msk, bool first, bool issue,
                   const Copies &cp) __attribute__((always_inline)) {
     auto op_of = [&](int g) __attribute__((always_inline)) {
@@ -393,7 +395,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     for (int r = 0; r < kReadsAhead; ++r) fr[r] = op_of(r);
     auto unit_tail = [&](int g) __attribute__((always_inline)) {
       if (g + kReadsAhead < NMF) fr[g % kReadsAhead] = op_of(g + kReadsAhead);
-      if ((g * NDMA) % NMF == NMF - NDMA && issue) copy_part(cp, g * NDMA / NMF);
+      if (g % 3 == 0 && g / 3 < NDMA && issue) copy_part(cp, g / 3);
     };
     u32x4 pw0[2], pw1[2];
     float rsum[4];
