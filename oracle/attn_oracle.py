@@ -32,7 +32,11 @@ Readings where the pages are silent or disagree (each also listed in the design 
   * RoPE pairing: half-split (Picotron and PaLM pages); the llama3 page's adjacent-pair
     complex form is the same rotation under a fixed permutation of head_dim and is used
     only as a cross-check in the tests.
-  * Positions are 0..S-1 for every batch row.
+  * Positions are 0..S-1 for every batch row, unless a sequence shard passes its first
+    query and key positions (q_pos0, k_pos0): queries then sit at q_pos0 + i and keys at
+    k_pos0 + j, for the rotation and for the mask alike.  A query with no visible key has
+    out = 0 and lse = -inf (an empty softmax denominator), so that merging it with another
+    shard's partial result leaves that result unchanged.
   * GQA grouping is contiguous: query head h reads K/V head h // (Hq // Hkv).
   * lse is the natural-log logsumexp of the scaled scores over the visible keys.
 """
@@ -49,6 +53,7 @@ __all__ = [
     "kv_head_of",
     "attention_weights",
     "attention",
+    "merge",
 ]
 
 
@@ -95,13 +100,14 @@ def apply_rope(x, positions, rope_theta):
     return x * cos + rotate_half(x) * sin
 
 
-def causal_mask(query_positions, n_keys):
-    """Additive mask (len(query_positions), n_keys): 0 where key j <= query i, -inf where j > i.
+def causal_mask(query_positions, n_keys, key_pos0=0):
+    """Additive mask (len(query_positions), n_keys): 0 where the key's position is at most the
+    query's, -inf where it is later.  Key j sits at position key_pos0 + j.
 
     llama3 page, "causal mask": full(-inf) followed by triu(diagonal=1), added to the scores.
     Written for an arbitrary set of query positions so single rows can be evaluated alone.
     """
-    j = np.arange(n_keys)
+    j = key_pos0 + np.arange(n_keys)
     i = np.asarray(query_positions)
     return np.where(j[None, :] > i[:, None], -np.inf, 0.0)
 
@@ -111,11 +117,12 @@ def softmax_rows(scores):
 
     PaLM page, section 2.5: subtract the row maximum, then softmax.
     Returns (P, m, l) with P = exp(scores - m) / l, m = row max, l = sum exp(scores - m).
+    A row whose every score is -inf (no visible key) has P = 0, m = -inf and l = 0.
     """
     m = scores.max(axis=-1, keepdims=True)
-    e = np.exp(scores - m)
+    e = np.exp(scores - np.where(np.isfinite(m), m, 0.0))
     l = e.sum(axis=-1, keepdims=True)
-    return e / l, m[..., 0], l[..., 0]
+    return e / np.where(l > 0, l, 1.0), m[..., 0], l[..., 0]
 
 
 def kv_head_of(h, n_q_heads, n_kv_heads):
@@ -129,8 +136,9 @@ def kv_head_of(h, n_q_heads, n_kv_heads):
     return h // (n_q_heads // n_kv_heads)
 
 
-def attention_weights(q_rot, k_rot, query_positions, causal):
-    """Softmax weights for one (batch, head): q_rot (R, d) at query_positions, k_rot (S, d).
+def attention_weights(q_rot, k_rot, query_positions, causal, key_pos0=0):
+    """Softmax weights for one (batch, head): q_rot (R, d) at query_positions, k_rot (S, d)
+    at positions key_pos0 + j.
 
     llama3 page, "attention score matrix": scores = q_rot @ k_rot.T / head_dim ** 0.5;
     "causal mask": add the mask; "softmax": over the key axis.
@@ -139,17 +147,19 @@ def attention_weights(q_rot, k_rot, query_positions, causal):
     d = q_rot.shape[-1]
     scores = (q_rot @ k_rot.T) / np.sqrt(np.float64(d))
     if causal:
-        scores = scores + causal_mask(query_positions, k_rot.shape[0])
+        scores = scores + causal_mask(query_positions, k_rot.shape[0], key_pos0)
     return softmax_rows(scores)
 
 
-def attention(q, k, v, rope_theta, causal=True, rows=None):
+def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
     """Causal (or full) RoPE attention with shared K/V heads, in float64.
 
     q: (B, S, Hq, d); k, v: (B, S, Hkv, d); Hq a multiple of Hkv; d even.
-    rows: optional 1-D array of query positions to evaluate (default: all S rows).  Each
-    output row depends only on its own query and the keys, so evaluating a subset is the
-    same definition restricted to those rows.
+    rows: optional 1-D array of query rows to evaluate (default: all S rows).  Each output row
+    depends only on its own query and the keys, so evaluating a subset is the same definition
+    restricted to those rows.
+    q_pos0, k_pos0: positions of query row 0 and key row 0 (a sequence shard's offsets; the
+    Picotron page's ring attention passes K/V blocks of other positions around the ranks).
 
     Returns (out, lse): out (B, R, Hq, d) float64 and lse (B, Hq, R) float64, R = len(rows).
     """
@@ -164,15 +174,38 @@ def attention(q, k, v, rope_theta, causal=True, rows=None):
         raise ValueError("head_dim must be even for the half-split rotation")
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
 
-    q_rot = apply_rope(q[:, rows], rows, rope_theta)
-    k_rot = apply_rope(k, np.arange(S), rope_theta)
+    q_positions = q_pos0 + rows
+    q_rot = apply_rope(q[:, rows], q_positions, rope_theta)
+    k_rot = apply_rope(k, k_pos0 + np.arange(S), rope_theta)
 
     out = np.empty((B, len(rows), Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, len(rows)), dtype=np.float64)
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            P, m, l = attention_weights(q_rot[b, :, h, :], k_rot[b, :, g, :], rows, causal)
+            P, m, l = attention_weights(q_rot[b, :, h, :], k_rot[b, :, g, :], q_positions, causal, k_pos0)
             out[b, :, h, :] = P @ v[b, :, g, :]
-            lse[b, h, :] = m + np.log(l)
+            with np.errstate(divide="ignore"):
+                lse[b, h, :] = m + np.log(l)  # -inf for a row with no visible key
+    return out, lse
+
+
+def merge(o1, lse1, o2, lse2):
+    """Join two partial results over disjoint key sets: lse = logaddexp(lse1, lse2) and
+    out = exp(lse1 - lse) * o1 + exp(lse2 - lse) * o2 (a row empty in both stays empty).
+
+    This is the combination ring attention performs when each rank has attended to one block
+    of keys (Picotron page, context parallelism and ring attention); with lse the natural-log
+    softmax denominator of each part it reproduces attention over the union of the keys.
+    o: (B, R, H, d); lse: (B, H, R).
+    """
+    lse1 = np.asarray(lse1, dtype=np.float64)
+    lse2 = np.asarray(lse2, dtype=np.float64)
+    lse = np.logaddexp(lse1, lse2)
+    safe = np.where(np.isfinite(lse), lse, 0.0)
+    w1 = np.where(np.isfinite(lse), np.exp(lse1 - safe), 0.0)
+    w2 = np.where(np.isfinite(lse), np.exp(lse2 - safe), 0.0)
+    # (B, H, R) weights onto (B, R, H, d) rows
+    out = (np.transpose(w1, (0, 2, 1))[..., None] * np.asarray(o1, dtype=np.float64)
+           + np.transpose(w2, (0, 2, 1))[..., None] * np.asarray(o2, dtype=np.float64))
     return out, lse

@@ -330,6 +330,58 @@ def pin_lse_merge():
     _close(out, full_out, 1e-12, "merged out")
 
 
+# ---------------------------------------------------------------- sequence shards
+def pin_shard_shift_invariance():
+    """Shifting query and key positions together changes nothing: RoPE scores depend only on
+    the position difference and so does the causal mask."""
+    rng = np.random.default_rng(31)
+    q, k, v = _rand(rng, 1, 20, 4, 8), _rand(rng, 1, 20, 2, 8), _rand(rng, 1, 20, 2, 8)
+    for causal in (True, False):
+        o0, l0 = O.attention(q, k, v, 500.0, causal)
+        o1, l1 = O.attention(q, k, v, 500.0, causal, q_pos0=37, k_pos0=37)
+        _close(o1, o0, 1e-12, "shifted shard out")
+        _close(l1, l0, 1e-12, "shifted shard lse")
+
+
+def pin_ring_split():
+    """Causal attention over S = 3 shards of queries, each merged over all 3 shards of keys at
+    their offsets (later shards see nothing and must not change the merge)."""
+    rng = np.random.default_rng(32)
+    S, n = 48, 16
+    q, k, v = _rand(rng, 2, S, 4, 8), _rand(rng, 2, S, 2, 8), _rand(rng, 2, S, 2, 8)
+    full_o, full_l = O.attention(q, k, v, 10000.0, True)
+    for s in range(3):
+        qs = q[:, s * n:(s + 1) * n]
+        o, l = None, None
+        for t in range(3):
+            ot, lt = O.attention(qs, k[:, t * n:(t + 1) * n], v[:, t * n:(t + 1) * n], 10000.0, True,
+                                 q_pos0=s * n, k_pos0=t * n)
+            if t > s:
+                assert np.all(lt == -np.inf) and np.all(ot == 0.0), "a later key shard must be empty"
+            o, l = (ot, lt) if o is None else O.merge(o, l, ot, lt)
+        _close(o, full_o[:, s * n:(s + 1) * n], 1e-12, f"ring shard {s} out")
+        _close(l, full_l[:, :, s * n:(s + 1) * n], 1e-12, f"ring shard {s} lse")
+
+
+def pin_empty_rows():
+    """Queries that precede every key: out exactly 0, lse exactly -inf; a partly visible shard
+    equals the plain definition on its visible keys."""
+    rng = np.random.default_rng(33)
+    q, k, v = _rand(rng, 1, 12, 2, 4), _rand(rng, 1, 12, 1, 4), _rand(rng, 1, 12, 1, 4)
+    o, l = O.attention(q, k, v, 100.0, True, q_pos0=0, k_pos0=12)
+    assert np.all(o == 0.0) and np.all(l == -np.inf), "queries before every key"
+    o, l = O.attention(q, k, v, 100.0, True, q_pos0=0, k_pos0=5)
+    assert np.all(o[:, :5] == 0.0) and np.all(l[:, :, :5] == -np.inf), "rows 0-4 see no key"
+    # row i >= 5 sees keys 0 .. i-5 of this shard: brute force with the page's formulas
+    qr = O.apply_rope(q, np.arange(12), 100.0)
+    kr = O.apply_rope(k, 5 + np.arange(12), 100.0)
+    for i in range(5, 12):
+        sc = kr[0, : i - 4, 0] @ qr[0, i, 0] / 2.0
+        e = np.exp(sc - sc.max())
+        _close(o[0, i, 0], (e / e.sum()) @ v[0, : i - 4, 0], 1e-12, f"partly visible row {i}")
+        _close(l[0, 0, i], sc.max() + np.log(e.sum()), 1e-12, f"partly visible row {i} lse")
+
+
 # ---------------------------------------------------------------- golden fixtures
 def pin_golden():
     path = os.path.join(GOLDEN_DIR, "closed_form_cases.json")
@@ -363,5 +415,8 @@ ALL_PINS = [
     pin_lse_scipy,
     pin_interleaved_equivalence,
     pin_lse_merge,
+    pin_shard_shift_invariance,
+    pin_ring_split,
+    pin_empty_rows,
     pin_golden,
 ]

@@ -49,22 +49,46 @@ def _apply_rope_positions_plus_one(x, positions, rope_theta):
     return x * np.cos(ang)[None, :, None, :] + O.rotate_half(x) * np.sin(ang)[None, :, None, :]
 
 
-def _mask_includes_diagonal(query_positions, n_keys):
-    j = np.arange(n_keys)
+def _mask_includes_diagonal(query_positions, n_keys, key_pos0=0):
+    j = key_pos0 + np.arange(n_keys)
     i = np.asarray(query_positions)
     return np.where(j[None, :] >= i[:, None], -np.inf, 0.0)
 
 
-def _mask_reversed(query_positions, n_keys):
-    j = np.arange(n_keys)
+def _mask_reversed(query_positions, n_keys, key_pos0=0):
+    j = key_pos0 + np.arange(n_keys)
     i = np.asarray(query_positions)
     return np.where(j[None, :] < i[:, None], -np.inf, 0.0)
 
 
-def _mask_off_by_one(query_positions, n_keys):
-    j = np.arange(n_keys)
+def _mask_off_by_one(query_positions, n_keys, key_pos0=0):
+    j = key_pos0 + np.arange(n_keys)
     i = np.asarray(query_positions)
     return np.where(j[None, :] > i[:, None] + 1, -np.inf, 0.0)
+
+
+def _mask_ignores_key_offset(query_positions, n_keys, key_pos0=0):
+    j = np.arange(n_keys)
+    i = np.asarray(query_positions)
+    return np.where(j[None, :] > i[:, None], -np.inf, 0.0)
+
+
+def _softmax_no_empty_guard(scores):
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, m[..., 0], l[..., 0]
+
+
+def _merge_weights_swapped(o1, lse1, o2, lse2):
+    lse = np.logaddexp(lse1, lse2)
+    w1 = np.exp(np.asarray(lse2) - lse)
+    w2 = np.exp(np.asarray(lse1) - lse)
+    return (np.transpose(w1, (0, 2, 1))[..., None] * o1 + np.transpose(w2, (0, 2, 1))[..., None] * o2), lse
+
+
+def _merge_plain_average(o1, lse1, o2, lse2):
+    return 0.5 * (np.asarray(o1) + np.asarray(o2)), np.logaddexp(lse1, lse2)
 
 
 def _softmax_wrong_axis(scores):
@@ -87,47 +111,51 @@ def _kv_head_modulo(h, n_q_heads, n_kv_heads):
     return h % n_kv_heads
 
 
-def _weights_scale_by_d(q_rot, k_rot, query_positions, causal):
+def _weights_scale_by_d(q_rot, k_rot, query_positions, causal, key_pos0=0):
     d = q_rot.shape[-1]
     scores = (q_rot @ k_rot.T) / np.float64(d)
     if causal:
-        scores = scores + O.causal_mask(query_positions, k_rot.shape[0])
+        scores = scores + O.causal_mask(query_positions, k_rot.shape[0], key_pos0)
     return O.softmax_rows(scores)
 
 
-def _weights_no_scale(q_rot, k_rot, query_positions, causal):
+def _weights_no_scale(q_rot, k_rot, query_positions, causal, key_pos0=0):
     scores = q_rot @ k_rot.T
     if causal:
-        scores = scores + O.causal_mask(query_positions, k_rot.shape[0])
+        scores = scores + O.causal_mask(query_positions, k_rot.shape[0], key_pos0)
     return O.softmax_rows(scores)
 
 
-def _weights_ignore_causal(q_rot, k_rot, query_positions, causal):
+def _weights_ignore_causal(q_rot, k_rot, query_positions, causal, key_pos0=0):
     d = q_rot.shape[-1]
     return O.softmax_rows((q_rot @ k_rot.T) / np.sqrt(np.float64(d)))
 
 
-def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, unrotated_k=False):
-    def attention(q, k, v, rope_theta, causal=True, rows=None):
+def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, unrotated_k=False,
+                       k_rope_no_offset=False, q_rope_no_offset=False):
+    def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
         q = np.asarray(q, dtype=np.float64)
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
         B, S, Hq, d = q.shape
         Hkv = k.shape[2]
         rows = np.arange(S) if rows is None else np.asarray(rows)
-        q_rot = O.apply_rope(q[:, rows], rows, rope_theta)
-        k_rot = k if unrotated_k else O.apply_rope(k, np.arange(S), rope_theta)
+        qp = rows + (0 if q_rope_no_offset else q_pos0)
+        q_rot = O.apply_rope(q[:, rows], qp, rope_theta)
+        kp = np.arange(S) + (0 if k_rope_no_offset else k_pos0)
+        k_rot = k if unrotated_k else O.apply_rope(k, kp, rope_theta)
         vv = O.apply_rope(v, np.arange(S), rope_theta) if rope_v else v
         out = np.empty((B, len(rows), Hq, d))
         lse = np.empty((B, Hq, len(rows)))
         for b in range(B):
             for h in range(Hq):
                 g = O.kv_head_of(h, Hq, Hkv)
-                P, m, l = O.attention_weights(q_rot[b, :, h], k_rot[b, :, g], rows, causal)
+                P, m, l = O.attention_weights(q_rot[b, :, h], k_rot[b, :, g], q_pos0 + rows, causal, k_pos0)
                 if transpose_p and P.shape[0] == P.shape[1]:
                     P = P.T
                 out[b, :, h] = P @ vv[b, :, g]
-                lse[b, h] = np.log(l) if lse_drops_max else m + np.log(l)
+                with np.errstate(divide="ignore"):
+                    lse[b, h] = np.log(l) if lse_drops_max else m + np.log(l)
         return out, lse
 
     return attention
@@ -154,6 +182,12 @@ MUTATIONS = {
     "rope_applied_to_v": ("attention", _attention_variant(rope_v=True)),
     "weights_transposed": ("attention", _attention_variant(transpose_p=True)),
     "k_left_unrotated": ("attention", _attention_variant(unrotated_k=True)),
+    "mask_ignores_key_offset": ("causal_mask", _mask_ignores_key_offset),
+    "empty_rows_unguarded": ("softmax_rows", _softmax_no_empty_guard),
+    "k_rotation_ignores_offset": ("attention", _attention_variant(k_rope_no_offset=True)),
+    "q_rotation_ignores_offset": ("attention", _attention_variant(q_rope_no_offset=True)),
+    "merge_weights_swapped": ("merge", _merge_weights_swapped),
+    "merge_plain_average": ("merge", _merge_plain_average),
 }
 
 
