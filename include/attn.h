@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Element types of q, k, v and out. */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
@@ -104,6 +104,40 @@ int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, in
                    int head_dim, double rope_theta, int causal, int dtype, void *out,
                    float *lse, void *workspace, size_t workspace_bytes, void *stream,
                    void *ev_start, void *ev_stop);
+
+/*
+ * One shard of a longer sequence: attn_fwd for queries at positions q_pos0 .. q_pos0+S-1
+ * against keys and values at positions k_pos0 .. k_pos0+S-1 (same S, e.g. one step of ring
+ * attention, where each rank attends its query block to the K/V blocks passed around the
+ * ring: Picotron page, "context parallelism and ring attention").  The positions rotate q and
+ * k, and with causal = 1 key j is visible to query i iff k_pos0 + j <= q_pos0 + i, so an
+ * earlier key shard is seen in full, the diagonal one causally, and a later one not at all.
+ * A query with no visible key gets out = 0 and lse = -inf, which attn_merge treats as an
+ * empty part.  attn_fwd is this call with q_pos0 = k_pos0 = 0.
+ *
+ *   q_pos0, k_pos0  >= 0, with q_pos0 + S and k_pos0 + S at most 2^30 (else ATTN_EINVAL)
+ *   other arguments as for attn_fwd (same workspace size)
+ */
+int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                   int head_dim, double rope_theta, int causal, int q_pos0, int k_pos0, int dtype,
+                   void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Join two partial results for the same queries over disjoint key sets (the merge step of
+ * ring attention, Picotron page, context parallelism):
+ *   lse = ln(exp(lse1) + exp(lse2)),   out = exp(lse1 - lse) * o1 + exp(lse2 - lse) * o2,
+ * with lse the natural-log softmax denominators attn_fwd / attn_fwd_shard return.  A part
+ * with lse = -inf contributes nothing; a row empty in both stays out = 0, lse = -inf.
+ *
+ *   o1, o2, out   device, (B, S, H, head_dim) contiguous, type `dtype`, 16-byte aligned
+ *   lse1, lse2, lse  device, (B, H, S) float32, 4-byte aligned
+ *   out may be o1 or o2 and lse may be lse1 or lse2 (in-place accumulation); other overlaps
+ *   are not allowed.  Computed in float32 and rounded to nearest even into `dtype`.
+ * Returns ATTN_OK, ATTN_EINVAL (null or misaligned pointer, B/S/H < 1) or ATTN_EUNSUPPORTED
+ * (head_dim not 64 or 128, unknown dtype, sizes too large), ATTN_EHIP on a launch error.
+ */
+int attn_merge(const void *o1, const float *lse1, const void *o2, const float *lse2, int B, int S,
+               int H, int head_dim, int dtype, void *out, float *lse, void *stream);
 
 /* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */
 void *attn_event_create(void);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert len(_lib.strerror(code)) > 5
     assert "unknown" in _lib.strerror(12345)
@@ -100,3 +100,49 @@ def test_event_helpers_reject_null():
     assert lib.attn_event_destroy(None) == _lib.ATTN_EINVAL
     ms = ctypes.c_float()
     assert lib.attn_event_elapsed_ms(None, None, ctypes.byref(ms)) == _lib.ATTN_EINVAL
+
+
+def shard_call(**over):
+    a = dict(q=P, k=P, v=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=10000.0, causal=1, qp=0, kp=0, dtype=0,
+             out=P, lse=P, ws=P, wsb=1 << 30, stream=None)
+    a.update(over)
+    return _lib.shard_raw(a["q"], a["k"], a["v"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"],
+                          a["causal"], a["qp"], a["kp"], a["dtype"], a["out"], a["lse"], a["ws"], a["wsb"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(qp=-1), dict(kp=-5), dict(qp=(1 << 30) - 63), dict(kp=1 << 30), dict(q=None), dict(lse=P + 1),
+    dict(Hq=3, Hkv=2), dict(causal=3),
+])
+def test_shard_invalid_arguments(over):
+    assert shard_call(**over) == _lib.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(dtype=5), _lib.ATTN_EUNSUPPORTED),
+    (dict(wsb=16), _lib.ATTN_EWORKSPACE), (dict(ws=None), _lib.ATTN_EWORKSPACE),
+])
+def test_shard_other_rejections(over, code):
+    assert shard_call(**over) == code
+
+
+def merge_call(**over):
+    a = dict(o1=P, l1=P, o2=P, l2=P, B=1, S=64, H=4, d=128, dtype=0, out=P, lse=P, stream=None)
+    a.update(over)
+    return _lib.merge_raw(a["o1"], a["l1"], a["o2"], a["l2"], a["B"], a["S"], a["H"], a["d"], a["dtype"],
+                          a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(o1=None), dict(l1=None), dict(o2=None), dict(l2=None), dict(out=None), dict(lse=None),
+    dict(o1=P + 8), dict(o2=P + 4), dict(out=P + 2), dict(l1=P + 1), dict(l2=P + 2), dict(lse=P + 3),
+    dict(B=0), dict(S=0), dict(H=0), dict(S=-2),
+])
+def test_merge_invalid_arguments(over):
+    assert merge_call(**over) == _lib.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("over", [dict(d=96), dict(d=256), dict(dtype=2), dict(dtype=-1)])
+def test_merge_unsupported(over):
+    assert merge_call(**over) == _lib.ATTN_EUNSUPPORTED

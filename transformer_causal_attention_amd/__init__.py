@@ -6,6 +6,12 @@ q: (B, S, Hq, D), k/v: (B, S, Hkv, D) contiguous CUDA (HIP) tensors, bfloat16 or
 D in {64, 128}, Hq a multiple of Hkv.  Returns out (B, S, Hq, D) in the input dtype and
 lse (B, Hq, S) float32 (natural-log logsumexp of the scaled scores of each row).
 
+    out, lse = attn_fwd(q, k, v, rope_theta, causal=True, q_pos0=p, k_pos0=r)
+    out, lse = attn_merge(o1, lse1, o2, lse2)
+
+A call with position offsets is one shard of a longer sequence (one ring-attention step);
+attn_merge joins two such partial results.
+
 PyTorch only provides device memory and the stream; the computation runs in the HIP
 kernels behind the C ABI of libattn.so (include/attn.h).
 """
@@ -20,4 +26,4 @@ from ._lib import (  # noqa: F401
     strerror,
     workspace_bytes,
 )
-from .api import attn_fwd, attn_fwd_into  # noqa: F401
+from .api import attn_fwd, attn_fwd_into, attn_merge  # noqa: F401

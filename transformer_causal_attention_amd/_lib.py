@@ -22,12 +22,16 @@ ATTN_EWORKSPACE = -4
 _VP = ctypes.c_void_p
 _I = ctypes.c_int
 _FWD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_SHARD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_MERGE_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]
 SIGNATURES = {
     "attn_abi_version": (_I, []),
     "attn_strerror": (ctypes.c_char_p, [_I]),
     "attn_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "attn_fwd": (_I, _FWD_ARGS),
     "attn_fwd_timed": (_I, _FWD_ARGS + [_VP, _VP]),
+    "attn_fwd_shard": (_I, _SHARD_ARGS),
+    "attn_merge": (_I, _MERGE_ARGS),
     "attn_event_create": (_VP, []),
     "attn_event_destroy": (_I, [_VP]),
     "attn_event_elapsed_ms": (_I, [_VP, _VP, ctypes.POINTER(ctypes.c_float)]),
@@ -80,6 +84,18 @@ def fwd_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, ls
     if ev_start is None and ev_stop is None:
         return lib.attn_fwd(*args)
     return lib.attn_fwd_timed(*args, ev_start, ev_stop)
+
+
+def shard_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dtype, out, lse,
+              workspace, workspace_bytes_, stream):
+    """Call attn_fwd_shard with raw pointers; returns the code."""
+    return load().attn_fwd_shard(q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(causal), int(q_pos0),
+                                 int(k_pos0), dtype, out, lse, workspace, workspace_bytes_, stream)
+
+
+def merge_raw(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream):
+    """Call attn_merge with raw pointers; returns the code."""
+    return load().attn_merge(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream)
 
 
 class Event:

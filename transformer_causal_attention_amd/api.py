@@ -26,12 +26,15 @@ def _shapes(q, k, v):
     return B, S, Hq, Hkv, D
 
 
-def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=None, events=None):
+def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=None, events=None,
+                  q_pos0=0, k_pos0=0):
     """attn_fwd writing into caller-provided out (like q) and lse (B, Hq, S) float32.
 
     workspace: optional uint8 GPU tensor of at least workspace_bytes(...) bytes.
     stream: torch.cuda.Stream to enqueue on (default: the current stream).
     events: optional (start, stop) pair of Event recorded around the attention kernel.
+    q_pos0, k_pos0: positions of query row 0 and key row 0 when the call is one shard of a
+    longer sequence (attn_fwd_shard); events are not available for shards.
     """
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
@@ -47,6 +50,15 @@ def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=
             workspace.record_stream(st)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if q_pos0 or k_pos0:
+        if events is not None:
+            raise ValueError("events are not available for a shard call")
+        rc = _lib.shard_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
+                            1 if causal else 0, q_pos0, k_pos0, code, out.data_ptr(), lse.data_ptr(),
+                            ws_ptr, ws_bytes, st.cuda_stream)
+        if rc != _lib.ATTN_OK:
+            raise _lib.AttnError(rc, "attn_fwd_shard")
+        return out, lse
     ev0, ev1 = (events[0].ptr, events[1].ptr) if events is not None else (None, None)
     rc = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
                       1 if causal else 0, code, out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
@@ -56,9 +68,42 @@ def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=
     return out, lse
 
 
-def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, events=None):
-    """Fused RoPE + causal GQA attention forward.  Returns (out, lse)."""
+def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, events=None, q_pos0=0, k_pos0=0):
+    """Fused RoPE + causal GQA attention forward.  Returns (out, lse).
+
+    With q_pos0 / k_pos0 the call is one shard of a longer sequence (queries at q_pos0 + i,
+    keys at k_pos0 + j); rows that see no key get out 0 and lse -inf, ready for attn_merge.
+    """
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events)
+    return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events, q_pos0, k_pos0)
+
+
+def attn_merge(o1, lse1, o2, lse2, out=None, lse=None, stream=None):
+    """Join two partial results over disjoint keys (attn_merge).  Returns (out, lse).
+
+    o1, o2: (B, S, H, D) like attn_fwd's out; lse1, lse2: (B, H, S) float32.  out / lse may be
+    given, and may be o1 / lse1 (in place).
+    """
+    for name, t in (("o1", o1), ("o2", o2)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor (B, S, H, D)")
+    if o2.shape != o1.shape or o2.dtype != o1.dtype or o1.dtype not in _DTYPE_CODE:
+        raise ValueError("o1 and o2 must share shape and a dtype of bfloat16 or float32")
+    B, S, H, D = o1.shape
+    for name, t in (("lse1", lse1), ("lse2", lse2)):
+        if tuple(t.shape) != (B, H, S) or t.dtype != torch.float32 or not t.is_contiguous() or t.device != o1.device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape (B, H, S)")
+    out = torch.empty_like(o1) if out is None else out
+    lse = torch.empty_like(lse1) if lse is None else lse
+    if out.shape != o1.shape or out.dtype != o1.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like o1")
+    if lse.shape != lse1.shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor shaped like lse1")
+    st = stream if stream is not None else torch.cuda.current_stream(o1.device)
+    rc = _lib.merge_raw(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(), B, S, H, D,
+                        _DTYPE_CODE[o1.dtype], out.data_ptr(), lse.data_ptr(), st.cuda_stream)
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_merge")
+    return out, lse

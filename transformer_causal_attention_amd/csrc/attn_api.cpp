@@ -51,8 +51,8 @@ float q_scale(int d) { return (float)(1.4426950408889634073599246810019 / std::s
 
 template <int D>
 hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                    const attn::RopeTable &tab, int causal, void *out, float *lse, void *ws,
-                    hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+                    const attn::RopeTable &tab, int causal, int q_pos0, int k_pos0, void *out,
+                    float *lse, void *ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const size_t s_pad = padded_len(S);
   attn::PrepParams pp;
   pp.k = static_cast<const __bf16 *>(k);
@@ -63,6 +63,7 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   pp.S = S;
   pp.Hkv = Hkv;
   pp.S_pad = (int)s_pad;
+  pp.k_pos0 = k_pos0;
   hipError_t err = attn::launch_prep_kv<D>(pp, tab, st);
   if (err != hipSuccess) return err;
 
@@ -83,6 +84,8 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.n_units = B * Hkv * (p.G / p.hpw);
   p.n_row_blocks = (S + p.rows_per_blk - 1) / p.rows_per_blk;
   p.n_pairs = (p.n_row_blocks + 1) / 2;
+  p.q_pos0 = q_pos0;
+  p.delta = q_pos0 - k_pos0;
   p.q_scale = q_scale(D);
 
   return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
@@ -91,8 +94,8 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
 
 template <int D>
 hipError_t run_f32(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                   const attn::RopeTable &tab, int causal, void *out, float *lse, hipStream_t st,
-                   hipEvent_t e0, hipEvent_t e1) {
+                   const attn::RopeTable &tab, int causal, int q_pos0, int k_pos0, void *out,
+                   float *lse, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   attn::F32Params p;
   p.q = static_cast<const float *>(q);
   p.k = static_cast<const float *>(k);
@@ -105,15 +108,20 @@ hipError_t run_f32(const void *q, const void *k, const void *v, int B, int S, in
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
   p.n_row_blocks = (S + 63) / 64;
+  p.q_pos0 = q_pos0;
+  p.k_pos0 = k_pos0;
   p.q_scale = q_scale(D);
   return causal ? attn::launch_attn_f32<D, true>(p, tab, st, e0, e1)
                 : attn::launch_attn_f32<D, false>(p, tab, st, e0, e1);
 }
 
 int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv, int d,
-             double rope_theta, int causal, int dtype, void *out, float *lse, void *workspace,
-             size_t workspace_bytes, void *stream, void *ev_start, void *ev_stop) {
+             double rope_theta, int causal, int q_pos0, int k_pos0, int dtype, void *out, float *lse,
+             void *workspace, size_t workspace_bytes, void *stream, void *ev_start, void *ev_stop) {
   if (!q || !k || !v || !out || !lse) return ATTN_EINVAL;
+  // positions (offset + row) stay below 2^30, so every position difference fits an int
+  if (q_pos0 < 0 || k_pos0 < 0 || (long long)q_pos0 + S > (1LL << 30) || (long long)k_pos0 + S > (1LL << 30))
+    return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
     return ATTN_EINVAL;
   const int rc = check_shape(B, S, Hq, Hkv, d, rope_theta, causal, dtype);
@@ -126,11 +134,11 @@ int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, 
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t err;
   if (dtype == ATTN_DTYPE_BF16)
-    err = d == 64 ? run_bf16<64>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, workspace, st, e0, e1)
-                  : run_bf16<128>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, workspace, st, e0, e1);
+    err = d == 64 ? run_bf16<64>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1)
+                  : run_bf16<128>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1);
   else
-    err = d == 64 ? run_f32<64>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, st, e0, e1)
-                  : run_f32<128>(q, k, v, B, S, Hq, Hkv, tab, causal, out, lse, st, e0, e1);
+    err = d == 64 ? run_f32<64>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, st, e0, e1)
+                  : run_f32<128>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, st, e0, e1);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -158,15 +166,53 @@ ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim,
 ATTN_EXPORT int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
                          int head_dim, double rope_theta, int causal, int dtype, void *out, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream) {
-  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, workspace,
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, 0, 0, dtype, out, lse, workspace,
                   workspace_bytes, stream, nullptr, nullptr);
+}
+
+ATTN_EXPORT int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                               int head_dim, double rope_theta, int causal, int q_pos0, int k_pos0,
+                               int dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dtype, out, lse,
+                  workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+ATTN_EXPORT int attn_merge(const void *o1, const float *lse1, const void *o2, const float *lse2, int B, int S,
+                           int H, int head_dim, int dtype, void *out, float *lse, void *stream) {
+  if (!o1 || !lse1 || !o2 || !lse2 || !out || !lse) return ATTN_EINVAL;
+  if (!aligned(o1, 16) || !aligned(o2, 16) || !aligned(out, 16) || !aligned(lse1, 4) || !aligned(lse2, 4) ||
+      !aligned(lse, 4))
+    return ATTN_EINVAL;
+  if (B < 1 || S < 1 || H < 1) return ATTN_EINVAL;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP32) return ATTN_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ATTN_EUNSUPPORTED;
+  const double rows = (double)B * S * H;
+  if (rows * (head_dim / 4) >= 2147483647.0 * 256.0 || rows * head_dim > 4.0e15) return ATTN_EUNSUPPORTED;
+  attn::MergeParams p;
+  p.o1 = o1;
+  p.o2 = o2;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.out = out;
+  p.lse = lse;
+  p.rows = (long long)B * S * H;
+  p.S = S;
+  p.H = H;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (dtype == ATTN_DTYPE_BF16)
+    err = head_dim == 64 ? attn::launch_merge<__bf16, 64>(p, st) : attn::launch_merge<__bf16, 128>(p, st);
+  else
+    err = head_dim == 64 ? attn::launch_merge<float, 64>(p, st) : attn::launch_merge<float, 128>(p, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
 ATTN_EXPORT int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
                                int head_dim, double rope_theta, int causal, int dtype, void *out,
                                float *lse, void *workspace, size_t workspace_bytes, void *stream,
                                void *ev_start, void *ev_stop) {
-  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, workspace,
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, 0, 0, dtype, out, lse, workspace,
                   workspace_bytes, stream, ev_start, ev_stop);
 }
 

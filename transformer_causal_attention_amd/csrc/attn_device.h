@@ -34,6 +34,8 @@ struct FwdParams {
   int n_units;       // B * Hkv * (G / hpw)
   int n_row_blocks;  // ceil(S / rows_per_blk)
   int n_pairs;       // ceil(n_row_blocks / 2): workgroups per unit
+  int q_pos0;        // position of query row 0 (a sequence shard's offset; 0 otherwise)
+  int delta;         // q_pos0 - k_pos0: key j is visible to query i iff j <= i + delta (causal)
   float q_scale;     // log2(e) / sqrt(D): scores come out in the base-2 domain
 };
 
@@ -43,6 +45,7 @@ struct F32Params {
   float *lse;
   int B, S, Hq, Hkv, G;
   int n_row_blocks;
+  int q_pos0, k_pos0;  // positions of query row 0 and key row 0
   float q_scale;
 };
 
@@ -52,6 +55,18 @@ struct PrepParams {
   __bf16 *kr;       // 64-key tiles (B, Hkv, S_pad/64) x [D/8][64][8]
   __bf16 *vt;       // 64-key tiles (B, Hkv, S_pad/64) x [8][D][8]
   int B, S, Hkv, S_pad;
+  int k_pos0;       // position of key row 0
+};
+
+// Merge of two partial results: o1, o2, out (B, S, H, D) of the element type; lse1, lse2, lse
+// (B, H, S) float32.  out / lse may be o1 / lse1 or o2 / lse2.
+struct MergeParams {
+  const void *o1, *o2;
+  const float *lse1, *lse2;
+  void *out;
+  float *lse;
+  long long rows;  // B * S * H
+  int S, H;
 };
 
 // Fraction of a turn for position p and frequency f (revolutions per position):

@@ -136,8 +136,15 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int RPB = p.rows_per_blk;
   const int r_lo = pi;
   const int r_hi = p.n_row_blocks - 1 - pi;
-  const int t_lo = ((CAUSAL ? min(S, (r_lo + 1) * RPB) : S) + BN - 1) / BN;
-  const int t_hi = ((CAUSAL ? min(S, (r_hi + 1) * RPB) : S) + BN - 1) / BN;
+  // key tiles a row block needs: causal, its last row i sees keys j <= i + delta (delta =
+  // q_pos0 - k_pos0, 0 unless the call is one shard of a longer sequence), clamped to [0, S]
+  const int delta = p.delta;
+  auto n_tiles_of = [&](int r) __attribute__((always_inline)) {
+    const int keys = CAUSAL ? max(0, min(S, min(S, (r + 1) * RPB) + delta)) : S;
+    return (keys + BN - 1) / BN;
+  };
+  const int t_lo = n_tiles_of(r_lo);
+  const int t_hi = n_tiles_of(r_hi);
   const bool two = r_lo != r_hi;
   // Steps of a group.  Group A: the t_lo tiles of block r_lo (when two), then tiles [0, x) of
   // block r_hi; group B: tiles [x, t_hi) of block r_hi, with x balancing the two.  Inside the
@@ -227,7 +234,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         for (int z = 0; z < 2; ++z) {
           const int e = 2 * w + z;
           const double f = freq[16 * kk + 8 * hh + e];
-          const float t = turn_fraction(my_row, f);
+          const float t = turn_fraction(p.q_pos0 + my_row, f);
           const float sn = __builtin_amdgcn_sinf(t);  // argument in turns
           const float cs = __builtin_amdgcn_cosf(t);
           const uint32_t lo = raw[kk][w], hi = raw[kk + NKK / 2][w];
@@ -255,7 +262,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       const int id = tid + 512 * j;
       const int r = id % 32, c = (id / 32) % 4, h2 = (id / 128) % 2, kk = (id / 256) % (NKK / 2);
       const int s = id / (256 * (NKK / 2));
-      const int pos = (s == 0 ? r_lo : r_hi) * RPB + r;
+      const int pos = p.q_pos0 + (s == 0 ? r_lo : r_hi) * RPB + r;
       f32x4 v;
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
@@ -319,7 +326,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     asm volatile("" : "+v"(lr), "+v"(lh));
     const int my_row = r0 + lr;
     if (my_row < S) {
-      const float inv = 1.0f / l_tot;
+      // a row with no visible key (possible only in a shard of later keys) has out 0, lse -inf
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       __bf16 *dst = p.out + (((size_t)b * S + my_row) * p.Hq + head) * D + 4 * lh;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -331,7 +339,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
           *reinterpret_cast<u32x2 *>(dst + 32 * cb + 8 * a) = w2;
         }
       if (lh == 0)
-        p.lse[((size_t)b * p.Hq + head) * S + my_row] = (m + __log2f(l_tot)) * 0.69314718055994531f;
+        p.lse[((size_t)b * p.Hq + head) * S + my_row] =
+            l_tot > 0.f ? (m + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     }
   };
 
@@ -356,7 +365,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int j = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-      if ((CAUSAL && j > my_row) || j >= S) sc[v] = -INFINITY;
+      if ((CAUSAL && j > my_row + delta) || j >= S) sc[v] = -INFINITY;
     }
   };
   auto needs_redo = [&](float rsum) __attribute__((always_inline)) {
@@ -531,7 +540,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         cur_seg = 1;
       }
       const int kb0 = tile_of(i) * BN;
-      const bool msk = (CAUSAL && kb0 + BN - 1 > row0) || kb0 + BN > S;
+      const bool msk = (CAUSAL && kb0 + BN - 1 > row0 + delta) || kb0 + BN > S;
       tile(kcur + go, vprev + go, kb0, msk, i == 0 || i == len0, true, cp);
       if (sw_now) {
         store_seg(r_lo * RPB + sub * 32, l_lo, m_lo);
@@ -562,6 +571,8 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       rotate_q(raw);
     }
     reset_seg();
+    // group A's block r_lo sees no key at all (a shard of later keys): its rows are empty
+    if (grp == 0 && two && t_lo == 0) store_seg(r_lo * RPB + sub * 32, 0.f, 0.f);
     __syncthreads();  // frequencies and table are no longer read
     // The P.V product of a step always runs; with zero probabilities it must read finite
     // values, so the V^T buffer that step 0 reads starts out zeroed (later the V^T buffers only
@@ -614,9 +625,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     if (grp == 1) {
       const float ma = mm[gw * 64 + lane];
       const float la = mm[256 + gw * 64 + lane];
-      const float m_new = fmaxf(ma, m_run);  // finite for every row below S
-      const float ca = __builtin_amdgcn_exp2f(ma - m_new);
-      const float cb_ = __builtin_amdgcn_exp2f(m_run - m_new);
+      // a part in which a row saw no key (sum 0 over both lane halves; only in a shard of
+      // later keys) holds a provisional reference only and must not set the merged one
+      const float ma_e = la + mm[256 + gw * 64 + (lane ^ 32)] > 0.f ? ma : -INFINITY;
+      const float mb_e = l_run + xor32(l_run) > 0.f ? m_run : -INFINITY;
+      const float m_max = fmaxf(ma_e, mb_e);
+      const float m_new = m_max == -INFINITY ? 0.f : m_max;  // both parts empty: sum stays 0
+      const float ca = __builtin_amdgcn_exp2f(ma_e - m_new);
+      const float cb_ = __builtin_amdgcn_exp2f(mb_e - m_new);
       l_run = la * ca + l_run * cb_;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)

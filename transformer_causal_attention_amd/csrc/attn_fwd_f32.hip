@@ -31,7 +31,8 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
   const int g = head / p.G;
   const int S = p.S;
   const int row = rb * 64 + lane;
-  const int kv_end = CAUSAL ? min(S, rb * 64 + 64) : S;
+  const int delta = p.q_pos0 - p.k_pos0;  // key j is visible to query i iff j <= i + delta
+  const int kv_end = CAUSAL ? max(0, min(S, min(S, rb * 64 + 64) + delta)) : S;
 
   // rotated, pre-scaled query row in registers
   float q[D];
@@ -40,7 +41,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
 #pragma unroll
     for (int c = 0; c < D / 2; ++c) {
       float sn, cs;
-      sincos_turns(turn_fraction(row, tab.rev[c]), &sn, &cs);
+      sincos_turns(turn_fraction(p.q_pos0 + row, tab.rev[c]), &sn, &cs);
       const float x = row < S ? src[c] : 0.f;
       const float y = row < S ? src[c + D / 2] : 0.f;
       q[c] = (x * cs - y * sn) * p.q_scale;
@@ -63,7 +64,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
 #pragma unroll 4
         for (int c = 0; c < D / 2; ++c) {
           float sn, cs;
-          sincos_turns(turn_fraction(j, tab.rev[c]), &sn, &cs);
+          sincos_turns(turn_fraction(p.k_pos0 + j, tab.rev[c]), &sn, &cs);
           const float x = j < S ? src[c] : 0.f;
           const float y = j < S ? src[c + D / 2] : 0.f;
           ks[t][c] = x * cs - y * sn;
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
 #pragma unroll
         for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[jl][c], acc);
         const int j = kbase + jl;
-        const bool masked = jl >= tile_end || j >= S || (CAUSAL && j > row);
+        const bool masked = jl >= tile_end || j >= S || (CAUSAL && j > row + delta);
         s[u] = masked ? -INFINITY : acc;
         mx = fmaxf(mx, s[u]);
       }
@@ -114,14 +115,15 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
   }
 
   if (row < S) {
-    const float inv = 1.0f / l_run;
+    // a row with no visible key (a shard of later keys) has out 0 and lse -inf
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     float *dst = p.out + (((size_t)b * S + row) * p.Hq + head) * D;
 #pragma unroll
     for (int c = 0; c < D; c += 4) {
       f32x4 w4 = {o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
       *reinterpret_cast<f32x4 *>(dst + c) = w4;
     }
-    p.lse[((size_t)b * p.Hq + head) * S + row] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    p.lse[((size_t)b * p.Hq + head) * S + row] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
   }
 }
 

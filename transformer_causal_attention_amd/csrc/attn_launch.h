@@ -18,4 +18,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream,
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
+template <typename T, int D>
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
+
 }  // namespace attn

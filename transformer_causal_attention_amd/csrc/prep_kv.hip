@@ -1,7 +1,8 @@
 // Key/value preparation, once per key: rotary embedding of K and transposition of V, into
 // head-major buffers padded to whole 64-key tiles.
 //
-// Rotation (half-split form): for pair i < D/2 at position p with angle a = p * theta_i,
+// Rotation (half-split form): for pair i < D/2 at position p = k_pos0 + j (the shard's first
+// key position plus the row) with angle a = p * theta_i,
 //   k'_i = k_i cos a - k_{i+D/2} sin a,   k'_{i+D/2} = k_{i+D/2} cos a + k_i sin a
 // i.e. x*cos + rotate_half(x)*sin with rotate_half = cat(-x2, x1) (Picotron page, section 1),
 // theta_i = rope_theta^(-2i/D) (PaLM page, section 2.3).  Values are not rotated.
@@ -88,8 +89,8 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
     if (j < p.S) {  // keys past S stay zero
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float t0 = turn_fraction(j, freq[c0 + 2 * w]);
-        const float t1 = turn_fraction(j, freq[c0 + 2 * w + 1]);
+        const float t0 = turn_fraction(p.k_pos0 + j, freq[c0 + 2 * w]);
+        const float t1 = turn_fraction(p.k_pos0 + j, freq[c0 + 2 * w + 1]);
         const float s0 = __builtin_amdgcn_sinf(t0), cs0 = __builtin_amdgcn_cosf(t0);
         const float s1 = __builtin_amdgcn_sinf(t1), cs1 = __builtin_amdgcn_cosf(t1);
         const float x0 = bf16_lo(kl[it][w]), x1 = bf16_hi(kl[it][w]);
