@@ -128,6 +128,87 @@ def cpu_baseline(w, budget_s=20.0):
             "sample": sample, "seconds": round(elapsed, 3)}
 
 
+def ring_bench(args):
+    """Causal attention over the workload's sequence split into args.ring shards: every query
+    shard against every key shard at or before it (attn_fwd with q_pos0 / k_pos0), joined by
+    attn_merge, as the ranks of a ring would compute it, here one after another on one GPU.
+    Also times the merge kernel alone against the HBM bandwidth."""
+    import torch
+
+    from transformer_causal_attention_amd import attn_fwd_into, attn_merge, workspace_bytes
+    from transformer_causal_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    n_sh = args.ring
+    if w.S % n_sh or not w.causal:
+        raise SystemExit("--ring needs a causal workload whose S is a multiple of the shard count")
+    n = w.S // n_sh
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    qs = [q[:, i * n:(i + 1) * n].contiguous() for i in range(n_sh)]
+    ks = [k[:, i * n:(i + 1) * n].contiguous() for i in range(n_sh)]
+    vs = [v[:, i * n:(i + 1) * n].contiguous() for i in range(n_sh)]
+    acc = [(torch.empty_like(qs[0]), torch.empty((w.B, w.Hq, n), dtype=torch.float32, device=dev)) for _ in range(n_sh)]
+    part = (torch.empty_like(qs[0]), torch.empty((w.B, w.Hq, n), dtype=torch.float32, device=dev))
+    ws = torch.empty(max(1, workspace_bytes(w.B, n, w.Hkv, w.d, 0 if w.dtype == "bf16" else 1)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        for s in range(n_sh):
+            for t in range(s + 1):  # later key shards would only give empty rows
+                dst = acc[s] if t == 0 else part
+                attn_fwd_into(qs[s], ks[t], vs[t], w.rope_theta, True, dst[0], dst[1], workspace=ws,
+                              q_pos0=s * n, k_pos0=t * n)
+                if t:
+                    attn_merge(acc[s][0], acc[s][1], part[0], part[1], out=acc[s][0], lse=acc[s][1])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the merge kernel alone, back to back (in place into one accumulator)
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        attn_merge(acc[0][0], acc[0][1], part[0], part[1], out=acc[0][0], lse=acc[0][1])
+    e1.record()
+    torch.cuda.synchronize()
+    merge_ms = e0.elapsed_time(e1) / reps
+    esz = 2 if w.dtype == "bf16" else 4
+    merge_bytes = 3 * w.B * n * w.Hq * w.d * esz + 3 * w.B * w.Hq * n * 4  # read 2 parts, write 1
+    fl = flops(w)
+    value = fl / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    res = {
+        "metric": f"ring-composed causal RoPE-GQA attn fwd TFLOP/s ({n_sh} shards on one GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0, sigma) q/k/v)",
+        "config": {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
+                               f"rope_theta={w.rope_theta:g} causal={w.causal}, {n_sh} shards of {n}",
+                   "shard_calls_per_step": n_sh * (n_sh + 1) // 2,
+                   "merges_per_step": n_sh * (n_sh - 1) // 2,
+                   "pct_peak": round(100.0 * value / peak, 2)},
+        "merge": {"bound": "hbm", "kernel_ms": round(merge_ms, 5), "bytes": merge_bytes,
+                  "achieved": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": round(merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +218,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 256 MiB device copy (scale for the rocprofv3 byte counters)")
+    ap.add_argument("--ring", type=int, default=0,
+                    help="split the sequence into this many shards and time one ring-attention pass "
+                         "(shard calls with position offsets + lse merges) on this GPU")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention forward is a single-GPU kernel here "
@@ -145,6 +229,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ring:
+        ring_bench(args)
         return
 
     import torch
