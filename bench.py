@@ -1,6 +1,7 @@
 """Benchmark of the fused causal RoPE-GQA attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline]
+    python bench.py --ring N | --decode [--batch B]   (shard composition / decode step)
 
 A step is one attn_fwd call (key-rotation pre-pass + fused attention kernel) over the whole
 workload, inputs already resident in HBM.  Prints one JSON line:
@@ -209,6 +210,82 @@ def ring_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def decode_bench(args):
+    """Decode steps over a full key/value cache: each step appends the newest key (attn_kv_prepare
+    re-prepares its 64-key tile) and attends one query per (batch row, head) at position S - 1 to
+    all S cached keys (attn_decode).  HBM-bound: the step reads every cached key and value once.
+    The rate is algorithmic bytes (cached K and V of the visible keys, q, out, lse) per second."""
+    import torch
+
+    from transformer_causal_attention_amd import attn_decode, decode_workspace_bytes, kv_prepare, new_kv_cache
+    from transformer_causal_attention_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if args.batch:
+        w = w.with_(B=args.batch)
+    if w.dtype != "bf16":
+        raise SystemExit("the decode path is bf16 only")
+    B, S, Hq, Hkv, d = w.B, w.S, w.Hq, w.Hkv, w.d
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(int(w.seed))
+    k = (torch.randn((B, S, Hkv, d), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    v = (torch.randn((B, S, Hkv, d), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    q = (torch.randn((B, Hq, d), generator=g, device=dev) * w.sigma).to(torch.bfloat16)
+    cache = new_kv_cache(B, S, Hkv, d, dev)
+    kv_prepare(k, v, w.rope_theta, 0, S, cache)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(decode_workspace_bytes(B, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    pos = S - 1
+
+    def step():
+        kv_prepare(k, v, w.rope_theta, pos, pos + 1, cache)
+        attn_decode(q, cache, S, Hkv, w.rope_theta, pos, out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # attn_decode alone (split kernel + join kernel), back to back between two events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        attn_decode(q, cache, S, Hkv, w.rope_theta, pos, out=out, lse=lse, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    decode_ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * B * Hkv * (pos + 1) * d * 2 + 2 * B * Hq * d * 2 + 4 * B * Hq
+    achieved = nbytes / (decode_ms * 1e-3) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": "decode-step attention over a KV cache, algorithmic HBM GB/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, sigma) q/k/v)",
+        "config": {"workload": f"decode over a full cache: B={B} S_cap={S} q_pos={pos} Hq={Hq} Hkv={Hkv} d={d} "
+                               f"rope_theta={w.rope_theta:g}",
+                   "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+                   "step": "attn_kv_prepare of the newest tile + attn_decode"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "attn_decode (attn_decode_kernel + attn_decode_join_kernel)",
+                     "kernel_ms": round(decode_ms, 5), "algorithmic_bytes": nbytes},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +298,9 @@ def main():
     ap.add_argument("--ring", type=int, default=0,
                     help="split the sequence into this many shards and time one ring-attention pass "
                          "(shard calls with position offsets + lse merges) on this GPU")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decode steps (one query per head at position S - 1 over a full KV cache)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size (--decode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention forward is a single-GPU kernel here "
@@ -232,6 +312,9 @@ def main():
         return
     if args.ring:
         ring_bench(args)
+        return
+    if args.decode:
+        decode_bench(args)
         return
 
     import torch

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Element types of q, k, v and out. */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
@@ -138,6 +138,51 @@ int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, in
  */
 int attn_merge(const void *o1, const float *lse1, const void *o2, const float *lse2, int B, int S,
                int H, int head_dim, int dtype, void *out, float *lse, void *stream);
+
+/*
+ * Decode step (the generation loop of the PaLM-in-ColossalAI page, section 2.7, appends one
+ * token at a time; section 2.5 notes that sharing one K/V head makes that step cheaper).
+ * A key/value cache of capacity S_cap keeps rotated keys and transposed values in the
+ * tile layout attn_fwd prepares internally, so each new token re-prepares only its own
+ * 64-key tile and attn_decode reads every cached key and value once.  bf16 only.
+ *
+ * attn_kv_prepare: rotate keys [key0, key1) of k at their own positions and store them, with
+ * the matching values, into `cache`.  Whole 64-key tiles are rewritten: the tile holding key0
+ * is re-read from row 64*floor(key0/64), and keys key1 .. (end of its tile) are stored as
+ * zeros, so k and v must hold valid rows [64*floor(key0/64), key1).
+ *   k, v     device, (B, S_cap, Hkv, head_dim) bfloat16 contiguous, 16-byte aligned
+ *   cache    device, at least attn_fwd_workspace_bytes(B, S_cap, Hkv, head_dim,
+ *            ATTN_DTYPE_BF16) bytes, 16-byte aligned, owned by the caller; layout private
+ *   0 <= key0 < key1 <= S_cap
+ * Returns ATTN_OK, ATTN_EINVAL (null or misaligned pointer, bad sizes or key range, theta not
+ * finite and > 0), ATTN_EUNSUPPORTED (head_dim not 64 or 128, sizes too large),
+ * ATTN_EWORKSPACE (cache too small) or ATTN_EHIP (launch error).
+ */
+int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, int Hkv, int head_dim,
+                    double rope_theta, int key0, int key1, void *cache, size_t cache_bytes,
+                    void *stream);
+
+/* Workspace bytes attn_decode needs for these sizes (partial results of its key splits),
+ * independent of S_cap and q_pos; 0 for unsupported sizes. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim);
+
+/*
+ * Decode attention: for every batch row b and query head h, the query q[b, h] at position
+ * q_pos (rotated there) attends to cached keys 0 .. q_pos of K/V head h / (Hq/Hkv):
+ * the row q_pos of the causal attention attn_fwd computes, with the same scale, rotation and
+ * lse.  Keys 0 .. q_pos of `cache` must have been prepared by attn_kv_prepare with the same
+ * rope_theta.  The key range is split over workgroups and joined by a second kernel.
+ *   q        device, (B, Hq, head_dim) bfloat16 contiguous, 16-byte aligned
+ *   cache    as filled by attn_kv_prepare for (B, S_cap, Hkv, head_dim)
+ *   out      device, (B, Hq, head_dim) bfloat16, 16-byte aligned (written)
+ *   lse      device, (B, Hq) float32, natural log (written)
+ *   workspace  device, >= attn_decode_workspace_bytes(...) bytes, 16-byte aligned, caller owned
+ *   0 <= q_pos < S_cap; Hq a multiple of Hkv
+ * Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE or ATTN_EHIP as above.
+ */
+int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
+                double rope_theta, int q_pos, void *out, float *lse, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */
 void *attn_event_create(void);

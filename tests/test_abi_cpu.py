@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert _lib.abi_version() == 2
+    assert _lib.abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert len(_lib.strerror(code)) > 5
     assert "unknown" in _lib.strerror(12345)
@@ -146,3 +146,55 @@ def test_merge_invalid_arguments(over):
 @pytest.mark.parametrize("over", [dict(d=96), dict(d=256), dict(dtype=2), dict(dtype=-1)])
 def test_merge_unsupported(over):
     assert merge_call(**over) == _lib.ATTN_EUNSUPPORTED
+
+
+def test_decode_workspace_bytes():
+    # partial (o, m, l) float32 rows: B * Hkv * ceil(G / 32) head blocks * splits * 32 heads
+    # with splits = ceil(512 / (B * Hkv * blocks))
+    assert _lib.decode_workspace_bytes(1, 32, 8, 128) == 8 * 64 * 32 * 130 * 4
+    assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 8 * 64 * 32 * 66 * 4
+    assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 2 * 2 * 2 * 64 * 32 * 66 * 4
+    assert _lib.decode_workspace_bytes(1024, 8, 1, 64) == 1024 * 32 * 66 * 4  # one split
+    assert _lib.decode_workspace_bytes(1, 32, 8, 96) == 0
+    assert _lib.decode_workspace_bytes(1, 6, 4, 64) == 0
+    assert _lib.decode_workspace_bytes(0, 8, 1, 64) == 0
+
+
+def prep_call(**over):
+    a = dict(k=P, v=P, B=1, S=256, Hkv=2, d=64, theta=1e4, key0=0, key1=256, cache=P, cb=1 << 30, stream=None)
+    a.update(over)
+    return _lib.kv_prepare_raw(a["k"], a["v"], a["B"], a["S"], a["Hkv"], a["d"], a["theta"], a["key0"], a["key1"],
+                               a["cache"], a["cb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), _lib.ATTN_EINVAL), (dict(v=P + 8), _lib.ATTN_EINVAL), (dict(cache=None), _lib.ATTN_EINVAL),
+    (dict(B=0), _lib.ATTN_EINVAL), (dict(S=0), _lib.ATTN_EINVAL), (dict(Hkv=-1), _lib.ATTN_EINVAL),
+    (dict(theta=0.0), _lib.ATTN_EINVAL), (dict(theta=float("nan")), _lib.ATTN_EINVAL),
+    (dict(key0=-1), _lib.ATTN_EINVAL), (dict(key0=5, key1=5), _lib.ATTN_EINVAL),
+    (dict(key1=257), _lib.ATTN_EINVAL), (dict(key0=300, key1=301), _lib.ATTN_EINVAL),
+    (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1, key1=1), _lib.ATTN_EUNSUPPORTED),
+    (dict(cb=2 * 2 * 256 * 64 * 2 - 1), _lib.ATTN_EWORKSPACE),
+])
+def test_kv_prepare_rejections(over, code):
+    assert prep_call(**over) == code
+
+
+def decode_call(**over):
+    a = dict(q=P, cache=P, B=1, S=256, Hq=8, Hkv=2, d=128, theta=1e4, pos=100, out=P, lse=P, ws=P, wsb=1 << 30,
+             stream=None)
+    a.update(over)
+    return _lib.decode_raw(a["q"], a["cache"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"], a["pos"],
+                           a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.ATTN_EINVAL), (dict(cache=P + 4), _lib.ATTN_EINVAL), (dict(out=P + 2), _lib.ATTN_EINVAL),
+    (dict(lse=P + 1), _lib.ATTN_EINVAL), (dict(lse=None), _lib.ATTN_EINVAL),
+    (dict(Hq=6, Hkv=4), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(theta=-2.0), _lib.ATTN_EINVAL),
+    (dict(pos=-1), _lib.ATTN_EINVAL), (dict(pos=256), _lib.ATTN_EINVAL),
+    (dict(d=32), _lib.ATTN_EUNSUPPORTED),
+    (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=64), _lib.ATTN_EWORKSPACE), (dict(ws=P + 4), _lib.ATTN_EWORKSPACE),
+])
+def test_decode_rejections(over, code):
+    assert decode_call(**over) == code

@@ -12,6 +12,13 @@ lse (B, Hq, S) float32 (natural-log logsumexp of the scaled scores of each row).
 A call with position offsets is one shard of a longer sequence (one ring-attention step);
 attn_merge joins two such partial results.
 
+    cache = new_kv_cache(B, S_cap, Hkv, D, device)
+    kv_prepare(k, v, rope_theta, key0, key1, cache)
+    out, lse = attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos)
+
+is the decode step: one query per (batch row, head) at position q_pos over the cached keys
+0 .. q_pos (bf16); kv_prepare rotates and stores keys as they are appended.
+
 PyTorch only provides device memory and the stream; the computation runs in the HIP
 kernels behind the C ABI of libattn.so (include/attn.h).
 """
@@ -24,6 +31,15 @@ from ._lib import (  # noqa: F401
     abi_version,
     load,
     strerror,
+    decode_workspace_bytes,
     workspace_bytes,
 )
-from .api import attn_fwd, attn_fwd_into, attn_merge  # noqa: F401
+from .api import (  # noqa: F401
+    attn_decode,
+    attn_fwd,
+    attn_fwd_into,
+    attn_merge,
+    kv_cache_bytes,
+    kv_prepare,
+    new_kv_cache,
+)

@@ -24,6 +24,8 @@ _I = ctypes.c_int
 _FWD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 _SHARD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 _MERGE_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]
+_PREP_ARGS = [_VP, _VP, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, ctypes.c_size_t, _VP]
+_DECODE_ARGS = [_VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 SIGNATURES = {
     "attn_abi_version": (_I, []),
     "attn_strerror": (ctypes.c_char_p, [_I]),
@@ -32,6 +34,9 @@ SIGNATURES = {
     "attn_fwd_timed": (_I, _FWD_ARGS + [_VP, _VP]),
     "attn_fwd_shard": (_I, _SHARD_ARGS),
     "attn_merge": (_I, _MERGE_ARGS),
+    "attn_kv_prepare": (_I, _PREP_ARGS),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_decode": (_I, _DECODE_ARGS),
     "attn_event_create": (_VP, []),
     "attn_event_destroy": (_I, [_VP]),
     "attn_event_elapsed_ms": (_I, [_VP, _VP, ctypes.POINTER(ctypes.c_float)]),
@@ -96,6 +101,23 @@ def shard_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_po
 def merge_raw(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream):
     """Call attn_merge with raw pointers; returns the code."""
     return load().attn_merge(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream)
+
+
+def kv_prepare_raw(k, v, B, S_cap, Hkv, head_dim, rope_theta, key0, key1, cache, cache_bytes, stream):
+    """Call attn_kv_prepare with raw pointers; returns the code."""
+    return load().attn_kv_prepare(k, v, B, S_cap, Hkv, head_dim, float(rope_theta), int(key0), int(key1), cache,
+                                  cache_bytes, stream)
+
+
+def decode_workspace_bytes(B, Hq, Hkv, head_dim):
+    return load().attn_decode_workspace_bytes(B, Hq, Hkv, head_dim)
+
+
+def decode_raw(q, cache, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, out, lse, workspace, workspace_bytes_,
+               stream):
+    """Call attn_decode with raw pointers; returns the code."""
+    return load().attn_decode(q, cache, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(q_pos), out, lse,
+                              workspace, workspace_bytes_, stream)
 
 
 class Event:

@@ -107,3 +107,71 @@ def attn_merge(o1, lse1, o2, lse2, out=None, lse=None, stream=None):
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_merge")
     return out, lse
+
+
+def _gpu_bf16(name, t, dims):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != dims or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dims}-D GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (the decode path is bf16 only)")
+
+
+def kv_cache_bytes(B, S_cap, Hkv, head_dim):
+    """Bytes of a decode key/value cache of capacity S_cap (rotated keys and transposed values)."""
+    return _lib.workspace_bytes(B, S_cap, Hkv, head_dim, _lib.ATTN_DTYPE_BF16)
+
+
+def new_kv_cache(B, S_cap, Hkv, head_dim, device):
+    """An uninitialised cache (uint8 GPU tensor) for kv_prepare / attn_decode."""
+    n = kv_cache_bytes(B, S_cap, Hkv, head_dim)
+    if n == 0:
+        raise ValueError("unsupported cache sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def kv_prepare(k, v, rope_theta, key0, key1, cache, stream=None):
+    """Rotate and store keys [key0, key1) of k (and their values) into cache (attn_kv_prepare).
+
+    k, v: (B, S_cap, Hkv, D) bfloat16 holding valid rows from 64 * (key0 // 64) to key1.
+    """
+    _gpu_bf16("k", k, 4)
+    _gpu_bf16("v", v, 4)
+    if v.shape != k.shape or v.device != k.device:
+        raise ValueError("k and v must share shape and device")
+    if cache.dtype != torch.uint8 or cache.device != k.device or not cache.is_contiguous():
+        raise ValueError("cache must be a contiguous uint8 tensor on k's device")
+    B, S_cap, Hkv, D = k.shape
+    st = stream if stream is not None else torch.cuda.current_stream(k.device)
+    rc = _lib.kv_prepare_raw(k.data_ptr(), v.data_ptr(), B, S_cap, Hkv, D, rope_theta, key0, key1,
+                             cache.data_ptr(), cache.numel(), st.cuda_stream)
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_kv_prepare")
+    return cache
+
+
+def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, workspace=None, stream=None):
+    """One decode step: q (B, Hq, D) bfloat16 at position q_pos against cached keys 0 .. q_pos.
+
+    Returns (out (B, Hq, D) bfloat16, lse (B, Hq) float32), equal to row q_pos of attn_fwd.
+    """
+    _gpu_bf16("q", q, 3)
+    B, Hq, D = q.shape
+    if cache.dtype != torch.uint8 or cache.device != q.device or not cache.is_contiguous():
+        raise ValueError("cache must be a contiguous uint8 tensor on q's device")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if tuple(lse.shape) != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq)")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if workspace is None:
+        need = _lib.decode_workspace_bytes(B, Hq, Hkv, D)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if stream is not None:
+            workspace.record_stream(st)
+    rc = _lib.decode_raw(q.data_ptr(), cache.data_ptr(), B, S_cap, Hq, Hkv, D, rope_theta, q_pos, out.data_ptr(),
+                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_decode")
+    return out, lse

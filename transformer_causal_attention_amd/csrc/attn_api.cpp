@@ -4,6 +4,7 @@
 
 #include "attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -63,6 +64,9 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   pp.S = S;
   pp.Hkv = Hkv;
   pp.S_pad = (int)s_pad;
+  pp.S_rows = S;
+  pp.tile0 = 0;
+  pp.n_run = (int)(s_pad / kTileKeys);
   pp.k_pos0 = k_pos0;
   hipError_t err = attn::launch_prep_kv<D>(pp, tab, st);
   if (err != hipSuccess) return err;
@@ -220,6 +224,108 @@ ATTN_EXPORT void *attn_event_create(void) {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+
+namespace {
+
+// Decode splits: about kDecodeWgs workgroups over (b, K/V head, head block, key range).
+constexpr int kDecodeWgs = 512;
+
+int decode_hblk(int G) { return (G + 31) / 32; }
+
+int decode_max_splits(int B, int Hkv, int G) {
+  const long long units = (long long)B * Hkv * decode_hblk(G);
+  return (int)std::max<long long>(1, (kDecodeWgs + units - 1) / units);
+}
+
+int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
+  if (B < 1 || S_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_EINVAL;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (S_cap > (1 << 28) || (double)Hkv * d > (double)(1 << 24)) return ATTN_EUNSUPPORTED;
+  // one (b, g) tile run of the cache is addressed with 32-bit offsets
+  if ((double)padded_len(S_cap) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
+  if ((double)B * Hq * d > 4.0e15) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, int Hkv, int head_dim,
+                                double rope_theta, int key0, int key1, void *cache, size_t cache_bytes,
+                                void *stream) {
+  if (!k || !v || !cache) return ATTN_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(cache, 16)) return ATTN_EINVAL;
+  const int rc = check_decode_shape(B, S_cap, Hkv, Hkv, head_dim);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
+  if (key0 < 0 || key1 <= key0 || key1 > S_cap) return ATTN_EINVAL;
+  if (cache_bytes < attn_fwd_workspace_bytes(B, S_cap, Hkv, head_dim, ATTN_DTYPE_BF16)) return ATTN_EWORKSPACE;
+  const size_t s_pad = padded_len(S_cap);
+  attn::PrepParams pp;
+  pp.k = static_cast<const __bf16 *>(k);
+  pp.v = static_cast<const __bf16 *>(v);
+  pp.kr = static_cast<__bf16 *>(cache);
+  pp.vt = pp.kr + (size_t)B * Hkv * s_pad * head_dim;
+  pp.B = B;
+  pp.S = key1;
+  pp.Hkv = Hkv;
+  pp.S_pad = (int)s_pad;
+  pp.S_rows = S_cap;
+  pp.tile0 = key0 / kTileKeys;
+  pp.n_run = (key1 + kTileKeys - 1) / kTileKeys - pp.tile0;
+  pp.k_pos0 = 0;
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = head_dim == 64 ? attn::launch_prep_kv<64>(pp, tab, st) : attn::launch_prep_kv<128>(pp, tab, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim) {
+  if (check_decode_shape(B, 1, Hq, Hkv, head_dim) != ATTN_OK) return 0;
+  const int G = Hq / Hkv;
+  const size_t rows = (size_t)B * Hkv * decode_hblk(G) * decode_max_splits(B, Hkv, G) * 32;
+  return rows * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
+                            double rope_theta, int q_pos, void *out, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!q || !cache || !out || !lse) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
+  const int rc = check_decode_shape(B, S_cap, Hq, Hkv, head_dim);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
+  if (q_pos < 0 || q_pos >= S_cap) return ATTN_EINVAL;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, head_dim);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_EWORKSPACE;
+  const size_t s_pad = padded_len(S_cap);
+  const int G = Hq / Hkv;
+  attn::DecodeParams p;
+  p.q = static_cast<const __bf16 *>(q);
+  p.kr = static_cast<const __bf16 *>(cache);
+  p.vt = p.kr + (size_t)B * Hkv * s_pad * head_dim;
+  p.out = static_cast<__bf16 *>(out);
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = G;
+  p.S_pad = (int)s_pad;
+  p.q_pos = q_pos;
+  p.n_hblk = decode_hblk(G);
+  const int tiles = (q_pos + 1 + kTileKeys - 1) / kTileKeys;
+  const int max_split = decode_max_splits(B, Hkv, G);
+  p.tiles_per_split = (tiles + max_split - 1) / max_split;
+  p.n_split = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  const size_t rows = (size_t)B * Hkv * p.n_hblk * p.n_split * 32;
+  p.po = static_cast<float *>(workspace);
+  p.pm = p.po + rows * head_dim;
+  p.pl = p.pm + rows;
+  p.q_scale = q_scale(head_dim);
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = head_dim == 64 ? attn::launch_decode<64>(p, tab, st) : attn::launch_decode<128>(p, tab, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
 ATTN_EXPORT int attn_event_destroy(void *ev) {

@@ -54,8 +54,11 @@ struct PrepParams {
   const __bf16 *v;  // (B, S, Hkv, D)
   __bf16 *kr;       // 64-key tiles (B, Hkv, S_pad/64) x [D/8][64][8]
   __bf16 *vt;       // 64-key tiles (B, Hkv, S_pad/64) x [8][D][8]
-  int B, S, Hkv, S_pad;
-  int k_pos0;       // position of key row 0
+  int B, S, Hkv, S_pad;  // S: rows that hold keys (later rows of a tile are zeros);
+                         // S_pad: keys per (b, g) in the output layout, a multiple of 64
+  int S_rows;            // rows per batch row in k and v (their batch stride), >= S
+  int tile0, n_run;      // the tiles prepared: [tile0, tile0 + n_run)
+  int k_pos0;            // position of key row 0
 };
 
 // Merge of two partial results: o1, o2, out (B, S, H, D) of the element type; lse1, lse2, lse
@@ -67,6 +70,22 @@ struct MergeParams {
   float *lse;
   long long rows;  // B * S * H
   int S, H;
+};
+
+// Decode step: one query row per (b, head) at position q_pos against a prepared K/V cache.
+struct DecodeParams {
+  const __bf16 *q;   // (B, Hq, D)
+  const __bf16 *kr;  // prepared cache: rotated keys, 64-key tiles (B, Hkv, S_pad/64) x [D/8][64][8]
+  const __bf16 *vt;  // prepared cache: transposed values, (B, Hkv, S_pad/64) x [8][D][8]
+  __bf16 *out;       // (B, Hq, D)
+  float *lse;        // (B, Hq)
+  float *po;         // partial outputs: (B, Hkv, n_hblk, n_split, 32 heads, D)
+  float *pm, *pl;    // partial maxima and sums: (B, Hkv, n_hblk, n_split, 32 heads)
+  int B, Hq, Hkv, G, S_pad;
+  int q_pos;             // the query's position; keys 0 .. q_pos are visible
+  int n_hblk;            // blocks of 32 heads per K/V head: ceil(G / 32)
+  int n_split, tiles_per_split;
+  float q_scale;
 };
 
 // Fraction of a turn for position p and frequency f (revolutions per position):

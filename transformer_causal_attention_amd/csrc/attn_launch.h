@@ -21,4 +21,7 @@ hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t
 template <typename T, int D>
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
 
+template <int D>
+hipError_t launch_decode(const DecodeParams &p, const RopeTable &tab, hipStream_t stream);
+
 }  // namespace attn

@@ -32,14 +32,14 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
   __shared__ __attribute__((aligned(16))) uint16_t vs[64 * VSTR];
   const int tid = threadIdx.x;
 
-  const int n_tiles = p.S_pad / 64;
-  const int unit = blockIdx.x / n_tiles;  // (b, g)
-  const int j0 = (blockIdx.x % n_tiles) * 64;
+  const int n_tiles = p.S_pad / 64;       // tiles per (b, g) in the output layout
+  const int unit = blockIdx.x / p.n_run;  // (b, g)
+  const int j0 = (p.tile0 + blockIdx.x % p.n_run) * 64;
   const int g = unit % p.Hkv;
   const int b = unit / p.Hkv;
   const size_t src_rs = (size_t)p.Hkv * D;  // elements between consecutive keys in k, v
-  const __bf16 *ksrc = p.k + ((size_t)b * p.S * p.Hkv + g) * D;
-  const __bf16 *vsrc = p.v + ((size_t)b * p.S * p.Hkv + g) * D;
+  const __bf16 *ksrc = p.k + ((size_t)b * p.S_rows * p.Hkv + g) * D;
+  const __bf16 *vsrc = p.v + ((size_t)b * p.S_rows * p.Hkv + g) * D;
 
   // Every load of the tile is issued before any of them is used, so the block waits for memory
   // once.  Rows past S load row S-1 (in bounds) and are replaced by zeros afterwards.
@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
 
 template <int D>
 hipError_t launch_prep_kv(const PrepParams &p, const RopeTable &tab, hipStream_t stream) {
-  const long long blocks = (long long)p.B * p.Hkv * (p.S_pad / 64);
+  const long long blocks = (long long)p.B * p.Hkv * p.n_run;
   hipLaunchKernelGGL(prep_kv_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
   return hipGetLastError();
 }
