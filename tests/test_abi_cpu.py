@@ -149,12 +149,12 @@ def test_merge_unsupported(over):
 
 
 def test_decode_workspace_bytes():
-    # partial (o, m, l) float32 rows: B * Hkv * ceil(G / 32) head blocks * splits * 32 heads
-    # with splits = ceil(512 / (B * Hkv * blocks))
-    assert _lib.decode_workspace_bytes(1, 32, 8, 128) == 8 * 64 * 32 * 130 * 4
-    assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 8 * 64 * 32 * 66 * 4
-    assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 2 * 2 * 2 * 64 * 32 * 66 * 4
-    assert _lib.decode_workspace_bytes(1024, 8, 1, 64) == 1024 * 32 * 66 * 4  # one split
+    # partial (o, m, l) float32 rows: B * Hq heads * splits, with
+    # splits = ceil(1024 / (B * Hkv * ceil(G / 32))) at most
+    assert _lib.decode_workspace_bytes(1, 32, 8, 128) == 32 * 128 * 130 * 4
+    assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 64 * 128 * 66 * 4
+    assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 256 * 128 * 66 * 4
+    assert _lib.decode_workspace_bytes(2048, 8, 1, 64) == 2048 * 8 * 66 * 4  # one split
     assert _lib.decode_workspace_bytes(1, 32, 8, 96) == 0
     assert _lib.decode_workspace_bytes(1, 6, 4, 64) == 0
     assert _lib.decode_workspace_bytes(0, 8, 1, 64) == 0

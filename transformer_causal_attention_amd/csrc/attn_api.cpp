@@ -228,14 +228,17 @@ ATTN_EXPORT void *attn_event_create(void) {
 
 namespace {
 
-// Decode splits: about kDecodeWgs workgroups over (b, K/V head, head block, key range).
-constexpr int kDecodeWgs = 512;
+// Decode splits: about kDecodeWaves one-wave workgroups over (b, K/V head, head block, key
+// range), i.e. four per CU, one per SIMD, and at least kDecodeMinHalves 32-key half tiles per
+// key range so that each wave's loads fill its pipeline.
+constexpr int kDecodeWaves = 1024;
+constexpr int kDecodeMinHalves = 4;
 
 int decode_hblk(int G) { return (G + 31) / 32; }
 
 int decode_max_splits(int B, int Hkv, int G) {
   const long long units = (long long)B * Hkv * decode_hblk(G);
-  return (int)std::max<long long>(1, (kDecodeWgs + units - 1) / units);
+  return (int)std::max<long long>(1, (kDecodeWaves + units - 1) / units);
 }
 
 int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
@@ -244,7 +247,7 @@ int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
   if (S_cap > (1 << 28) || (double)Hkv * d > (double)(1 << 24)) return ATTN_EUNSUPPORTED;
   // one (b, g) tile run of the cache is addressed with 32-bit offsets
   if ((double)padded_len(S_cap) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
-  if ((double)B * Hq * d > 4.0e15) return ATTN_EUNSUPPORTED;
+  if ((double)B * Hq > (double)(1 << 24)) return ATTN_EUNSUPPORTED;  // one join workgroup per (b, head)
   return ATTN_OK;
 }
 
@@ -282,8 +285,7 @@ ATTN_EXPORT int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, 
 
 ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim) {
   if (check_decode_shape(B, 1, Hq, Hkv, head_dim) != ATTN_OK) return 0;
-  const int G = Hq / Hkv;
-  const size_t rows = (size_t)B * Hkv * decode_hblk(G) * decode_max_splits(B, Hkv, G) * 32;
+  const size_t rows = (size_t)B * Hq * decode_max_splits(B, Hkv, Hq / Hkv);
   return rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
@@ -313,11 +315,11 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, 
   p.S_pad = (int)s_pad;
   p.q_pos = q_pos;
   p.n_hblk = decode_hblk(G);
-  const int tiles = (q_pos + 1 + kTileKeys - 1) / kTileKeys;
-  const int max_split = decode_max_splits(B, Hkv, G);
-  p.tiles_per_split = (tiles + max_split - 1) / max_split;
-  p.n_split = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
-  const size_t rows = (size_t)B * Hkv * p.n_hblk * p.n_split * 32;
+  const int halves = (q_pos + 1 + 31) / 32;
+  const int max_split = std::max(1, std::min(decode_max_splits(B, Hkv, G), halves / kDecodeMinHalves));
+  p.halves_per_split = (halves + max_split - 1) / max_split;
+  p.n_split = (halves + p.halves_per_split - 1) / p.halves_per_split;
+  const size_t rows = (size_t)B * Hq * p.n_split;
   p.po = static_cast<float *>(workspace);
   p.pm = p.po + rows * head_dim;
   p.pl = p.pm + rows;

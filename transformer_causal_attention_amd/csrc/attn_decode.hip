@@ -2,29 +2,36 @@
 // for gfx950.  Same definition as the forward (RoPE on q and k, scores / sqrt(head_dim), keys
 // after the query masked, stable softmax, lse; Picotron, PaLM and llama3-from-scratch pages),
 // restricted to the single row at position q_pos -- the generation loop of the PaLM page
-// (section 2.5 notes that a shared K/V head makes this step cheaper) appends one token at a
-// time and attends it to every cached key.
+// (section 2.7) appends one token at a time and attends it to every cached key; section 2.5
+// notes that a shared K/V head makes this step cheaper.
 //
 // The cache is kept in the preparation pass's tile layout (rotated keys, transposed values,
-// 64-key tiles), so every MFMA operand is one 16-byte LDS read as in the forward kernel, and
-// a new token only re-prepares the last tile.  The step is HBM-bound: every cached key and
-// value is read once.  The key range is split over workgroups (split-K), each leaves a
-// partial (o, m, l) for its keys, and a second kernel joins the partials by their maxima.
+// 64-key tiles), so every MFMA operand is one 16-byte load at (per-lane base + constant), and a
+// new token only re-prepares the last tile.  The step is HBM-bound: every cached key and value
+// is read once and no tile is shared between waves, so tiles go straight from HBM into
+// registers (no LDS), PD half tiles (32 keys) in flight per wave: the bytes in flight per CU are
+// then bounded by the register file rather than by LDS.  The key range of each (b, K/V head) is
+// split over waves (split-K); each leaves a partial (o, m, l) for its keys, and a second kernel
+// joins the partials by their maxima.
 //
-// A workgroup is one wave: it holds the 32 query heads of a head block (the G heads sharing
-// the K/V head, 32 at a time) as the columns of the MFMA operand Q^T, so S^T = K Q^T puts one
-// head per lane and each staged tile serves every head of the group.  Tiles are copied to
-// LDS with buffer_load ... lds, two in flight.
+// A workgroup is one wave holding the (up to) 32 query heads of a head block, the G heads that
+// share the K/V head, 32 at a time, as the columns of the MFMA operand Q^T: S^T = K Q^T puts one
+// head per lane and each loaded half tile serves every head of the block.
 
 #include "attn_device.h"
-
-#define LDS_AS __attribute__((address_space(3)))
 
 namespace attn {
 
 namespace {
 
 constexpr int DBN = 64;  // keys per tile
+#ifndef DECODE_DEPTH
+#define DECODE_DEPTH 2
+#endif
+constexpr int kDecodeDepth = DECODE_DEPTH;  // half tiles in flight per wave
+// A buffer offset past every cache run (runs are < 2^31 bytes); with the per-lane part added
+// it stays below 2^31, so the range check sees it as out of bounds.
+constexpr int kPastEnd = 0x7ff00000;
 
 __device__ __forceinline__ float dec_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -42,13 +49,11 @@ __device__ __forceinline__ f32x16 dec_mfma(const bf16x8 &a, const bf16x8 &b, con
 
 }  // namespace
 
-template <int D>
+template <int D, int PD>
 __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTable tab) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int TB = DBN * D * 2;  // bytes of one K or V^T tile
-  // [buffer][K tile, V^T tile]
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TB];
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -63,65 +68,83 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   const int g = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  const int n_keys = p.q_pos + 1;  // keys 0 .. q_pos are visible
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min((n_keys + DBN - 1) / DBN, t_begin + p.tiles_per_split);
-
-  const size_t n_tiles = (size_t)(p.S_pad / DBN);
-  const size_t unit_bytes = n_tiles * TB;
-  const char *kr_tiles = reinterpret_cast<const char *>(p.kr) + ((size_t)b * p.Hkv + g) * unit_bytes;
-  const char *vt_tiles = reinterpret_cast<const char *>(p.vt) + ((size_t)b * p.Hkv + g) * unit_bytes;
-  const __amdgpu_buffer_rsrc_t kr_buf =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kr_tiles), 0, (int)unit_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vt_buf =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vt_tiles), 0, (int)unit_bytes, 0x00020000);
-  const uint32_t dma_lane = 16u * (uint32_t)lane;
-  auto stage = [&](int t, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < TB / 1024; ++r) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr_buf, (LDS_AS void *)(lds[buf][0] + r * 1024), 16, dma_lane,
-                                               (uint32_t)t * TB + r * 1024, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vt_buf, (LDS_AS void *)(lds[buf][1] + r * 1024), 16, dma_lane,
-                                               (uint32_t)t * TB + r * 1024, 0, 0);
-    }
-  };
-  if (t_begin < t_end) stage(t_begin, 0);
+  const int key_end0 = p.q_pos + 1;  // keys 0 .. q_pos are visible
+  const int h_begin = split * p.halves_per_split;
+  const int h_end = min((key_end0 + 31) / 32, h_begin + p.halves_per_split);
+  const int key_end = min(key_end0, 32 * h_end);  // first key past this split's range
 
   // Q^T operand: lane l holds head column l % 32 (zeros past the group), dimensions 16kk + 8hh
-  // + e, rotated at q_pos and scaled by log2(e)/sqrt(D)
+  // + e, rotated at q_pos and scaled by log2(e)/sqrt(D).  Loaded before the cache so that the
+  // rotation only waits for these loads.
   const int hc = hb * 32 + l32;  // head within the group
   const bool head_ok = hc < p.G;
   const int head = g * p.G + hc;
-  bf16x8 qf[NKK];
+  u32x4 raw[NKK];
   {
-    u32x4 raw[NKK];
     const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       raw[kk] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // The (b, g) run of tiles as buffer resources: a load whose (per-lane) offset lies past the
+  // end returns zeros without a memory access, which is how the padded steps after h_end read
+  // nothing.
+  const uint32_t unit_bytes = (uint32_t)(p.S_pad / DBN) * TB;
+  const size_t unit = (size_t)b * p.Hkv + g;
+  const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(reinterpret_cast<const char *>(p.kr) + unit * unit_bytes), 0, (int)unit_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(reinterpret_cast<const char *>(p.vt) + unit * unit_bytes), 0, (int)unit_bytes, 0x00020000);
+  // half tile h = 2t + jb: keys 64t + 32jb .. +31.  K operand chunk kk: [chunk 2kk+hh][key][8];
+  // V^T operand (tt, cb): key group 4jb + 2tt + hh, column 32cb + l32.
+  const int k_lane = hh * 1024 + l32 * 16;
+  const int v_lane = hh * 16 * D + l32 * 16;
+  auto half_base = [&](int h) __attribute__((always_inline)) {
+    return h < h_end ? (h >> 1) * TB + (h & 1) * 512 : kPastEnd;
+  };
+  auto half_vbase = [&](int h) __attribute__((always_inline)) {
+    return h < h_end ? (h >> 1) * TB + (h & 1) * 4 * 16 * D : kPastEnd;
+  };
+  bf16x8 kq[PD][NKK], vq[PD][2][NCB];
+  auto load_half = [&](int h, int r) __attribute__((always_inline)) {
+    const int kb = half_base(h), vb = half_vbase(h);
 #pragma unroll
-    for (int kk = 0; kk < NKK / 2; ++kk) {
-      u32x4 olo, ohi;
+    for (int kk = 0; kk < NKK; ++kk)
+      kq[r][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kbuf, kb + k_lane + kk * 2048, 0, 0));
 #pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
-        float r[2][2];
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int z = 0; z < 2; ++z) {
-          const int e = 2 * wv + z;
-          const float t = turn_fraction(p.q_pos, tab.rev[16 * kk + 8 * hh + e]);
-          const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);  // turns
-          const uint32_t lo = raw[kk][wv], hi = raw[kk + NKK / 2][wv];
-          const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
-          const float yv = z ? bf16_hi(hi) : bf16_lo(hi);
-          r[0][z] = (xv * cs - yv * sn) * p.q_scale;
-          r[1][z] = (yv * cs + xv * sn) * p.q_scale;
-        }
-        olo[wv] = pack_bf16x2(r[0][0], r[0][1]);
-        ohi[wv] = pack_bf16x2(r[1][0], r[1][1]);
+      for (int cb = 0; cb < NCB; ++cb)
+        vq[r][tt][cb] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vbuf, vb + v_lane + tt * 2 * 16 * D + cb * 512, 0, 0));
+  };
+#pragma unroll
+  for (int r = 0; r < PD; ++r) load_half(h_begin + r, r);
+
+  bf16x8 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK / 2; ++kk) {
+    u32x4 olo, ohi;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) {
+      float r[2][2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const int e = 2 * wv + z;
+        const float t = turn_fraction(p.q_pos, tab.rev[16 * kk + 8 * hh + e]);
+        const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);  // turns
+        const uint32_t lo = raw[kk][wv], hi = raw[kk + NKK / 2][wv];
+        const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
+        const float yv = z ? bf16_hi(hi) : bf16_lo(hi);
+        r[0][z] = (xv * cs - yv * sn) * p.q_scale;
+        r[1][z] = (yv * cs + xv * sn) * p.q_scale;
       }
-      qf[kk] = __builtin_bit_cast(bf16x8, olo);
-      qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
+      olo[wv] = pack_bf16x2(r[0][0], r[0][1]);
+      ohi[wv] = pack_bf16x2(r[1][0], r[1][1]);
     }
+    qf[kk] = __builtin_bit_cast(bf16x8, olo);
+    qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
   }
 
   f32x16 o[NCB];
@@ -130,130 +153,137 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   float m_run = -INFINITY;  // running maximum of the base-2 scores of this lane's head
   float l_run = 0.f;        // this lane half's share of the running sum
 
-  const int k_lane = hh * 1024 + l32 * 16;
-  const int v_lane = hh * 16 * D + l32 * 16;
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t is in LDS; the other buffer's reads of the previous step are done
-    if (t + 1 < t_end) stage(t + 1, buf ^ 1);
-    const char *kd = lds[buf][0];
-    const char *vd = lds[buf][1];
-    const int kb0 = t * DBN;
-    f32x16 sc[2];
+  // Steps past h_end (padding to a multiple of PD) load zeros and have every key masked, so the
+  // loop body needs no branch around its loads.
+  const int n_steps = (h_end - h_begin + PD - 1) / PD * PD;
+  for (int s0 = 0; s0 < n_steps; s0 += PD) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      sc[jb] = f32x16{};
+    for (int r = 0; r < PD; ++r) {
+      const int h = h_begin + s0 + r;
+      f32x16 sc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        sc[jb] = dec_mfma(*reinterpret_cast<const bf16x8 *>(kd + k_lane + 2 * kk * 1024 + jb * 512), qf[kk], sc[jb]);
-    }
-    if (kb0 + DBN - 1 > p.q_pos) {  // keys after the query
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int kk = 0; kk < NKK; ++kk) sc = dec_mfma(kq[r][kk], qf[kk], sc);
+      // keys of this half: 32h + 8(v>>2) + 4hh + (v&3)
+      if (32 * h + 31 >= key_end) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (kb0 + 32 * jb + 8 * (v >> 2) + 4 * hh + (v & 3) > p.q_pos) sc[jb][v] = -INFINITY;
-    }
-    float mx = -INFINITY;
+          if (32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) >= key_end) sc[v] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jb][v]);
-    mx = dec_max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx);  // finite: key kb0 <= q_pos is in every tile
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.f;
-    bf16x8 pk[2][2];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+      mx = dec_max_xor32(mx);
+      // finite from the first step on: key 32 h_begin <= q_pos is in it
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float rs = 0.f;
+      bf16x8 pk[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         u32x4 wd;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          const float e0 = __builtin_amdgcn_exp2f(sc[jb][8 * tt + 2 * ww] - m_new);
-          const float e1 = __builtin_amdgcn_exp2f(sc[jb][8 * tt + 2 * ww + 1] - m_new);
+          const float e0 = __builtin_amdgcn_exp2f(sc[8 * tt + 2 * ww] - m_new);
+          const float e1 = __builtin_amdgcn_exp2f(sc[8 * tt + 2 * ww + 1] - m_new);
           rs += e0 + e1;
           wd[ww] = pack_bf16x2(e0, e1);
         }
-        pk[jb][tt] = __builtin_bit_cast(bf16x8, wd);
+        pk[tt] = __builtin_bit_cast(bf16x8, wd);
       }
-    l_run = l_run * alpha + rs;
+      l_run = l_run * alpha + rs;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+      for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          o[cb] = dec_mfma(*reinterpret_cast<const bf16x8 *>(vd + v_lane + (4 * jb + 2 * tt) * 16 * D + cb * 512),
-                           pk[jb][tt], o[cb]);
+        for (int cb = 0; cb < NCB; ++cb) o[cb] = dec_mfma(vq[r][tt][cb], pk[tt], o[cb]);
+      load_half(h + PD, r);
+    }
   }
 
-  // partial result of this split: o as [split-row][32 heads][D] floats, m and l per head
-  const size_t prow = (((size_t)b * p.Hkv + g) * p.n_hblk + hb) * p.n_split + split;
-  float *po = p.po + (prow * 32 + l32) * D;
+  // partial result of this split for the heads of the group: o as [split][G heads][D] floats,
+  // m and l per head
+  if (head_ok) {
+    const size_t prow = (unit * p.n_split + split) * p.G + hc;
+    float *po = p.po + prow * D;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4)
-      *reinterpret_cast<f32x4 *>(po + 32 * cb + 8 * v4 + 4 * hh) =
-          f32x4{o[cb][4 * v4], o[cb][4 * v4 + 1], o[cb][4 * v4 + 2], o[cb][4 * v4 + 3]};
+      for (int v4 = 0; v4 < 4; ++v4)
+        *reinterpret_cast<f32x4 *>(po + 32 * cb + 8 * v4 + 4 * hh) =
+            f32x4{o[cb][4 * v4], o[cb][4 * v4 + 1], o[cb][4 * v4 + 2], o[cb][4 * v4 + 3]};
+  }
   const float l_tot = l_run + dec_xor32(l_run);
-  if (hh == 0) {
-    p.pm[prow * 32 + l32] = m_run;
-    p.pl[prow * 32 + l32] = l_tot;
+  if (hh == 0 && head_ok) {
+    const size_t prow = (unit * p.n_split + split) * p.G + hc;
+    p.pm[prow] = m_run;
+    p.pl[prow] = l_tot;
   }
 }
 
 // Joins the splits of every (b, head): m = max m_i, l = sum l_i 2^(m_i - m),
-// out = sum o_i 2^(m_i - m) / l (bf16), lse = ln 2 * (m + log2 l).  32 threads per head, each
-// owning D/32 consecutive dimensions.
+// out = sum o_i 2^(m_i - m) / l (bf16), lse = ln 2 * (m + log2 l).  One 256-thread workgroup
+// per (b, head): the n_split partial rows are read in parallel, R = 256 / (D/4) rows at a time
+// with D/4 threads (16 bytes each) per row, and the R partial sums are added through LDS.
 template <int D>
 __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
-  constexpr int E = D / 32;
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long bh = t / 32;  // (b, head)
-  if (bh >= (long long)p.B * p.Hq) return;
-  const int part = (int)(t % 32);
-  const int head = (int)(bh % p.Hq);
-  const int b = (int)(bh / p.Hq);
+  constexpr int TPR = D / 4;      // threads per partial row
+  constexpr int R = 256 / TPR;    // rows read at once
+  __shared__ float red_m[4];
+  __shared__ float red_l[R];
+  __shared__ __attribute__((aligned(16))) float red_o[R][D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;  // (b, head)
+  const int head = bh % p.Hq;
+  const int b = bh / p.Hq;
   const int g = head / p.G;
   const int hc = head % p.G;
-  const int hb = hc / 32;
-  const size_t row0 = (((size_t)b * p.Hkv + g) * p.n_hblk + hb) * p.n_split;
-  const int n_used = min(p.n_split, ((p.q_pos + 1 + DBN - 1) / DBN + p.tiles_per_split - 1) / p.tiles_per_split);
+  const size_t unit = (size_t)b * p.Hkv + g;
+  auto row = [&](int s) __attribute__((always_inline)) { return (unit * p.n_split + s) * p.G + hc; };
+
   float m = -INFINITY;
-  for (int s = 0; s < n_used; ++s) m = fmaxf(m, p.pm[(row0 + s) * 32 + hc % 32]);
-  float l = 0.f, acc[E];
+  for (int s = tid; s < p.n_split; s += 256) m = fmaxf(m, p.pm[row(s)]);
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s = 0; s < n_used; ++s) {
-    const size_t r = (row0 + s) * 32 + hc % 32;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) red_m[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+  const int sg = tid / TPR;  // row group
+  const int c4 = tid % TPR;  // dimensions 4 c4 .. 4 c4 + 3
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int s = sg; s < p.n_split; s += R) {
+    const size_t r = row(s);
     const float c = __builtin_amdgcn_exp2f(p.pm[r] - m);
+    acc += *reinterpret_cast<const f32x4 *>(p.po + r * D + 4 * c4) * c;
     l += p.pl[r] * c;
-    const float *src = p.po + r * D + part * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += src[e] * c;
   }
-  const float inv = 1.0f / l;
-  __bf16 *dst = p.out + ((size_t)b * p.Hq + head) * D + part * E;
+  *reinterpret_cast<f32x4 *>(&red_o[sg][4 * c4]) = acc;
+  if (c4 == 0) red_l[sg] = l;
+  __syncthreads();
+  if (tid < D / 2) {
+    float o0 = 0.f, o1 = 0.f, lt = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; e += 2) *reinterpret_cast<uint32_t *>(dst + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
-  if (part == 0) p.lse[(size_t)b * p.Hq + head] = (m + __log2f(l)) * 0.69314718055994531f;
+    for (int i = 0; i < R; ++i) {
+      o0 += red_o[i][2 * tid];
+      o1 += red_o[i][2 * tid + 1];
+      lt += red_l[i];
+    }
+    const float inv = 1.0f / lt;
+    *reinterpret_cast<uint32_t *>(p.out + ((size_t)b * p.Hq + head) * D + 2 * tid) = pack_bf16x2(o0 * inv, o1 * inv);
+    if (tid == 0) p.lse[(size_t)b * p.Hq + head] = (m + __log2f(lt)) * 0.69314718055994531f;
+  }
 }
 
 template <int D>
 hipError_t launch_decode(const DecodeParams &p, const RopeTable &tab, hipStream_t stream) {
   const long long wgs = (long long)p.B * p.Hkv * p.n_hblk * p.n_split;
-  hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((unsigned)wgs), dim3(64), 0, stream, p, tab);
+  hipLaunchKernelGGL((attn_decode_kernel<D, kDecodeDepth>), dim3((unsigned)wgs), dim3(64), 0, stream, p, tab);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long threads = (long long)p.B * p.Hq * 32;
-  hipLaunchKernelGGL(attn_decode_join_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(attn_decode_join_kernel<D>, dim3((unsigned)((long long)p.B * p.Hq)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -79,12 +79,13 @@ struct DecodeParams {
   const __bf16 *vt;  // prepared cache: transposed values, (B, Hkv, S_pad/64) x [8][D][8]
   __bf16 *out;       // (B, Hq, D)
   float *lse;        // (B, Hq)
-  float *po;         // partial outputs: (B, Hkv, n_hblk, n_split, 32 heads, D)
-  float *pm, *pl;    // partial maxima and sums: (B, Hkv, n_hblk, n_split, 32 heads)
+  float *po;         // partial outputs: (B, Hkv, n_split, G, D)
+  float *pm, *pl;    // partial maxima and sums: (B, Hkv, n_split, G)
   int B, Hq, Hkv, G, S_pad;
   int q_pos;             // the query's position; keys 0 .. q_pos are visible
   int n_hblk;            // blocks of 32 heads per K/V head: ceil(G / 32)
-  int n_split, tiles_per_split;
+  int n_split;           // key ranges per (b, K/V head)
+  int halves_per_split;  // 32-key half tiles per key range
   float q_scale;
 };
 
