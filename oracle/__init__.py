@@ -3,6 +3,7 @@
 from .attn_oracle import (  # noqa: F401
     apply_rope,
     attention,
+    attention_backward,
     merge,
     attention_weights,
     causal_mask,

@@ -39,6 +39,10 @@ Readings where the pages are silent or disagree (each also listed in the design 
     shard's partial result leaves that result unchanged.
   * GQA grouping is contiguous: query head h reads K/V head h // (Hq // Hkv).
   * lse is the natural-log logsumexp of the scaled scores over the visible keys.
+  * The backward is the exact gradient of this forward with respect to q, k and v for a given
+    gradient of the output (the pages train these models -- the PaLM page's wrapper returns a
+    cross-entropy loss, section 2.7 -- but print no backward); the gradient of lse is not
+    an input.
 """
 
 import numpy as np
@@ -54,6 +58,7 @@ __all__ = [
     "attention_weights",
     "attention",
     "merge",
+    "attention_backward",
 ]
 
 
@@ -209,3 +214,48 @@ def merge(o1, lse1, o2, lse2):
     out = (np.transpose(w1, (0, 2, 1))[..., None] * np.asarray(o1, dtype=np.float64)
            + np.transpose(w2, (0, 2, 1))[..., None] * np.asarray(o2, dtype=np.float64))
     return out, lse
+
+
+def attention_backward(q, k, v, dout, rope_theta, causal=True):
+    """Gradients (dq, dk, dv) of the attention above for an output gradient dout, in float64.
+
+    q, dout: (B, S, Hq, d); k, v: (B, S, Hkv, d).  Differentiating the forward's steps in
+    reverse order, for each (batch, query head h) with K/V head g:
+      out = P v                 ->  dv_g += P^T dout,   dP = dout v^T
+      P = softmax(s) per row    ->  ds = P * (dP - rowsum(dout * out))
+      s = q' k'^T / sqrt(d)     ->  dq' = ds k' / sqrt(d),   dk'_g += ds^T q' / sqrt(d)
+      x' = R(position) x        ->  dx = R(position)^T dx' = R(-position) dx'
+    (masked scores have P = 0 and so no gradient; a K/V head's gradient sums over the query
+    heads that share it).
+    Returns dq (B, S, Hq, d), dk and dv (B, S, Hkv, d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("k, v must be (B, S, Hkv, d) and dout like q")
+    pos = np.arange(S)
+    q_rot = apply_rope(q, pos, rope_theta)
+    k_rot = apply_rope(k, pos, rope_theta)
+    scale = 1.0 / np.sqrt(np.float64(d))
+
+    dq_rot = np.zeros_like(q_rot)
+    dk_rot = np.zeros_like(k_rot)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            P, _, _ = attention_weights(q_rot[b, :, h, :], k_rot[b, :, g, :], pos, causal)
+            o = P @ v[b, :, g, :]
+            do = dout[b, :, h, :]
+            dv[b, :, g, :] += P.T @ do
+            dP = do @ v[b, :, g, :].T
+            ds = P * (dP - (do * o).sum(axis=-1, keepdims=True))
+            dq_rot[b, :, h, :] = (ds @ k_rot[b, :, g, :]) * scale
+            dk_rot[b, :, g, :] += (ds.T @ q_rot[b, :, h, :]) * scale
+    dq = apply_rope(dq_rot, -pos, rope_theta)
+    dk = apply_rope(dk_rot, -pos, rope_theta)
+    return dq, dk, dv

@@ -20,7 +20,11 @@ What each pin rests on:
   * other page form  -- the llama3 page's adjacent-pair complex rotation equals the
                         half-split rotation after a fixed permutation of head_dim;
   * lse meaning      -- two disjoint key sets merged by logaddexp reproduce the full result;
-  * golden fixtures  -- hand-derived closed-form cases in tests/golden/.
+  * golden fixtures  -- hand-derived closed-form cases in tests/golden/;
+  * backward         -- central finite differences of the forward oracle (sum of dout * out)
+                        on tiny shapes; the value gradient sums to the output gradient over
+                        keys (softmax rows sum to 1); row 0 of dq is exactly 0 under the causal
+                        mask (one visible key, so the softmax has nothing to trade off).
 """
 
 import json
@@ -397,6 +401,63 @@ def pin_golden():
         _close(lse, np.array(c["lse"]), 1e-14, f"golden {c['name']} lse")
 
 
+BACKWARD_FD_CASES = [
+    # B, S, Hq, Hkv, d, causal, rope_theta, seed
+    (1, 5, 2, 1, 4, True, 100.0, 1),
+    (2, 4, 2, 2, 6, False, 10.0, 2),
+    (1, 6, 3, 1, 8, True, 10000.0, 3),
+    (1, 3, 4, 2, 2, True, 3.0, 4),
+]
+
+
+def pin_backward_finite_differences():
+    """dq, dk, dv against central differences of L = sum(dout * out) through the forward."""
+    h = 1e-6
+    for B, S, Hq, Hkv, d, causal, theta, seed in BACKWARD_FD_CASES:
+        rng = np.random.default_rng(seed)
+        q, k, v = _rand(rng, B, S, Hq, d), _rand(rng, B, S, Hkv, d), _rand(rng, B, S, Hkv, d)
+        do = _rand(rng, B, S, Hq, d)
+        grads = dict(zip("qkv", O.attention_backward(q, k, v, do, theta, causal)))
+        x = {"q": q, "k": k, "v": v}
+        for name in "qkv":
+            num = np.zeros_like(x[name])
+            for idx in np.ndindex(x[name].shape):
+                args = dict(x)
+                xp = x[name].copy()
+                xp[idx] += h
+                args[name] = xp
+                lp = (O.attention(args["q"], args["k"], args["v"], theta, causal)[0] * do).sum()
+                xm = x[name].copy()
+                xm[idx] -= h
+                args[name] = xm
+                lm = (O.attention(args["q"], args["k"], args["v"], theta, causal)[0] * do).sum()
+                num[idx] = (lp - lm) / (2 * h)
+            _close(grads[name], num, 1e-7, f"d{name} vs finite differences, case seed {seed}")
+
+
+def pin_backward_dv_sums_to_dout():
+    """sum over keys of dv[:, :, g] = sum over the group's query heads and rows of dout."""
+    rng = np.random.default_rng(31)
+    B, S, Hq, Hkv, d = 2, 40, 6, 2, 16
+    q, k, v = _rand(rng, B, S, Hq, d), _rand(rng, B, S, Hkv, d), _rand(rng, B, S, Hkv, d)
+    do = _rand(rng, B, S, Hq, d)
+    for causal in (True, False):
+        _, _, dv = O.attention_backward(q, k, v, do, 500.0, causal)
+        want = do.reshape(B, S, Hkv, Hq // Hkv, d).sum(axis=(1, 3))
+        _close(dv.sum(axis=1), want, 1e-10, f"dv column sums, causal {causal}")
+
+
+def pin_backward_row0_dq_zero():
+    """Causal row 0 attends to key 0 alone: its softmax weight is 1 whatever the score, so
+    dq[:, 0] is exactly 0 (up to rounding), while later rows are not."""
+    rng = np.random.default_rng(32)
+    q, k, v = _rand(rng, 1, 12, 4, 8), _rand(rng, 1, 12, 2, 8), _rand(rng, 1, 12, 2, 8)
+    do = _rand(rng, 1, 12, 4, 8)
+    dq, _, _ = O.attention_backward(q, k, v, do, 10000.0, True)
+    assert np.abs(dq[:, 0]).max() < 1e-12, "causal dq row 0 must vanish"
+    assert np.abs(dq[:, 1:]).max() > 1e-3, "later dq rows must not vanish"
+
+
 ALL_PINS = [
     pin_bruteforce,
     pin_rows_sum_to_one,
@@ -418,5 +479,8 @@ ALL_PINS = [
     pin_shard_shift_invariance,
     pin_ring_split,
     pin_empty_rows,
+    pin_backward_finite_differences,
+    pin_backward_dv_sums_to_dout,
+    pin_backward_row0_dq_zero,
     pin_golden,
 ]

@@ -161,6 +161,38 @@ def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, 
     return attention
 
 
+def _backward_variant(*, drop_rowsum=False, rope_forward_sign=False, no_scale=False, ds_untransposed=False,
+                      dv_untransposed=False, rowsum_of_dp=False):
+    def attention_backward(q, k, v, dout, rope_theta, causal=True):
+        q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+        B, S, Hq, d = q.shape
+        Hkv = k.shape[2]
+        pos = np.arange(S)
+        q_rot, k_rot = O.apply_rope(q, pos, rope_theta), O.apply_rope(k, pos, rope_theta)
+        scale = 1.0 if no_scale else 1.0 / np.sqrt(np.float64(d))
+        dq_rot, dk_rot, dv = np.zeros_like(q_rot), np.zeros_like(k_rot), np.zeros_like(v)
+        for b in range(B):
+            for h in range(Hq):
+                g = O.kv_head_of(h, Hq, Hkv)
+                P, _, _ = O.attention_weights(q_rot[b, :, h], k_rot[b, :, g], pos, causal)
+                o = P @ v[b, :, g]
+                do = dout[b, :, h]
+                dv[b, :, g] += (P if dv_untransposed else P.T) @ do
+                dP = do @ v[b, :, g].T
+                if drop_rowsum:
+                    ds = P * dP
+                elif rowsum_of_dp:
+                    ds = P * (dP - dP.sum(axis=-1, keepdims=True))
+                else:
+                    ds = P * (dP - (do * o).sum(axis=-1, keepdims=True))
+                dq_rot[b, :, h] = (ds @ k_rot[b, :, g]) * scale
+                dk_rot[b, :, g] += ((ds if ds_untransposed else ds.T) @ q_rot[b, :, h]) * scale
+        back = pos if rope_forward_sign else -pos
+        return O.apply_rope(dq_rot, back, rope_theta), O.apply_rope(dk_rot, back, rope_theta), dv
+
+    return attention_backward
+
+
 MUTATIONS = {
     "rotate_half_wrong_sign": ("rotate_half", _rotate_half_wrong_sign),
     "rotate_half_swapped_halves": ("rotate_half", _rotate_half_swapped_halves),
@@ -188,6 +220,12 @@ MUTATIONS = {
     "q_rotation_ignores_offset": ("attention", _attention_variant(q_rope_no_offset=True)),
     "merge_weights_swapped": ("merge", _merge_weights_swapped),
     "merge_plain_average": ("merge", _merge_plain_average),
+    "backward_drops_rowsum": ("attention_backward", _backward_variant(drop_rowsum=True)),
+    "backward_rowsum_of_dp": ("attention_backward", _backward_variant(rowsum_of_dp=True)),
+    "backward_rope_not_inverted": ("attention_backward", _backward_variant(rope_forward_sign=True)),
+    "backward_scale_dropped": ("attention_backward", _backward_variant(no_scale=True)),
+    "backward_dk_untransposed": ("attention_backward", _backward_variant(ds_untransposed=True)),
+    "backward_dv_untransposed": ("attention_backward", _backward_variant(dv_untransposed=True)),
 }
 
 
