@@ -1,7 +1,7 @@
 """Benchmark of the fused causal RoPE-GQA attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline]
-    python bench.py --ring N | --decode [--batch B]   (shard composition / decode step)
+    python bench.py --ring N | --decode [--batch B] | --backward   (shard composition / decode / backward)
 
 A step is one attn_fwd call (key-rotation pre-pass + fused attention kernel) over the whole
 workload, inputs already resident in HBM.  Prints one JSON line:
@@ -289,6 +289,72 @@ def decode_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def backward_bench(args):
+    """Backward steps: attn_bwd (layout passes + dk/dv kernel + dq kernel) over the workload,
+    from one forward's out and lse, with a seeded output gradient.  FLOPs are the usual
+    2.5x the forward's (S recomputed, dP, dV, dK, dQ: five products of the forward's size);
+    the kernels execute seven, recomputing S and dP in the dq kernel rather than using atomics."""
+    import torch
+
+    from transformer_causal_attention_amd import attn_bwd, attn_fwd, bwd_workspace_bytes
+    from transformer_causal_attention_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("the backward is bf16 only")
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    g = torch.Generator(device=dev).manual_seed(int(w.seed) + 1000)
+    dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+    out, lse = attn_fwd(q, k, v, w.rope_theta, w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(bwd_workspace_bytes(w.B, w.S, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+
+    def step():
+        attn_bwd(q, k, v, out, lse, dout, w.rope_theta, w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / args.steps
+    fl = 2.5 * flops(w)
+    value = fl / (ms_per_step * 1e-3) / 1e12
+    achieved = fl / (call_ms * 1e-3) / 1e12
+    res = {
+        "metric": "causal RoPE-GQA attention backward TFLOP/s (2.5x forward FLOPs)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, sigma) q/k/v and output gradient)",
+        "config": {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
+                               f"rope_theta={w.rope_theta:g} causal={w.causal}",
+                   "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bwd (bwd_prep_k + bwd_prep_q + bwd_dkdv + bwd_dq)",
+                     "kernel_ms": round(call_ms, 5)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +370,7 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time decode steps (one query per head at position S - 1 over a full KV cache)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size (--decode)")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (attn_bwd)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention forward is a single-GPU kernel here "
@@ -318,6 +385,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import torch

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Element types of q, k, v and out. */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
@@ -183,6 +183,31 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim);
 int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
                 double rope_theta, int q_pos, void *out, float *lse, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * Backward pass: the gradients dq, dk, dv of attn_fwd's out for a given output gradient dout
+ * (the pages train these models -- PaLM-in-ColossalAI page, section 2.7, a cross-entropy
+ * training loss -- and a training step needs them).  With P = softmax of the scaled, masked
+ * scores of the rotated q and k, recomputed from the saved lse:
+ *   dv = P^T dout (summed over the query heads sharing a K/V head),
+ *   ds = P * (dout v^T - rowsum(dout * out)),
+ *   dq = R^T (ds k' / sqrt(d)),  dk = R^T (ds^T q' / sqrt(d)) (summed like dv),
+ * R the rotary rotation at each row's position.  The gradient of lse is taken as zero.
+ *
+ *   q, dout        device, (B, S, Hq, head_dim) bfloat16 contiguous, 16-byte aligned
+ *   k, v           device, (B, S, Hkv, head_dim) bfloat16, 16-byte aligned
+ *   out, lse       attn_fwd's outputs for the same q, k, v, rope_theta and causal
+ *   dq; dk, dv     device, shaped like q; like k (written), 16-byte aligned
+ *   workspace      device, >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned (the
+ *                  re-laid-out operands), caller owned
+ * bf16 only; head_dim 64 or 128.  Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED,
+ * ATTN_EWORKSPACE or ATTN_EHIP with the meanings given for attn_fwd.
+ */
+size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim);
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+             const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
+             int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+             void *stream);
 
 /* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */
 void *attn_event_create(void);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert _lib.abi_version() == 3
+    assert _lib.abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert len(_lib.strerror(code)) > 5
     assert "unknown" in _lib.strerror(12345)
@@ -198,3 +198,33 @@ def decode_call(**over):
 ])
 def test_decode_rejections(over, code):
     assert decode_call(**over) == code
+
+
+def test_bwd_workspace_bytes():
+    # 3 key-side and 4 query-side tiles of 32 rows x d bf16 per block, 2 floats per query row
+    nb = (100 + 31) // 32
+    assert _lib.bwd_workspace_bytes(2, 100, 8, 2, 128) == (3 * 2 * 2 + 4 * 2 * 8) * nb * 32 * 128 * 2 + 2 * 2 * 8 * nb * 32 * 4
+    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 64) == (3 + 4 * 4) * 2 * 32 * 64 * 2 + 2 * 4 * 2 * 32 * 4
+    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 96) == 0
+    assert _lib.bwd_workspace_bytes(1, 64, 6, 4, 64) == 0
+
+
+def bwd_call(**over):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, dout=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=1e4, causal=1, dq=P, dk=P,
+             dv=P, ws=P, wsb=1 << 30, stream=None)
+    a.update(over)
+    return _lib.bwd_raw(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["B"], a["S"], a["Hq"], a["Hkv"],
+                        a["d"], a["theta"], a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), _lib.ATTN_EINVAL), (dict(out=None), _lib.ATTN_EINVAL), (dict(lse=None), _lib.ATTN_EINVAL),
+    (dict(dout=None), _lib.ATTN_EINVAL), (dict(dq=None), _lib.ATTN_EINVAL), (dict(dv=None), _lib.ATTN_EINVAL),
+    (dict(k=P + 8), _lib.ATTN_EINVAL), (dict(dout=P + 2), _lib.ATTN_EINVAL), (dict(dk=P + 4), _lib.ATTN_EINVAL),
+    (dict(lse=P + 2), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(S=-4), _lib.ATTN_EINVAL),
+    (dict(Hq=3, Hkv=2), _lib.ATTN_EINVAL), (dict(causal=2), _lib.ATTN_EINVAL), (dict(theta=float("inf")), _lib.ATTN_EINVAL),
+    (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1), _lib.ATTN_EUNSUPPORTED),
+    (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=100), _lib.ATTN_EWORKSPACE), (dict(ws=P + 8), _lib.ATTN_EWORKSPACE),
+])
+def test_bwd_rejections(over, code):
+    assert bwd_call(**over) == code

@@ -19,6 +19,10 @@ attn_merge joins two such partial results.
 is the decode step: one query per (batch row, head) at position q_pos over the cached keys
 0 .. q_pos (bf16); kv_prepare rotates and stores keys as they are appended.
 
+    dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True)
+
+is the backward pass (bf16), from the forward's out and lse.
+
 PyTorch only provides device memory and the stream; the computation runs in the HIP
 kernels behind the C ABI of libattn.so (include/attn.h).
 """
@@ -31,10 +35,12 @@ from ._lib import (  # noqa: F401
     abi_version,
     load,
     strerror,
+    bwd_workspace_bytes,
     decode_workspace_bytes,
     workspace_bytes,
 )
 from .api import (  # noqa: F401
+    attn_bwd,
     attn_decode,
     attn_fwd,
     attn_fwd_into,

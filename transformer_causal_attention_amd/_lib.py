@@ -25,6 +25,8 @@ _FWD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _V
 _SHARD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 _MERGE_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]
 _PREP_ARGS = [_VP, _VP, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, ctypes.c_size_t, _VP]
+_BWD_ARGS = [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _VP, _VP, _VP, _VP,
+             ctypes.c_size_t, _VP]
 _DECODE_ARGS = [_VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 SIGNATURES = {
     "attn_abi_version": (_I, []),
@@ -37,6 +39,8 @@ SIGNATURES = {
     "attn_kv_prepare": (_I, _PREP_ARGS),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_decode": (_I, _DECODE_ARGS),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, _BWD_ARGS),
     "attn_event_create": (_VP, []),
     "attn_event_destroy": (_I, [_VP]),
     "attn_event_elapsed_ms": (_I, [_VP, _VP, ctypes.POINTER(ctypes.c_float)]),
@@ -118,6 +122,17 @@ def decode_raw(q, cache, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, out, ls
     """Call attn_decode with raw pointers; returns the code."""
     return load().attn_decode(q, cache, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(q_pos), out, lse,
                               workspace, workspace_bytes_, stream)
+
+
+def bwd_workspace_bytes(B, S, Hq, Hkv, head_dim):
+    return load().attn_bwd_workspace_bytes(B, S, Hq, Hkv, head_dim)
+
+
+def bwd_raw(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, rope_theta, causal, dq, dk, dv, workspace,
+            workspace_bytes_, stream):
+    """Call attn_bwd with raw pointers; returns the code."""
+    return load().attn_bwd(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, float(rope_theta), int(causal), dq, dk,
+                           dv, workspace, workspace_bytes_, stream)
 
 
 class Event:

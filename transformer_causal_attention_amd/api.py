@@ -175,3 +175,36 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_decode")
     return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd's out for the output gradient dout (bf16).
+
+    out, lse: attn_fwd's results for the same q, k, v, rope_theta and causal.
+    """
+    B, S, Hq, Hkv, D = _shapes(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("attn_bwd takes bfloat16 tensors")
+    for name, t in (("out", out), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
+    if tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, S)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like {name[1:]}")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if workspace is None:
+        workspace = torch.empty(_lib.bwd_workspace_bytes(B, S, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+        if stream is not None:
+            workspace.record_stream(st)
+    rc = _lib.bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                      B, S, Hq, Hkv, D, rope_theta, 1 if causal else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_bwd")
+    return dq, dk, dv

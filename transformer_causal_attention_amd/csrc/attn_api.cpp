@@ -330,6 +330,74 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, 
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+namespace {
+
+constexpr int kBwdRows = 32;  // query and key block of the backward kernels
+
+size_t bwd_blocks(int S) { return ((size_t)S + kBwdRows - 1) / kBwdRows; }
+
+}  // namespace
+
+ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim) {
+  if (check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
+  const size_t nb = bwd_blocks(S);
+  const size_t tile = (size_t)kBwdRows * head_dim * 2;
+  return 3 * (size_t)B * Hkv * nb * tile + 4 * (size_t)B * Hq * nb * tile + 2 * (size_t)B * Hq * nb * kBwdRows * 4;
+}
+
+ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                         const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
+                         int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  for (const void *ptr : {q, k, v, out, dout, (const void *)dq, (const void *)dk, (const void *)dv})
+    if (!aligned(ptr, 16)) return ATTN_EINVAL;
+  if (!aligned(lse, 4)) return ATTN_EINVAL;
+  const int rc = check_shape(B, S, Hq, Hkv, head_dim, rope_theta, causal, ATTN_DTYPE_BF16);
+  if (rc != ATTN_OK) return rc;
+  const size_t nb = bwd_blocks(S);
+  if ((double)B * Hq * nb >= 2147483647.0) return ATTN_EUNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, S, Hq, Hkv, head_dim);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_EWORKSPACE;
+  const int G = Hq / Hkv;
+  const size_t tile = (size_t)kBwdRows * head_dim;  // elements
+  attn::BwdParams p;
+  p.q = static_cast<const __bf16 *>(q);
+  p.k = static_cast<const __bf16 *>(k);
+  p.v = static_cast<const __bf16 *>(v);
+  p.out = static_cast<const __bf16 *>(out);
+  p.dout = static_cast<const __bf16 *>(dout);
+  p.lse = lse;
+  p.dq = static_cast<__bf16 *>(dq);
+  p.dk = static_cast<__bf16 *>(dk);
+  p.dv = static_cast<__bf16 *>(dv);
+  const size_t kt_n = (size_t)B * Hkv * nb * tile, qt_n = (size_t)B * Hq * nb * tile;
+  p.kc = static_cast<__bf16 *>(workspace);
+  p.kt = p.kc + kt_n;
+  p.vc = p.kt + kt_n;
+  p.qc = p.vc + kt_n;
+  p.qt = p.qc + qt_n;
+  p.dc = p.qt + qt_n;
+  p.dt = p.dc + qt_n;
+  p.l2 = reinterpret_cast<float *>(p.dt + qt_n);
+  p.dd = p.l2 + (size_t)B * Hq * nb * kBwdRows;
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = G;
+  p.NB = (int)nb;
+  p.n_pairs = (int)((nb + 1) / 2);
+  p.W = std::min(G, 4);
+  p.causal = causal;
+  p.scale_log2 = q_scale(head_dim);
+  p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)head_dim));
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = head_dim == 64 ? attn::launch_bwd<64>(p, tab, st) : attn::launch_bwd<128>(p, tab, st);
+  return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
 ATTN_EXPORT int attn_event_destroy(void *ev) {
   if (!ev) return ATTN_EINVAL;
   return hipEventDestroy(static_cast<hipEvent_t>(ev)) == hipSuccess ? ATTN_OK : ATTN_EHIP;

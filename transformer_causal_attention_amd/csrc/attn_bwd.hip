@@ -1,0 +1,481 @@
+// Backward pass of the fused causal RoPE-GQA attention for gfx950: dq, dk, dv from q, k, v,
+// the forward's out and lse, and the output gradient dout.
+//
+// The gradient of the forward (Picotron, PaLM and llama3-from-scratch pages define the
+// forward; the PaLM page's wrapper trains it with a cross-entropy loss, section 2.7):
+//   P = exp(s - lse) with s = q'.k'/sqrt(D) (q', k' rotated), recomputed from the saved lse;
+//   dv_g = sum over the group's heads of P^T dout;   dP = dout v^T;
+//   ds = P (dP - rowsum(dout * out));
+//   dq' = ds k' / sqrt(D);   dk'_g = sum over the group's heads of ds^T q' / sqrt(D);
+//   dq = R^T dq', dk = R^T dk' (the rotation by minus the position's angles).
+//
+// Four kernels, 32-row blocks of queries and keys throughout:
+//   bwd_prep_k  rotated keys in "c" and "t" layouts, values in "c" layout, per key block;
+//   bwd_prep_q  rotated queries (scaled) in "c" and "t" layouts, dout in both, and per row
+//               lse * log2(e) and rowsum(dout * out), per query block;
+//   bwd_dkdv    one workgroup per (b, K/V head, pair of key blocks kb, NB-1-kb), one wave per
+//               query head of the group (up to 4, each looping over the rest): for every
+//               query block that sees the key block, S = Q K^T and dP = dO V^T on MFMA with
+//               one key per lane, then dv += P^T dO and dk += dS^T Q; the waves' sums are
+//               added through LDS, dk is rotated back, and both are written once (no atomics);
+//   bwd_dq      one wave per (b, query head, pair of query blocks): S^T = K Q^T and
+//               dP^T = V dO^T with one query per lane, dq += dS K; rotated back and written.
+// Causal work is balanced by pairing block kb with NB-1-kb.  Operands are read straight from
+// the pre-laid-out tiles into registers (16-byte loads, each a whole MFMA operand per lane), so
+// no LDS is needed outside the dk/dv reduction and the layout passes.
+//
+// MFMA v_mfma_f32_32x32x16_bf16: A lane l holds row l%32, k = 8(l/32) .. +7; B lane l holds
+// column l%32, same k; the result's register v in lane l is row 8(v/4) + 4(l/32) + v%4,
+// column l%32.  A score result packed as bf16 (registers 8t .. 8t+7 -> one operand) therefore
+// lists its rows in the order 16t + swap23(8(l/32) + e), which is the row order of the "t"
+// layout.
+
+#include "attn_device.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int BR = 32;  // rows per block
+
+__device__ __forceinline__ f32x16 bwd_mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup i runs on XCD i % 8 (round-robin dispatch).  This renumbers the n workgroups so
+// that each XCD gets a contiguous run of the logical order, i.e. the blocks of the same K/V
+// head group, whose tiles then stay in that XCD's L2.  A bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_order(int i, int n) {
+  const int x = i & 7, q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + (i >> 3);
+}
+
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+__device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// Row of result register v in lane half hh.
+__device__ __forceinline__ int res_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+// Writes a 32-row block staged in LDS (rows of stride LS elements) in "t" layout: 4*D chunks of
+// 16 bytes, chunk (half, j, column) = rows 16 half + swap23(8 j + e), e = 0..7, of that column.
+template <int D, int LS>
+__device__ __forceinline__ void write_t_layout(const uint16_t *lds, __bf16 *dst, int tid, int nthreads) {
+  for (int ch = tid; ch < 4 * D; ch += nthreads) {
+    const int col = ch % D;
+    const int hj = ch / D;  // 2 half + j
+    const int half = hj >> 1, j = hj & 1;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int r0 = 16 * half + swap23(8 * j + e);
+      const int r1 = 16 * half + swap23(8 * j + e + 1);
+      w[e / 2] = (uint32_t)lds[r0 * LS + col] | ((uint32_t)lds[r1 * LS + col] << 16);
+    }
+    *reinterpret_cast<u32x4 *>(dst + (size_t)ch * 8) = w;
+  }
+}
+
+// Rotation of 8 pairs (x_i, y_i) = (dims 8c + i, D/2 + 8c + i) of one row at position pos.
+template <int D>
+__device__ __forceinline__ void rotate8(const RopeTable &tab, int c, int pos, const u32x4 &xr, const u32x4 &yr,
+                                        float x[8], float y[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t xw = xr[i / 2], yw = yr[i / 2];
+    const float xv = (i & 1) ? bf16_hi(xw) : bf16_lo(xw);
+    const float yv = (i & 1) ? bf16_hi(yw) : bf16_lo(yw);
+    const float t = turn_fraction(pos, tab.rev[8 * c + i]);
+    const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+    x[i] = xv * cs - yv * sn;
+    y[i] = yv * cs + xv * sn;
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float a[8], float s) {
+  return u32x4{pack_bf16x2(a[0] * s, a[1] * s), pack_bf16x2(a[2] * s, a[3] * s), pack_bf16x2(a[4] * s, a[5] * s),
+               pack_bf16x2(a[6] * s, a[7] * s)};
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Layout passes.  256 threads; item = row * NCH + c covers dims 8c .. 8c+7 and D/2 + 8c .. of
+// one row (NCH = D/16 pairs of 8-dim chunks).
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NCH = D / 16;
+  constexpr int LS = D + 8;
+  constexpr int T = BR * D;  // elements per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sk[BR * LS];
+  const int tid = threadIdx.x;
+  const int kb = blockIdx.x % p.NB;
+  const int unit = blockIdx.x / p.NB;  // b * Hkv + g
+  const int g = unit % p.Hkv, b = unit / p.Hkv;
+  const size_t tile = (size_t)blockIdx.x * T;
+  if (tid < BR * NCH) {
+    const int row = tid / NCH, c = tid % NCH;
+    const int r = kb * BR + row;
+    u32x4 kx = {0u, 0u, 0u, 0u}, ky = kx, vx = kx, vy = kx;
+    if (r < p.S) {
+      const size_t src = (((size_t)b * p.S + r) * p.Hkv + g) * D + 8 * c;
+      kx = *reinterpret_cast<const u32x4 *>(p.k + src);
+      ky = *reinterpret_cast<const u32x4 *>(p.k + src + D / 2);
+      vx = *reinterpret_cast<const u32x4 *>(p.v + src);
+      vy = *reinterpret_cast<const u32x4 *>(p.v + src + D / 2);
+    }
+    float x[8], y[8];
+    rotate8<D>(tab, c, r, kx, ky, x, y);
+    const u32x4 wx = r < p.S ? pack8(x, 1.f) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 wy = r < p.S ? pack8(y, 1.f) : u32x4{0u, 0u, 0u, 0u};
+    // c layout: chunk c at [c][row][8]
+    *reinterpret_cast<u32x4 *>(p.kc + tile + ((size_t)c * BR + row) * 8) = wx;
+    *reinterpret_cast<u32x4 *>(p.kc + tile + ((size_t)(c + NCH) * BR + row) * 8) = wy;
+    *reinterpret_cast<u32x4 *>(p.vc + tile + ((size_t)c * BR + row) * 8) = vx;
+    *reinterpret_cast<u32x4 *>(p.vc + tile + ((size_t)(c + NCH) * BR + row) * 8) = vy;
+    *reinterpret_cast<u32x4 *>(sk + row * LS + 8 * c) = wx;
+    *reinterpret_cast<u32x4 *>(sk + row * LS + D / 2 + 8 * c) = wy;
+  }
+  __syncthreads();
+  write_t_layout<D, LS>(sk, p.kt + tile, tid, 256);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NCH = D / 16;
+  constexpr int LS = D + 8;
+  constexpr int T = BR * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[BR * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t sd[BR * LS];
+  const int tid = threadIdx.x;
+  const int qb = blockIdx.x % p.NB;
+  const int unit = blockIdx.x / p.NB;  // b * Hq + h
+  const int h = unit % p.Hq, b = unit / p.Hq;
+  const size_t tile = (size_t)blockIdx.x * T;
+  if (tid < BR * NCH) {
+    const int row = tid / NCH, c = tid % NCH;
+    const int r = qb * BR + row;
+    const bool ok = r < p.S;
+    u32x4 qx = {0u, 0u, 0u, 0u}, qy = qx, gx = qx, gy = qx, ox = qx, oy = qx;
+    if (ok) {
+      const size_t src = (((size_t)b * p.S + r) * p.Hq + h) * D + 8 * c;
+      qx = *reinterpret_cast<const u32x4 *>(p.q + src);
+      qy = *reinterpret_cast<const u32x4 *>(p.q + src + D / 2);
+      gx = *reinterpret_cast<const u32x4 *>(p.dout + src);
+      gy = *reinterpret_cast<const u32x4 *>(p.dout + src + D / 2);
+      ox = *reinterpret_cast<const u32x4 *>(p.out + src);
+      oy = *reinterpret_cast<const u32x4 *>(p.out + src + D / 2);
+    }
+    float x[8], y[8];
+    rotate8<D>(tab, c, r, qx, qy, x, y);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(p.qc + tile + ((size_t)c * BR + row) * 8) = ok ? pack8(x, p.scale_log2) : zero;
+    *reinterpret_cast<u32x4 *>(p.qc + tile + ((size_t)(c + NCH) * BR + row) * 8) = ok ? pack8(y, p.scale_log2) : zero;
+    *reinterpret_cast<u32x4 *>(sq + row * LS + 8 * c) = ok ? pack8(x, p.inv_sqrt_d) : zero;
+    *reinterpret_cast<u32x4 *>(sq + row * LS + D / 2 + 8 * c) = ok ? pack8(y, p.inv_sqrt_d) : zero;
+    *reinterpret_cast<u32x4 *>(p.dc + tile + ((size_t)c * BR + row) * 8) = gx;
+    *reinterpret_cast<u32x4 *>(p.dc + tile + ((size_t)(c + NCH) * BR + row) * 8) = gy;
+    *reinterpret_cast<u32x4 *>(sd + row * LS + 8 * c) = gx;
+    *reinterpret_cast<u32x4 *>(sd + row * LS + D / 2 + 8 * c) = gy;
+    // rowsum(dout * out) over this item's 16 dims, then over the NCH items of the row
+    // (consecutive lanes of one wave)
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += bf16_lo(gx[i]) * bf16_lo(ox[i]) + bf16_hi(gx[i]) * bf16_hi(ox[i]);
+      acc += bf16_lo(gy[i]) * bf16_lo(oy[i]) + bf16_hi(gy[i]) * bf16_hi(oy[i]);
+    }
+#pragma unroll
+    for (int off = NCH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0) {
+      const size_t ri = (size_t)unit * p.NB * BR + (size_t)qb * BR + row;
+      p.dd[ri] = ok ? acc : 0.f;
+      p.l2[ri] = ok ? p.lse[((size_t)b * p.Hq + h) * p.S + r] * 1.4426950408889634f : INFINITY;
+    }
+  }
+  __syncthreads();
+  write_t_layout<D, LS>(sq, p.qt + tile, tid, 256);
+  write_t_layout<D, LS>(sd, p.dt + tile, tid, 256);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dk, dv.  Workgroup: (b, g, key-block pair), W waves; wave w takes the group's heads w, w+W, ...
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  constexpr int RED = NCB * 16 * 64;  // floats of one accumulator set of a wave
+  __shared__ float red[3][2][RED];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int blk = xcd_order(blockIdx.x, gridDim.x);
+  const int pair = blk % p.n_pairs;
+  const int unit = blk / p.n_pairs;  // b * Hkv + g
+  const int g = unit % p.Hkv, b = unit / p.Hkv;
+  const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
+
+  for (int side = 0; side < 2; ++side) {
+    const int kb = side == 0 ? pair : p.NB - 1 - pair;
+    if (side == 1 && kb == pair) break;
+    const size_t ktile = ((size_t)unit * p.NB + kb) * T;
+    bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
+      vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+    }
+    const bool key_ok = kb * BR + l32 < p.S;
+    f32x16 dk[NCB], dv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) dk[cb] = dv[cb] = f32x16{};
+
+    for (int hc = wave; hc < p.G; hc += p.W) {
+      const int h = g * p.G + hc;
+      const size_t qunit = (size_t)b * p.Hq + h;
+      // from the last query block down, so that the workgroups of a group sweep the same
+      // query tiles at about the same time
+      for (int qb = p.NB - 1; qb >= (p.causal ? kb : 0); --qb) {
+        const size_t qtile = (qunit * p.NB + qb) * T;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s = bwd_mfma(ld16(p.qc + qtile + c_off + kk * 2 * BR * 8), kf[kk], s);
+          dp = bwd_mfma(ld16(p.dc + qtile + c_off + kk * 2 * BR * 8), vf[kk], dp);
+        }
+        // per-row lse and rowsum for this lane's rows 8c + 4hh + 0..3
+        const float *l2r = p.l2 + (qunit * p.NB + qb) * BR + 4 * hh;
+        const float *ddr = p.dd + (qunit * p.NB + qb) * BR + 4 * hh;
+        f32x4 L[4], Dd[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          L[c] = *reinterpret_cast<const f32x4 *>(l2r + 8 * c);
+          Dd[c] = *reinterpret_cast<const f32x4 *>(ddr + 8 * c);
+        }
+        const bool diag = p.causal && qb == kb;
+        bf16x8 pa[2], sa[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 wp, ws;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float pv[2], sv[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int v = 8 * tt + e + z;
+              float pr = __builtin_amdgcn_exp2f(s[v] - L[v >> 2][v & 3]);
+              if (!key_ok || (diag && l32 > res_row(v, hh))) pr = 0.f;
+              pv[z] = pr;
+              sv[z] = pr * (dp[v] - Dd[v >> 2][v & 3]);
+            }
+            wp[e / 2] = pack_bf16x2(pv[0], pv[1]);
+            ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
+          }
+          pa[tt] = __builtin_bit_cast(bf16x8, wp);
+          sa[tt] = __builtin_bit_cast(bf16x8, ws);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const size_t t_off = qtile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8;
+            dv[cb] = bwd_mfma(pa[tt], ld16(p.dt + t_off), dv[cb]);
+            dk[cb] = bwd_mfma(sa[tt], ld16(p.qt + t_off), dk[cb]);
+          }
+      }
+    }
+
+    // add the waves' sums into wave 0
+    if (wave > 0) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          red[wave - 1][0][(cb * 16 + v) * 64 + lane] = dk[cb][v];
+          red[wave - 1][1][(cb * 16 + v) * 64 + lane] = dv[cb][v];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < p.W; ++w)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            dk[cb][v] += red[w - 1][0][(cb * 16 + v) * 64 + lane];
+            dv[cb][v] += red[w - 1][1][(cb * 16 + v) * 64 + lane];
+          }
+      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block;
+      // dk' -> dk: rotate the pair (column i, i + D/2) back by the key's angle
+#pragma unroll
+      for (int cb = 0; cb < NCB / 2; ++cb) {
+        const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BR + res_row(v, hh);
+          const float t = turn_fraction(key, rev);
+          const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+          const float x = dk[cb][v], y = dk[cb + NCB / 2][v];
+          dk[cb][v] = x * cs + y * sn;
+          dk[cb + NCB / 2][v] = y * cs - x * sn;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * BR + res_row(v, hh);
+        if (key < p.S) {
+          const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D + l32;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            p.dk[dst + 32 * cb] = (__bf16)dk[cb][v];
+            p.dv[dst + 32 * cb] = (__bf16)dv[cb][v];
+          }
+        }
+      }
+    }
+    __syncthreads();  // the reduction slots are reused by the second block
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dq.  One wave per (b, h, query-block pair).
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int blk = xcd_order(blockIdx.x, gridDim.x);
+  const int pair = blk % p.n_pairs;
+  const int qunit = blk / p.n_pairs;  // b * Hq + h
+  const int h = qunit % p.Hq, b = qunit / p.Hq;
+  const int g = h / p.G;
+  const size_t kunit = (size_t)b * p.Hkv + g;
+  const int c_off = hh * BR * 8 + l32 * 8;
+
+  for (int side = 0; side < 2; ++side) {
+    const int qb = side == 0 ? pair : p.NB - 1 - pair;
+    if (side == 1 && qb == pair) break;
+    const size_t qtile = ((size_t)qunit * p.NB + qb) * T;
+    bf16x8 qf[NKK], df[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[kk] = ld16(p.qc + qtile + c_off + kk * 2 * BR * 8);
+      df[kk] = ld16(p.dc + qtile + c_off + kk * 2 * BR * 8);
+    }
+    // this lane's query: row l32 of the block
+    const float Lq = p.l2[((size_t)qunit * p.NB + qb) * BR + l32];
+    const float Dq = p.dd[((size_t)qunit * p.NB + qb) * BR + l32];
+    f32x16 dq[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
+    const int kb_end = p.causal ? qb + 1 : p.NB;
+    // key-block operands, two sets: the next block's are loaded while the current one is used
+    // (the index is clamped, so the last step re-reads its own block instead of branching)
+    bf16x8 ka[2][NKK], va[2][NKK], kt[2][2][NCB];
+    auto load_kv = [&](int kb, int buf) __attribute__((always_inline)) {
+      const size_t ktile = (kunit * p.NB + kb) * T;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        ka[buf][kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
+        va[buf][kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          kt[buf][tt][cb] = ld16(p.kt + ktile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8);
+    };
+    auto step = [&](int kb, int buf) __attribute__((always_inline)) {
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        st = bwd_mfma(ka[buf][kk], qf[kk], st);
+        dpt = bwd_mfma(va[buf][kk], df[kk], dpt);
+      }
+      const bool diag = p.causal && kb == qb;
+      bf16x8 sa[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 ws;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float sv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int v = 8 * tt + e + z;
+            const int key = res_row(v, hh);  // within the block
+            float pr = __builtin_amdgcn_exp2f(st[v] - Lq);
+            if (kb * BR + key >= p.S || (diag && key > l32)) pr = 0.f;
+            sv[z] = pr * (dpt[v] - Dq);
+          }
+          ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
+        }
+        sa[tt] = __builtin_bit_cast(bf16x8, ws);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) dq[cb] = bwd_mfma(sa[tt], kt[buf][tt][cb], dq[cb]);
+    };
+    load_kv(0, 0);
+    for (int kb = 0; kb < kb_end; kb += 2) {
+      load_kv(min(kb + 1, kb_end - 1), 1);
+      step(kb, 0);
+      if (kb + 1 < kb_end) {
+        load_kv(min(kb + 2, kb_end - 1), 0);
+        step(kb + 1, 1);
+      }
+    }
+    // result lane = column 32 cb + l32, register v = query 8(v/4) + 4 hh + v%4 of the block
+#pragma unroll
+    for (int cb = 0; cb < NCB / 2; ++cb) {
+      const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = qb * BR + res_row(v, hh);
+        const float t = turn_fraction(row, rev);
+        const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+        const float x = dq[cb][v] * p.inv_sqrt_d, y = dq[cb + NCB / 2][v] * p.inv_sqrt_d;
+        dq[cb][v] = x * cs + y * sn;
+        dq[cb + NCB / 2][v] = y * cs - x * sn;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = qb * BR + res_row(v, hh);
+      if (row < p.S) {
+        const size_t dst = (((size_t)b * p.S + row) * p.Hq + h) * D + l32;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) p.dq[dst + 32 * cb] = (__bf16)dq[cb][v];
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
+  const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
+  const unsigned qblocks = (unsigned)((long long)p.B * p.Hq * p.NB);
+  hipLaunchKernelGGL(bwd_prep_k_kernel<D>, dim3(kblocks), dim3(256), 0, stream, p, tab);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(qblocks), dim3(256), 0, stream, p, tab);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)((long long)p.B * p.Hkv * p.n_pairs)), dim3(64 * p.W), 0,
+                     stream, p, tab);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((long long)p.B * p.Hq * p.n_pairs)), dim3(64), 0, stream, p,
+                     tab);
+  return hipGetLastError();
+}
+
+template hipError_t launch_bwd<64>(const BwdParams &, const RopeTable &, hipStream_t);
+template hipError_t launch_bwd<128>(const BwdParams &, const RopeTable &, hipStream_t);
+
+}  // namespace attn

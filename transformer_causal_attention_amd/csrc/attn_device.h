@@ -89,6 +89,25 @@ struct DecodeParams {
   float q_scale;
 };
 
+// Backward pass: 32-row blocks of queries and keys, operands pre-laid-out per block.
+//   "c" layout (chunk-major), one 32-row block: [D/8 chunks][32 rows][8 dims]
+//   "t" layout (transposed), one 32-row block: [2 halves][2][D columns][8 rows], where row
+//     16*half + swap23(8*j + e) sits at (half, j, column, e), swap23 exchanging bits 2 and 3
+struct BwdParams {
+  const __bf16 *q, *k, *v;  // (B, S, Hq | Hkv, D)
+  const __bf16 *out, *dout; // (B, S, Hq, D)
+  const float *lse;         // (B, Hq, S)
+  __bf16 *dq, *dk, *dv;     // like q, k, v
+  // workspace, one T = 32*D*2-byte tile per (b, head, block)
+  __bf16 *kc, *kt, *vc;     // (B, Hkv, NB) tiles: rotated keys (c, t), values (c)
+  __bf16 *qc, *qt, *dc, *dt;  // (B, Hq, NB) tiles: rotated q * log2(e)/sqrt(D) (c), rotated
+                              // q / sqrt(D) (t), dout (c, t)
+  float *l2, *dd;           // (B, Hq, NB*32): lse * log2(e) (+inf past S); rowsum(dout * out)
+  int B, S, Hq, Hkv, G, NB, n_pairs, W, causal;
+  float scale_log2;         // log2(e) / sqrt(D)
+  float inv_sqrt_d;         // 1 / sqrt(D)
+};
+
 // Fraction of a turn for position p and frequency f (revolutions per position):
 // p * f is formed in double precision and reduced to [-0.5, 0.5], so the angle stays
 // accurate to ~1e-12 turns even at p = 32767, where a float product would be off by

@@ -24,4 +24,7 @@ hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
 template <int D>
 hipError_t launch_decode(const DecodeParams &p, const RopeTable &tab, hipStream_t stream);
 
+template <int D>
+hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream);
+
 }  // namespace attn
