@@ -37,10 +37,10 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 12447.16, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 6263.14, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 33663.26, "WRITE_SIZE_KiB": 16896.09},
-    "long_shard": {"sources_sha256": "fc9ad29fb7f767a5", "FETCH_SIZE_KiB": 1081772.29, "WRITE_SIZE_KiB": 266240.0},
+    "llama3_8b": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 12448.15, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 6267.14, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 33633.96, "WRITE_SIZE_KiB": 16896.0},
+    "long_shard": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 1110042.23, "WRITE_SIZE_KiB": 266241.76},
 }
 
 
