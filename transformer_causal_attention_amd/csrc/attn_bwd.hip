@@ -9,15 +9,16 @@
 //   dq' = ds k' / sqrt(D);   dk'_g = sum over the group's heads of ds^T q' / sqrt(D);
 //   dq = R^T dq', dk = R^T dk' (the rotation by minus the position's angles).
 //
-// Four kernels, 32-row blocks of queries and keys throughout:
+// Five launches, 32-row blocks of queries and keys throughout:
 //   bwd_prep_k  rotated keys in "c" and "t" layouts, values in "c" layout, per key block;
 //   bwd_prep_q  rotated queries (scaled) in "c" and "t" layouts, dout in both, and per row
 //               lse * log2(e) and rowsum(dout * out), per query block;
-//   bwd_dkdv    one workgroup per (b, K/V head, pair of key blocks kb, NB-1-kb), one wave per
-//               query head of the group (up to 4, each looping over the rest): for every
-//               query block that sees the key block, S = Q K^T and dP = dO V^T on MFMA with
-//               one key per lane, then dv += P^T dO and dk += dS^T Q; the waves' sums are
-//               added through LDS, dk is rotated back, and both are written once (no atomics);
+//   bwd_dkdv    twice, for dv and for dk: one workgroup per (b, K/V head, pair of key blocks
+//               kb, NB-1-kb), one wave per query head of the group (up to 4, each looping over
+//               the rest): for every query block that sees the key block, S = Q K^T (and
+//               dP = dO V^T) on MFMA with one key per lane, then dv += P^T dO or
+//               dk += dS^T Q; the waves' sums are added through LDS, dk is rotated back, and
+//               each row is written once (no atomics);
 //   bwd_dq      one wave per (b, query head, pair of query blocks): S^T = K Q^T and
 //               dP^T = V dO^T with one query per lane, dq += dS K; rotated back and written.
 // Causal work is balanced by pairing block kb with NB-1-kb.  Operands are read straight from
@@ -200,15 +201,18 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dk, dv.  Workgroup: (b, g, key-block pair), W waves; wave w takes the group's heads w, w+W, ...
+// dv (DV) or dk (!DV).  Workgroup: (b, g, key-block pair), W waves; wave w takes the group's
+// heads w, w+W, ...  The two gradients are separate kernels so that each holds one set of
+// accumulators and has the registers to load the next query block's operands while it uses the
+// current ones; the dv kernel needs neither dP nor dout in "c" layout.
 
-template <int D>
+template <int D, bool DV>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
   constexpr int RED = NCB * 16 * 64;  // floats of one accumulator set of a wave
-  __shared__ float red[3][2][RED];
+  __shared__ float red[3][RED];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -226,65 +230,82 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable ta
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
-      vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+      if (!DV) vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
     }
     const bool key_ok = kb * BR + l32 < p.S;
-    f32x16 dk[NCB], dv[NCB];
+    f32x16 acc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) dk[cb] = dv[cb] = f32x16{};
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
 
+    // query-block operands, two sets (see the dq kernel)
+    bf16x8 qa[2][NKK], da[2][NKK], tb[2][2][NCB];
+    f32x4 L[2][4], Dd[2][4];
+    const int qb_lo = p.causal ? kb : 0;
     for (int hc = wave; hc < p.G; hc += p.W) {
-      const int h = g * p.G + hc;
-      const size_t qunit = (size_t)b * p.Hq + h;
-      // from the last query block down, so that the workgroups of a group sweep the same
-      // query tiles at about the same time
-      for (int qb = p.NB - 1; qb >= (p.causal ? kb : 0); --qb) {
+      const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
+      auto load_q = [&](int qb, int buf) __attribute__((always_inline)) {
         const size_t qtile = (qunit * p.NB + qb) * T;
-        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s = bwd_mfma(ld16(p.qc + qtile + c_off + kk * 2 * BR * 8), kf[kk], s);
-          dp = bwd_mfma(ld16(p.dc + qtile + c_off + kk * 2 * BR * 8), vf[kk], dp);
+          qa[buf][kk] = ld16(p.qc + qtile + c_off + kk * 2 * BR * 8);
+          if (!DV) da[buf][kk] = ld16(p.dc + qtile + c_off + kk * 2 * BR * 8);
         }
         // per-row lse and rowsum for this lane's rows 8c + 4hh + 0..3
-        const float *l2r = p.l2 + (qunit * p.NB + qb) * BR + 4 * hh;
-        const float *ddr = p.dd + (qunit * p.NB + qb) * BR + 4 * hh;
-        f32x4 L[4], Dd[4];
+        const size_t r0 = (qunit * p.NB + qb) * BR + 4 * hh;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          L[c] = *reinterpret_cast<const f32x4 *>(l2r + 8 * c);
-          Dd[c] = *reinterpret_cast<const f32x4 *>(ddr + 8 * c);
+          L[buf][c] = *reinterpret_cast<const f32x4 *>(p.l2 + r0 + 8 * c);
+          if (!DV) Dd[buf][c] = *reinterpret_cast<const f32x4 *>(p.dd + r0 + 8 * c);
         }
-        const bool diag = p.causal && qb == kb;
-        bf16x8 pa[2], sa[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          u32x4 wp, ws;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float pv[2], sv[2];
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-              const int v = 8 * tt + e + z;
-              float pr = __builtin_amdgcn_exp2f(s[v] - L[v >> 2][v & 3]);
-              if (!key_ok || (diag && l32 > res_row(v, hh))) pr = 0.f;
-              pv[z] = pr;
-              sv[z] = pr * (dp[v] - Dd[v >> 2][v & 3]);
-            }
-            wp[e / 2] = pack_bf16x2(pv[0], pv[1]);
-            ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
-          }
-          pa[tt] = __builtin_bit_cast(bf16x8, wp);
-          sa[tt] = __builtin_bit_cast(bf16x8, ws);
-        }
+        const __bf16 *tsrc = DV ? p.dt : p.qt;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const size_t t_off = qtile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8;
-            dv[cb] = bwd_mfma(pa[tt], ld16(p.dt + t_off), dv[cb]);
-            dk[cb] = bwd_mfma(sa[tt], ld16(p.qt + t_off), dk[cb]);
+          for (int cb = 0; cb < NCB; ++cb)
+            tb[buf][tt][cb] = ld16(tsrc + qtile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8);
+      };
+      auto step = [&](int qb, int buf) __attribute__((always_inline)) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s = bwd_mfma(qa[buf][kk], kf[kk], s);
+          if (!DV) dp = bwd_mfma(da[buf][kk], vf[kk], dp);
+        }
+        const bool diag = p.causal && qb == kb;
+        bf16x8 op[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 wv;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float x[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int v = 8 * tt + e + z;
+              float pr = __builtin_amdgcn_exp2f(s[v] - L[buf][v >> 2][v & 3]);
+              if (!key_ok || (diag && l32 > res_row(v, hh))) pr = 0.f;
+              x[z] = DV ? pr : pr * (dp[v] - Dd[buf][v >> 2][v & 3]);
+            }
+            wv[e / 2] = pack_bf16x2(x[0], x[1]);
           }
+          op[tt] = __builtin_bit_cast(bf16x8, wv);
+        }
+        // dv += P^T dO, dk += dS^T (q'/sqrt(D))
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) acc[cb] = bwd_mfma(op[tt], tb[buf][tt][cb], acc[cb]);
+      };
+      // from the last query block down, so that the workgroups of a group sweep the same
+      // query tiles at about the same time; the clamped index re-reads the last block
+      load_q(p.NB - 1, 0);
+      for (int qb = p.NB - 1; qb >= qb_lo; qb -= 2) {
+        load_q(max(qb - 1, qb_lo), 1);
+        step(qb, 0);
+        if (qb - 1 >= qb_lo) {
+          load_q(max(qb - 2, qb_lo), 0);
+          step(qb - 1, 1);
+        }
       }
     }
 
@@ -293,10 +314,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable ta
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          red[wave - 1][0][(cb * 16 + v) * 64 + lane] = dk[cb][v];
-          red[wave - 1][1][(cb * 16 + v) * 64 + lane] = dv[cb][v];
-        }
+        for (int v = 0; v < 16; ++v) red[wave - 1][(cb * 16 + v) * 64 + lane] = acc[cb][v];
     }
     __syncthreads();
     if (wave == 0) {
@@ -304,35 +322,32 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable ta
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            dk[cb][v] += red[w - 1][0][(cb * 16 + v) * 64 + lane];
-            dv[cb][v] += red[w - 1][1][(cb * 16 + v) * 64 + lane];
-          }
+          for (int v = 0; v < 16; ++v) acc[cb][v] += red[w - 1][(cb * 16 + v) * 64 + lane];
       // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block;
       // dk' -> dk: rotate the pair (column i, i + D/2) back by the key's angle
+      if (!DV) {
 #pragma unroll
-      for (int cb = 0; cb < NCB / 2; ++cb) {
-        const double rev = tab.rev[32 * cb + l32];
+        for (int cb = 0; cb < NCB / 2; ++cb) {
+          const double rev = tab.rev[32 * cb + l32];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * BR + res_row(v, hh);
-          const float t = turn_fraction(key, rev);
-          const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
-          const float x = dk[cb][v], y = dk[cb + NCB / 2][v];
-          dk[cb][v] = x * cs + y * sn;
-          dk[cb + NCB / 2][v] = y * cs - x * sn;
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb * BR + res_row(v, hh);
+            const float t = turn_fraction(key, rev);
+            const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+            const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
+            acc[cb][v] = x * cs + y * sn;
+            acc[cb + NCB / 2][v] = y * cs - x * sn;
+          }
         }
       }
+      __bf16 *dst0 = DV ? p.dv : p.dk;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kb * BR + res_row(v, hh);
         if (key < p.S) {
           const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D + l32;
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            p.dk[dst + 32 * cb] = (__bf16)dk[cb][v];
-            p.dv[dst + 32 * cb] = (__bf16)dv[cb][v];
-          }
+          for (int cb = 0; cb < NCB; ++cb) dst0[dst + 32 * cb] = (__bf16)acc[cb][v];
         }
       }
     }
@@ -467,8 +482,10 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(qblocks), dim3(256), 0, stream, p, tab);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)((long long)p.B * p.Hkv * p.n_pairs)), dim3(64 * p.W), 0,
-                     stream, p, tab);
+  const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.n_pairs));
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((long long)p.B * p.Hq * p.n_pairs)), dim3(64), 0, stream, p,
                      tab);
