@@ -2,6 +2,7 @@
 
 from .attn_oracle import (  # noqa: F401
     apply_rope,
+    apply_rope_interleaved,
     attention,
     attention_backward,
     merge,

@@ -29,9 +29,9 @@ Sources (the pages this oracle follows):
     for n_heads=32: every 4 query heads share one K/V head).
 
 Readings where the pages are silent or disagree (each also listed in the design notes):
-  * RoPE pairing: half-split (Picotron and PaLM pages); the llama3 page's adjacent-pair
-    complex form is the same rotation under a fixed permutation of head_dim and is used
-    only as a cross-check in the tests.
+  * RoPE pairing: half-split (Picotron and PaLM pages) by default; with interleaved=True the
+    llama3 page's adjacent pairs (2i, 2i+1), which it rotates as complex numbers.  The two are
+    the same rotation under a fixed permutation of head_dim.
   * Positions are 0..S-1 for every batch row, unless a sequence shard passes its first
     query and key positions (q_pos0, k_pos0): queries then sit at q_pos0 + i and keys at
     k_pos0 + j, for the rotation and for the mask alike.  A query with no visible key has
@@ -52,6 +52,7 @@ __all__ = [
     "rope_angles",
     "rotate_half",
     "apply_rope",
+    "apply_rope_interleaved",
     "causal_mask",
     "softmax_rows",
     "kv_head_of",
@@ -105,6 +106,25 @@ def apply_rope(x, positions, rope_theta):
     return x * cos + rotate_half(x) * sin
 
 
+def apply_rope_interleaved(x, positions, rope_theta):
+    """Rotate adjacent pairs (x_2i, x_2i+1) of x (B, len(positions), H, head_dim) by position x
+    theta_i: x_2i' = x_2i cos - x_2i+1 sin, x_2i+1' = x_2i+1 cos + x_2i sin.
+
+    llama3 page, "parallel rotation of queries and keys": the vector is split into adjacent
+    pairs, each read as a complex number and multiplied by a unit complex number of angle
+    position x theta_i, theta_i = rope_theta ** (-2i / head_dim) as for the half-split form.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.outer(np.asarray(positions, dtype=np.float64), rope_frequencies(x.shape[-1], rope_theta))
+    cos = np.cos(ang)[None, :, None, :]
+    sin = np.sin(ang)[None, :, None, :]
+    ev, od = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = ev * cos - od * sin
+    out[..., 1::2] = od * cos + ev * sin
+    return out
+
+
 def causal_mask(query_positions, n_keys, key_pos0=0):
     """Additive mask (len(query_positions), n_keys): 0 where the key's position is at most the
     query's, -inf where it is later.  Key j sits at position key_pos0 + j.
@@ -156,7 +176,7 @@ def attention_weights(q_rot, k_rot, query_positions, causal, key_pos0=0):
     return softmax_rows(scores)
 
 
-def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
+def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0, interleaved=False):
     """Causal (or full) RoPE attention with shared K/V heads, in float64.
 
     q: (B, S, Hq, d); k, v: (B, S, Hkv, d); Hq a multiple of Hkv; d even.
@@ -165,6 +185,7 @@ def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
     restricted to those rows.
     q_pos0, k_pos0: positions of query row 0 and key row 0 (a sequence shard's offsets; the
     Picotron page's ring attention passes K/V blocks of other positions around the ranks).
+    interleaved: rotate adjacent pairs (llama3 page) instead of the two halves.
 
     Returns (out, lse): out (B, R, Hq, d) float64 and lse (B, Hq, R) float64, R = len(rows).
     """
@@ -180,8 +201,9 @@ def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
 
     q_positions = q_pos0 + rows
-    q_rot = apply_rope(q[:, rows], q_positions, rope_theta)
-    k_rot = apply_rope(k, k_pos0 + np.arange(S), rope_theta)
+    rope = apply_rope_interleaved if interleaved else apply_rope
+    q_rot = rope(q[:, rows], q_positions, rope_theta)
+    k_rot = rope(k, k_pos0 + np.arange(S), rope_theta)
 
     out = np.empty((B, len(rows), Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, len(rows)), dtype=np.float64)
@@ -216,7 +238,7 @@ def merge(o1, lse1, o2, lse2):
     return out, lse
 
 
-def attention_backward(q, k, v, dout, rope_theta, causal=True):
+def attention_backward(q, k, v, dout, rope_theta, causal=True, interleaved=False):
     """Gradients (dq, dk, dv) of the attention above for an output gradient dout, in float64.
 
     q, dout: (B, S, Hq, d); k, v: (B, S, Hkv, d).  Differentiating the forward's steps in
@@ -227,6 +249,7 @@ def attention_backward(q, k, v, dout, rope_theta, causal=True):
       x' = R(position) x        ->  dx = R(position)^T dx' = R(-position) dx'
     (masked scores have P = 0 and so no gradient; a K/V head's gradient sums over the query
     heads that share it).
+    interleaved: the adjacent-pair rotation, as in attention().
     Returns dq (B, S, Hq, d), dk and dv (B, S, Hkv, d).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -238,8 +261,9 @@ def attention_backward(q, k, v, dout, rope_theta, causal=True):
     if k.shape != (B, S, Hkv, d) or v.shape != k.shape or dout.shape != q.shape:
         raise ValueError("k, v must be (B, S, Hkv, d) and dout like q")
     pos = np.arange(S)
-    q_rot = apply_rope(q, pos, rope_theta)
-    k_rot = apply_rope(k, pos, rope_theta)
+    rope = apply_rope_interleaved if interleaved else apply_rope
+    q_rot = rope(q, pos, rope_theta)
+    k_rot = rope(k, pos, rope_theta)
     scale = 1.0 / np.sqrt(np.float64(d))
 
     dq_rot = np.zeros_like(q_rot)
@@ -256,6 +280,6 @@ def attention_backward(q, k, v, dout, rope_theta, causal=True):
             ds = P * (dP - (do * o).sum(axis=-1, keepdims=True))
             dq_rot[b, :, h, :] = (ds @ k_rot[b, :, g, :]) * scale
             dk_rot[b, :, g, :] += (ds.T @ q_rot[b, :, h, :]) * scale
-    dq = apply_rope(dq_rot, -pos, rope_theta)
-    dk = apply_rope(dk_rot, -pos, rope_theta)
+    dq = rope(dq_rot, -pos, rope_theta)
+    dk = rope(dk_rot, -pos, rope_theta)
     return dq, dk, dv

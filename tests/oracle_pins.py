@@ -311,6 +311,12 @@ def pin_interleaved_equivalence():
                "interleaved complex form vs permuted half-split (out)")
         _close(lse_h[0, h], (m[:, 0] + np.log(e.sum(-1))), 1e-12,
                "interleaved complex form vs permuted half-split (lse)")
+    # the oracle's own interleaved path: its rotation is the complex form, and its attention
+    # equals the permuted half-split one
+    _close(O.apply_rope_interleaved(q, pos, theta), qi, 1e-12, "apply_rope_interleaved vs complex form")
+    out_i, lse_i = O.attention(q, k, v, theta, causal=True, interleaved=True)
+    _close(out_i, out_h, 1e-12, "interleaved attention vs permuted half-split (out)")
+    _close(lse_i, lse_h, 1e-12, "interleaved attention vs permuted half-split (lse)")
 
 
 # ---------------------------------------------------------------- lse meaning
@@ -402,22 +408,23 @@ def pin_golden():
 
 
 BACKWARD_FD_CASES = [
-    # B, S, Hq, Hkv, d, causal, rope_theta, seed
-    (1, 5, 2, 1, 4, True, 100.0, 1),
-    (2, 4, 2, 2, 6, False, 10.0, 2),
-    (1, 6, 3, 1, 8, True, 10000.0, 3),
-    (1, 3, 4, 2, 2, True, 3.0, 4),
+    # B, S, Hq, Hkv, d, causal, rope_theta, seed, interleaved
+    (1, 5, 2, 1, 4, True, 100.0, 1, False),
+    (2, 4, 2, 2, 6, False, 10.0, 2, False),
+    (1, 6, 3, 1, 8, True, 10000.0, 3, False),
+    (1, 3, 4, 2, 2, True, 3.0, 4, False),
+    (1, 5, 2, 1, 6, True, 20.0, 5, True),
 ]
 
 
 def pin_backward_finite_differences():
     """dq, dk, dv against central differences of L = sum(dout * out) through the forward."""
     h = 1e-6
-    for B, S, Hq, Hkv, d, causal, theta, seed in BACKWARD_FD_CASES:
+    for B, S, Hq, Hkv, d, causal, theta, seed, il in BACKWARD_FD_CASES:
         rng = np.random.default_rng(seed)
         q, k, v = _rand(rng, B, S, Hq, d), _rand(rng, B, S, Hkv, d), _rand(rng, B, S, Hkv, d)
         do = _rand(rng, B, S, Hq, d)
-        grads = dict(zip("qkv", O.attention_backward(q, k, v, do, theta, causal)))
+        grads = dict(zip("qkv", O.attention_backward(q, k, v, do, theta, causal, interleaved=il)))
         x = {"q": q, "k": k, "v": v}
         for name in "qkv":
             num = np.zeros_like(x[name])
@@ -426,11 +433,11 @@ def pin_backward_finite_differences():
                 xp = x[name].copy()
                 xp[idx] += h
                 args[name] = xp
-                lp = (O.attention(args["q"], args["k"], args["v"], theta, causal)[0] * do).sum()
+                lp = (O.attention(args["q"], args["k"], args["v"], theta, causal, interleaved=il)[0] * do).sum()
                 xm = x[name].copy()
                 xm[idx] -= h
                 args[name] = xm
-                lm = (O.attention(args["q"], args["k"], args["v"], theta, causal)[0] * do).sum()
+                lm = (O.attention(args["q"], args["k"], args["v"], theta, causal, interleaved=il)[0] * do).sum()
                 num[idx] = (lp - lm) / (2 * h)
             _close(grads[name], num, 1e-7, f"d{name} vs finite differences, case seed {seed}")
 

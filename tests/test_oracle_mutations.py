@@ -133,7 +133,7 @@ def _weights_ignore_causal(q_rot, k_rot, query_positions, causal, key_pos0=0):
 
 def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, unrotated_k=False,
                        k_rope_no_offset=False, q_rope_no_offset=False):
-    def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0):
+    def attention(q, k, v, rope_theta, causal=True, rows=None, q_pos0=0, k_pos0=0, interleaved=False):
         q = np.asarray(q, dtype=np.float64)
         k = np.asarray(k, dtype=np.float64)
         v = np.asarray(v, dtype=np.float64)
@@ -141,9 +141,10 @@ def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, 
         Hkv = k.shape[2]
         rows = np.arange(S) if rows is None else np.asarray(rows)
         qp = rows + (0 if q_rope_no_offset else q_pos0)
-        q_rot = O.apply_rope(q[:, rows], qp, rope_theta)
+        rope = O.apply_rope_interleaved if interleaved else O.apply_rope
+        q_rot = rope(q[:, rows], qp, rope_theta)
         kp = np.arange(S) + (0 if k_rope_no_offset else k_pos0)
-        k_rot = k if unrotated_k else O.apply_rope(k, kp, rope_theta)
+        k_rot = k if unrotated_k else rope(k, kp, rope_theta)
         vv = O.apply_rope(v, np.arange(S), rope_theta) if rope_v else v
         out = np.empty((B, len(rows), Hq, d))
         lse = np.empty((B, Hq, len(rows)))
@@ -163,12 +164,13 @@ def _attention_variant(*, lse_drops_max=False, rope_v=False, transpose_p=False, 
 
 def _backward_variant(*, drop_rowsum=False, rope_forward_sign=False, no_scale=False, ds_untransposed=False,
                       dv_untransposed=False, rowsum_of_dp=False):
-    def attention_backward(q, k, v, dout, rope_theta, causal=True):
+    def attention_backward(q, k, v, dout, rope_theta, causal=True, interleaved=False):
         q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
         B, S, Hq, d = q.shape
         Hkv = k.shape[2]
         pos = np.arange(S)
-        q_rot, k_rot = O.apply_rope(q, pos, rope_theta), O.apply_rope(k, pos, rope_theta)
+        rope = O.apply_rope_interleaved if interleaved else O.apply_rope
+        q_rot, k_rot = rope(q, pos, rope_theta), rope(k, pos, rope_theta)
         scale = 1.0 if no_scale else 1.0 / np.sqrt(np.float64(d))
         dq_rot, dk_rot, dv = np.zeros_like(q_rot), np.zeros_like(k_rot), np.zeros_like(v)
         for b in range(B):
@@ -188,9 +190,23 @@ def _backward_variant(*, drop_rowsum=False, rope_forward_sign=False, no_scale=Fa
                 dq_rot[b, :, h] = (ds @ k_rot[b, :, g]) * scale
                 dk_rot[b, :, g] += ((ds if ds_untransposed else ds.T) @ q_rot[b, :, h]) * scale
         back = pos if rope_forward_sign else -pos
-        return O.apply_rope(dq_rot, back, rope_theta), O.apply_rope(dk_rot, back, rope_theta), dv
+        return rope(dq_rot, back, rope_theta), rope(dk_rot, back, rope_theta), dv
 
     return attention_backward
+
+
+def _rope_interleaved_half_split(x, positions, rope_theta):
+    return O.apply_rope(x, positions, rope_theta)
+
+
+def _rope_interleaved_sign(x, positions, rope_theta):
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.outer(np.asarray(positions, dtype=np.float64), O.rope_frequencies(x.shape[-1], rope_theta))
+    c, s_ = np.cos(ang)[None, :, None, :], np.sin(ang)[None, :, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s_
+    out[..., 1::2] = x[..., 1::2] * c - x[..., 0::2] * s_
+    return out
 
 
 MUTATIONS = {
@@ -226,6 +242,8 @@ MUTATIONS = {
     "backward_scale_dropped": ("attention_backward", _backward_variant(no_scale=True)),
     "backward_dk_untransposed": ("attention_backward", _backward_variant(ds_untransposed=True)),
     "backward_dv_untransposed": ("attention_backward", _backward_variant(dv_untransposed=True)),
+    "interleaved_is_half_split": ("apply_rope_interleaved", _rope_interleaved_half_split),
+    "interleaved_wrong_sign": ("apply_rope_interleaved", _rope_interleaved_sign),
 }
 
 
