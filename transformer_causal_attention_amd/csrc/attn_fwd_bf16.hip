@@ -254,19 +254,29 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   // forms each (row, frequency) angle once: a table of (cos, sin) * q_scale for the 32 rows of
   // both row blocks, laid out [block][kk][hh][pair of e][row] x 16 bytes so that a lane's read
   // of its two entries is one 16-byte read and a wave's reads are consecutive.
-  char *const rot_tab = ldsv1;  // free until the prologue ends (2 * TB >= 4096 * D / 16 bytes)
-  auto build_rot_tab = [&]() __attribute__((always_inline)) {
-    constexpr int SLOTS = 2 * (NKK / 2) * 2 * 4 * 32;
+  // The table sits in a V^T buffer that the first step fills, and is built while the queries
+  // are still on their way: the frequencies are loaded before the queries (so waiting for them
+  // does not wait for the queries), and the angles only need them and the row positions.
+  char *const rot_tab = ldsv0;  // free until step 0 (2 * TB >= 4096 * D / 16 bytes)
+  constexpr int TAB_SLOTS = 2 * (NKK / 2) * 2 * 4 * 32;
+  constexpr int TAB_FJ = (128 * NKK) / 512;  // distinct frequency sets over a thread's entries
+  static_assert(TAB_SLOTS % 512 == 0 && TAB_FJ >= 1, "table entries per thread");
+  auto tab_freq_index = [&](int j, int z) __attribute__((always_inline)) {
+    const int id = tid + 512 * j;
+    const int c = (id / 32) % 4, h2 = (id / 128) % 2, kk = (id / 256) % (NKK / 2);
+    return 16 * kk + 8 * h2 + 2 * c + z;
+  };
+  auto build_rot_tab = [&](const double (&fq)[TAB_FJ][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < SLOTS / 512; ++j) {
+    for (int j = 0; j < TAB_SLOTS / 512; ++j) {
       const int id = tid + 512 * j;
-      const int r = id % 32, c = (id / 32) % 4, h2 = (id / 128) % 2, kk = (id / 256) % (NKK / 2);
+      const int r = id % 32;
       const int s = id / (256 * (NKK / 2));
       const int pos = p.q_pos0 + (s == 0 ? r_lo : r_hi) * RPB + r;
       f32x4 v;
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
-        const float t = turn_fraction(pos, freq[16 * kk + 8 * h2 + 2 * c + z]);
+        const float t = turn_fraction(pos, fq[j % TAB_FJ][z]);
         v[2 * z] = __builtin_amdgcn_cosf(t) * p.q_scale;  // argument in turns
         v[2 * z + 1] = __builtin_amdgcn_sinf(t) * p.q_scale;
       }
@@ -551,42 +561,51 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     wait_vm_all();
     __syncthreads();
   };
-  // ---- prologue: the first row block's queries are loaded while the first K tile is copied;
-  // then rotated, and group B leaves its rotated queries in its hand-off slot for group A
-  // (read at A's switch to block r_hi, at step len0 >= 1, so after at least one barrier).
+  // ---- prologue: the first row block's queries are loaded while the first K tile is copied,
+  // then rotated; group B leaves its rotated queries in its hand-off slot for group A (read at
+  // A's switch to block r_hi, at step len0 >= 1, so after at least one barrier).  The P.V
+  // product of a step always runs; with zero probabilities it must read finite values, so the
+  // V^T buffer that step 0 reads starts out zeroed (later the V^T buffers only ever hold
+  // staged tiles).
   {
     seg_rows(len0 > 0 ? 0 : 1);
     cur_seg = n_mine > 0 ? (len0 > 0 ? 0 : 1) : -1;
+    const bool shared_tab = p.hpw == 4;
+    double fq[TAB_FJ][2];
+    if (shared_tab) {
+#pragma unroll
+      for (int j = 0; j < TAB_FJ; ++j)
+#pragma unroll
+        for (int z = 0; z < 2; ++z) fq[j][z] = tab.rev[tab_freq_index(j, z)];
+    }
     u32x4 raw[NKK];
     load_q(raw);
     if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
-    if (tid < D / 2) freq[tid] = tab.rev[tid];
-    wait_vm_all();
-    __syncthreads();
-    if (p.hpw == 4) {
-      build_rot_tab();
-      __syncthreads();
-      rotate_q_tab(raw, len0 > 0 ? 0 : 1);
-    } else {
-      rotate_q(raw);
-    }
-    reset_seg();
-    // group A's block r_lo sees no key at all (a shard of later keys): its rows are empty
-    if (grp == 0 && two && t_lo == 0) store_seg(r_lo * RPB + sub * 32, 0.f, 0.f);
-    __syncthreads();  // frequencies and table are no longer read
-    // The P.V product of a step always runs; with zero probabilities it must read finite
-    // values, so the V^T buffer that step 0 reads starts out zeroed (later the V^T buffers only
-    // ever hold staged tiles).  Group B leaves its rotated queries in its slot.
     {
       u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
 #pragma unroll
       for (int r = 0; r < 2 * TB / 16 / 512; ++r) z1[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
     }
+    if (shared_tab) {
+      build_rot_tab(fq);
+      wait_vm_all();
+      __syncthreads();
+      rotate_q_tab(raw, len0 > 0 ? 0 : 1);
+    } else {
+      if (tid < D / 2) freq[tid] = tab.rev[tid];
+      wait_vm_all();
+      __syncthreads();
+      rotate_q(raw);
+      __syncthreads();  // the frequencies (in the hand-off slot) are no longer read
+    }
+    reset_seg();
+    // group A's block r_lo sees no key at all (a shard of later keys): its rows are empty
+    if (grp == 0 && two && t_lo == 0) store_seg(r_lo * RPB + sub * 32, 0.f, 0.f);
     if (grp == 1) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) *reinterpret_cast<bf16x8 *>(q_slot() + kk * 1024) = qf[kk];
     }
-    __syncthreads();
+    __syncthreads();  // the table is no longer read before step 0 copies into its buffer
   }
   for (int i = 0; i < n_iter; i += 2) {
     step(i, ldsk0, ldsk1, ldsv1, ldsv0);
@@ -605,11 +624,11 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 
   // ---- finish: the split block r_hi is merged in B.  Once every wave's last P.V product is
   // done the tile buffers are free: per-wave accumulators of group A go to ldsk0 (waves 0, 1)
-  // and ldsk1 (waves 2, 3), maxima and sums to ldsv0.
+  // and ldsk1 (waves 2, 3), maxima and sums to ldsv0; B's finished rows go to ldsv1.
+  __syncthreads();  // every wave's last P.V product has read its V^T tile
   if (x > 0) {
     float *mo = reinterpret_cast<float *>(gw < 2 ? ldsk0 : ldsk1) + (gw & 1) * NCB * 16 * 64;
     float *mm = reinterpret_cast<float *>(ldsv0);
-    __syncthreads();  // every wave's last P.V product has read its V^T tile (ldsv0 may hold one)
     // accumulators as [cb][v / 4][lane][v % 4]: one 16-byte access per lane and 4 registers
     f32x4 *mo4 = reinterpret_cast<f32x4 *>(mo);
     if (grp == 0) {
@@ -645,7 +664,40 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       m_run = m_new;
     }
   }
-  if (grp == 1) store_seg(row0, l_run, m_run);
+  // Group B's rows of block r_hi leave through LDS: each wave writes its 32 rows x D output
+  // (bf16) to ldsv1 as rows of D / 8 16-byte chunks, chunk c of row r at position c ^ (r % (D / 8))
+  // (so a store instruction's 32 rows spread over the banks), and then all eight waves copy
+  // whole rows to HBM with 16-byte stores, D * 2 contiguous bytes per (row, head).
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int WB = 32 * D * 2;    // staged bytes per wave
+  if (grp == 1) {
+    const float l_tot = l_run + xor32(l_run);
+    const int my_row = row0 + l32;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row with no visible key: out 0
+    char *st = ldsv1 + gw * WB + l32 * (D * 2) + 8 * hh;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(o[cb][4 * a + 0] * inv, o[cb][4 * a + 1] * inv);
+        w2[1] = pack_bf16x2(o[cb][4 * a + 2] * inv, o[cb][4 * a + 3] * inv);
+        *reinterpret_cast<u32x2 *>(st + (((4 * cb + a) ^ (l32 % CPR)) * 16)) = w2;
+      }
+    if (hh == 0 && my_row < S)
+      p.lse[((size_t)b * p.Hq + head) * S + my_row] =
+          l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16 * D / 512; ++k) {
+    const int c = tid + 512 * k;      // chunk of the 4 staged waves' rows
+    const int w = c / (4 * D), r = (c % (4 * D)) / CPR, ch = c % CPR;
+    const int row = r_hi * RPB + (w / p.hpw) * 32 + r;
+    const int hd = g * p.G + hg * p.hpw + (w % p.hpw);
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(ldsv1 + w * WB + r * (D * 2) + ((ch ^ (r % CPR)) * 16));
+    if (row < S) *reinterpret_cast<u32x4 *>(p.out + (((size_t)b * S + row) * p.Hq + hd) * D + 8 * ch) = val;
+  }
 }
 
 template <int D, bool CAUSAL>
