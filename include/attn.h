@@ -13,7 +13,10 @@
  *     rotate_half(x) = cat(-x2, x1) over the two halves of head_dim
  *     (Picotron page "Llama architecture and Flash Attention integration", section 1),
  *     frequencies rope_theta^(-2i/d), i < d/2, angle = position * frequency, applied to q
- *     and k only (PaLM-in-ColossalAI page, section 2.3 RotaryEmbedding);
+ *     and k only (PaLM-in-ColossalAI page, section 2.3 RotaryEmbedding); or, with
+ *     rope_style = ATTN_ROPE_INTERLEAVED, the adjacent-pair form in which dims (2i, 2i+1)
+ *     turn together by frequency i, the rotation read as multiplication by complex numbers
+ *     (llama3-from-scratch page, rotary position embedding);
  *   - scores scaled by 1/sqrt(head_dim), causal mask on keys later than the query, row
  *     softmax (llama3-from-scratch page: "attention score matrix", "causal mask",
  *     "softmax"); the row maximum is subtracted before exponentiating (PaLM page, 2.5);
@@ -40,16 +43,21 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Element types of q, k, v and out. */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
 #define ATTN_DTYPE_FP32 1 /* float32 inputs/outputs; float32 arithmetic throughout */
 
+/* Rotary pairing (rope_style arguments). */
+#define ATTN_ROPE_HALF 0        /* dims (i, i + d/2) form a rotated pair (rotate_half form) */
+#define ATTN_ROPE_INTERLEAVED 1 /* dims (2i, 2i + 1) form a rotated pair (complex form) */
+
 /* Return codes. */
 #define ATTN_OK 0
 #define ATTN_EINVAL (-1)       /* null or misaligned pointer, B/S/Hq/Hkv < 1, Hq % Hkv != 0,
-                                  rope_theta not finite or <= 0, causal not 0/1 */
+                                  rope_theta not finite or <= 0, rope_style or causal not
+                                  0/1 */
 #define ATTN_EUNSUPPORTED (-2) /* head_dim not 64 or 128, unknown dtype, sizes too large */
 #define ATTN_EHIP (-3)         /* the HIP runtime rejected an event record or kernel launch */
 #define ATTN_EWORKSPACE (-4)   /* workspace pointer null while needed, or workspace too small */
@@ -78,6 +86,7 @@ size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
  *   Hq, Hkv    query heads and K/V heads; Hq must be a multiple of Hkv
  *   head_dim   64 or 128 (even, split into two rotation halves)
  *   rope_theta rotary base (> 0, finite); frequencies rope_theta^(-2i/head_dim)
+ *   rope_style ATTN_ROPE_HALF or ATTN_ROPE_INTERLEAVED: which dims form a rotated pair
  *   causal     1: key j is visible to query i iff j <= i;  0: every key is visible
  *   dtype      ATTN_DTYPE_BF16 or ATTN_DTYPE_FP32
  *   out        device, (B, S, Hq, head_dim) contiguous, type `dtype`, 16-byte aligned;
@@ -91,8 +100,8 @@ size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
  * Returns ATTN_OK or one of the error codes above.
  */
 int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-             int head_dim, double rope_theta, int causal, int dtype, void *out, float *lse,
-             void *workspace, size_t workspace_bytes, void *stream);
+             int head_dim, double rope_theta, int rope_style, int causal, int dtype, void *out,
+             float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Same as attn_fwd, and additionally has the runtime record `ev_start` and `ev_stop` with the
@@ -101,8 +110,8 @@ int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, 
  * it.  Either event may be NULL.  Events come from attn_event_create.  For benchmarking.
  */
 int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                   int head_dim, double rope_theta, int causal, int dtype, void *out,
-                   float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                   int head_dim, double rope_theta, int rope_style, int causal, int dtype,
+                   void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
                    void *ev_start, void *ev_stop);
 
 /*
@@ -119,8 +128,9 @@ int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, in
  *   other arguments as for attn_fwd (same workspace size)
  */
 int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                   int head_dim, double rope_theta, int causal, int q_pos0, int k_pos0, int dtype,
-                   void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+                   int head_dim, double rope_theta, int rope_style, int causal, int q_pos0,
+                   int k_pos0, int dtype, void *out, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * Join two partial results for the same queries over disjoint key sets (the merge step of
@@ -153,14 +163,15 @@ int attn_merge(const void *o1, const float *lse1, const void *o2, const float *l
  *   k, v     device, (B, S_cap, Hkv, head_dim) bfloat16 contiguous, 16-byte aligned
  *   cache    device, at least attn_fwd_workspace_bytes(B, S_cap, Hkv, head_dim,
  *            ATTN_DTYPE_BF16) bytes, 16-byte aligned, owned by the caller; layout private
+ *   rope_style ATTN_ROPE_HALF or ATTN_ROPE_INTERLEAVED, as for attn_fwd
  *   0 <= key0 < key1 <= S_cap
  * Returns ATTN_OK, ATTN_EINVAL (null or misaligned pointer, bad sizes or key range, theta not
- * finite and > 0), ATTN_EUNSUPPORTED (head_dim not 64 or 128, sizes too large),
+ * finite and > 0, bad rope_style), ATTN_EUNSUPPORTED (head_dim not 64 or 128, sizes too large),
  * ATTN_EWORKSPACE (cache too small) or ATTN_EHIP (launch error).
  */
 int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, int Hkv, int head_dim,
-                    double rope_theta, int key0, int key1, void *cache, size_t cache_bytes,
-                    void *stream);
+                    double rope_theta, int rope_style, int key0, int key1, void *cache,
+                    size_t cache_bytes, void *stream);
 
 /* Workspace bytes attn_decode needs for these sizes (partial results of its key splits),
  * independent of S_cap and q_pos; 0 for unsupported sizes. */
@@ -171,7 +182,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim);
  * q_pos (rotated there) attends to cached keys 0 .. q_pos of K/V head h / (Hq/Hkv):
  * the row q_pos of the causal attention attn_fwd computes, with the same scale, rotation and
  * lse.  Keys 0 .. q_pos of `cache` must have been prepared by attn_kv_prepare with the same
- * rope_theta.  The key range is split over workgroups and joined by a second kernel.
+ * rope_theta and rope_style.  The key range is split over workgroups and joined by a second kernel.
  *   q        device, (B, Hq, head_dim) bfloat16 contiguous, 16-byte aligned
  *   cache    as filled by attn_kv_prepare for (B, S_cap, Hkv, head_dim)
  *   out      device, (B, Hq, head_dim) bfloat16, 16-byte aligned (written)
@@ -181,8 +192,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim);
  * Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE or ATTN_EHIP as above.
  */
 int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
-                double rope_theta, int q_pos, void *out, float *lse, void *workspace,
-                size_t workspace_bytes, void *stream);
+                double rope_theta, int rope_style, int q_pos, void *out, float *lse,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass: the gradients dq, dk, dv of attn_fwd's out for a given output gradient dout
@@ -196,7 +207,7 @@ int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int 
  *
  *   q, dout        device, (B, S, Hq, head_dim) bfloat16 contiguous, 16-byte aligned
  *   k, v           device, (B, S, Hkv, head_dim) bfloat16, 16-byte aligned
- *   out, lse       attn_fwd's outputs for the same q, k, v, rope_theta and causal
+ *   out, lse       attn_fwd's outputs for the same q, k, v, rope_theta, rope_style, causal
  *   dq; dk, dv     device, shaped like q; like k (written), 16-byte aligned
  *   workspace      device, >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned (the
  *                  re-laid-out operands), caller owned
@@ -206,7 +217,7 @@ int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int 
 size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim);
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
              const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
-             int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+             int rope_style, int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
              void *stream);
 
 /* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */

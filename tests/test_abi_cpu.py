@@ -28,6 +28,23 @@ def test_header_declares_the_documented_entry_points():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
 
 
+def declared_arity():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(attn_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_the_header():
+    arity = declared_arity()
+    assert set(arity) == set(_lib.SIGNATURES)
+    for name, (_, args) in _lib.SIGNATURES.items():
+        assert len(args) == arity[name], f"{name}: binding has {len(args)} arguments, header {arity[name]}"
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in declared_functions():
@@ -35,7 +52,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert _lib.abi_version() == 4
+    assert _lib.abi_version() == 5
     for code in (0, -1, -2, -3, -4):
         assert len(_lib.strerror(code)) > 5
     assert "unknown" in _lib.strerror(12345)
@@ -58,10 +75,11 @@ P = 0x10000
 
 def call(**over):
     a = dict(q=P, k=P, v=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=10000.0, causal=1, dtype=0,
-             out=P, lse=P, ws=P, wsb=1 << 30, stream=None)
+             out=P, lse=P, ws=P, wsb=1 << 30, stream=None, rope=0)
     a.update(over)
     return _lib.fwd_raw(a["q"], a["k"], a["v"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"],
-                        a["causal"], a["dtype"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+                        a["causal"], a["dtype"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"],
+                        rope_style=a["rope"])
 
 
 @pytest.mark.parametrize("over", [
@@ -70,7 +88,7 @@ def call(**over):
     dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(B=-3), dict(S=-1),
     dict(Hq=6, Hkv=4), dict(Hq=3, Hkv=2),
     dict(theta=0.0), dict(theta=-1.0), dict(theta=float("nan")), dict(theta=float("inf")),
-    dict(causal=2), dict(causal=-1),
+    dict(causal=2), dict(causal=-1), dict(rope=2), dict(rope=-1),
 ])
 def test_invalid_arguments(over):
     assert call(**over) == _lib.ATTN_EINVAL
@@ -91,8 +109,10 @@ def test_workspace_rejected(over):
 
 def test_timed_variant_validates_too():
     lib = _lib.load()
-    rc = lib.attn_fwd_timed(P, P, P, 1, 64, 4, 1, 96, 1e4, 1, 0, P, P, P, 1 << 30, None, None, None)
+    rc = lib.attn_fwd_timed(P, P, P, 1, 64, 4, 1, 96, 1e4, 0, 1, 0, P, P, P, 1 << 30, None, None, None)
     assert rc == _lib.ATTN_EUNSUPPORTED
+    rc = lib.attn_fwd_timed(P, P, P, 1, 64, 4, 1, 64, 1e4, 7, 1, 0, P, P, P, 1 << 30, None, None, None)
+    assert rc == _lib.ATTN_EINVAL
 
 
 def test_event_helpers_reject_null():
@@ -104,16 +124,16 @@ def test_event_helpers_reject_null():
 
 def shard_call(**over):
     a = dict(q=P, k=P, v=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=10000.0, causal=1, qp=0, kp=0, dtype=0,
-             out=P, lse=P, ws=P, wsb=1 << 30, stream=None)
+             out=P, lse=P, ws=P, wsb=1 << 30, stream=None, rope=0)
     a.update(over)
     return _lib.shard_raw(a["q"], a["k"], a["v"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"],
                           a["causal"], a["qp"], a["kp"], a["dtype"], a["out"], a["lse"], a["ws"], a["wsb"],
-                          a["stream"])
+                          a["stream"], rope_style=a["rope"])
 
 
 @pytest.mark.parametrize("over", [
     dict(qp=-1), dict(kp=-5), dict(qp=(1 << 30) - 63), dict(kp=1 << 30), dict(q=None), dict(lse=P + 1),
-    dict(Hq=3, Hkv=2), dict(causal=3),
+    dict(Hq=3, Hkv=2), dict(causal=3), dict(rope=5),
 ])
 def test_shard_invalid_arguments(over):
     assert shard_call(**over) == _lib.ATTN_EINVAL
@@ -161,10 +181,11 @@ def test_decode_workspace_bytes():
 
 
 def prep_call(**over):
-    a = dict(k=P, v=P, B=1, S=256, Hkv=2, d=64, theta=1e4, key0=0, key1=256, cache=P, cb=1 << 30, stream=None)
+    a = dict(k=P, v=P, B=1, S=256, Hkv=2, d=64, theta=1e4, key0=0, key1=256, cache=P, cb=1 << 30, stream=None,
+             rope=0)
     a.update(over)
     return _lib.kv_prepare_raw(a["k"], a["v"], a["B"], a["S"], a["Hkv"], a["d"], a["theta"], a["key0"], a["key1"],
-                               a["cache"], a["cb"], a["stream"])
+                               a["cache"], a["cb"], a["stream"], rope_style=a["rope"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -174,7 +195,7 @@ def prep_call(**over):
     (dict(key0=-1), _lib.ATTN_EINVAL), (dict(key0=5, key1=5), _lib.ATTN_EINVAL),
     (dict(key1=257), _lib.ATTN_EINVAL), (dict(key0=300, key1=301), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1, key1=1), _lib.ATTN_EUNSUPPORTED),
-    (dict(cb=2 * 2 * 256 * 64 * 2 - 1), _lib.ATTN_EWORKSPACE),
+    (dict(cb=2 * 2 * 256 * 64 * 2 - 1), _lib.ATTN_EWORKSPACE), (dict(rope=3), _lib.ATTN_EINVAL),
 ])
 def test_kv_prepare_rejections(over, code):
     assert prep_call(**over) == code
@@ -182,17 +203,17 @@ def test_kv_prepare_rejections(over, code):
 
 def decode_call(**over):
     a = dict(q=P, cache=P, B=1, S=256, Hq=8, Hkv=2, d=128, theta=1e4, pos=100, out=P, lse=P, ws=P, wsb=1 << 30,
-             stream=None)
+             stream=None, rope=0)
     a.update(over)
     return _lib.decode_raw(a["q"], a["cache"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"], a["pos"],
-                           a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+                           a["out"], a["lse"], a["ws"], a["wsb"], a["stream"], rope_style=a["rope"])
 
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), _lib.ATTN_EINVAL), (dict(cache=P + 4), _lib.ATTN_EINVAL), (dict(out=P + 2), _lib.ATTN_EINVAL),
     (dict(lse=P + 1), _lib.ATTN_EINVAL), (dict(lse=None), _lib.ATTN_EINVAL),
     (dict(Hq=6, Hkv=4), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(theta=-2.0), _lib.ATTN_EINVAL),
-    (dict(pos=-1), _lib.ATTN_EINVAL), (dict(pos=256), _lib.ATTN_EINVAL),
+    (dict(pos=-1), _lib.ATTN_EINVAL), (dict(pos=256), _lib.ATTN_EINVAL), (dict(rope=-1), _lib.ATTN_EINVAL),
     (dict(d=32), _lib.ATTN_EUNSUPPORTED),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=64), _lib.ATTN_EWORKSPACE), (dict(ws=P + 4), _lib.ATTN_EWORKSPACE),
 ])
@@ -211,10 +232,11 @@ def test_bwd_workspace_bytes():
 
 def bwd_call(**over):
     a = dict(q=P, k=P, v=P, out=P, lse=P, dout=P, B=1, S=64, Hq=4, Hkv=1, d=64, theta=1e4, causal=1, dq=P, dk=P,
-             dv=P, ws=P, wsb=1 << 30, stream=None)
+             dv=P, ws=P, wsb=1 << 30, stream=None, rope=0)
     a.update(over)
     return _lib.bwd_raw(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["B"], a["S"], a["Hq"], a["Hkv"],
-                        a["d"], a["theta"], a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], a["stream"])
+                        a["d"], a["theta"], a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], a["stream"],
+                        rope_style=a["rope"])
 
 
 @pytest.mark.parametrize("over,code", [
@@ -223,6 +245,7 @@ def bwd_call(**over):
     (dict(k=P + 8), _lib.ATTN_EINVAL), (dict(dout=P + 2), _lib.ATTN_EINVAL), (dict(dk=P + 4), _lib.ATTN_EINVAL),
     (dict(lse=P + 2), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(S=-4), _lib.ATTN_EINVAL),
     (dict(Hq=3, Hkv=2), _lib.ATTN_EINVAL), (dict(causal=2), _lib.ATTN_EINVAL), (dict(theta=float("inf")), _lib.ATTN_EINVAL),
+    (dict(rope=2), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1), _lib.ATTN_EUNSUPPORTED),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=100), _lib.ATTN_EWORKSPACE), (dict(ws=P + 8), _lib.ATTN_EWORKSPACE),
 ])

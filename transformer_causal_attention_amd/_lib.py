@@ -12,6 +12,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 ATTN_DTYPE_BF16 = 0
 ATTN_DTYPE_FP32 = 1
 
+ATTN_ROPE_HALF = 0
+ATTN_ROPE_INTERLEAVED = 1
+
 ATTN_OK = 0
 ATTN_EINVAL = -1
 ATTN_EUNSUPPORTED = -2
@@ -21,13 +24,14 @@ ATTN_EWORKSPACE = -4
 # Every symbol include/attn.h declares, with its ctypes signature.
 _VP = ctypes.c_void_p
 _I = ctypes.c_int
-_FWD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
-_SHARD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_FWD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_SHARD_ARGS = [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _I, _I, _VP, _VP, _VP, ctypes.c_size_t,
+               _VP]
 _MERGE_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]
-_PREP_ARGS = [_VP, _VP, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, ctypes.c_size_t, _VP]
-_BWD_ARGS = [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _VP, _VP, _VP, _VP,
+_PREP_ARGS = [_VP, _VP, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _VP, ctypes.c_size_t, _VP]
+_BWD_ARGS = [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, _VP,
              ctypes.c_size_t, _VP]
-_DECODE_ARGS = [_VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_DECODE_ARGS = [_VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
 SIGNATURES = {
     "attn_abi_version": (_I, []),
     "attn_strerror": (ctypes.c_char_p, [_I]),
@@ -85,10 +89,10 @@ def workspace_bytes(B, S, Hkv, head_dim, dtype):
 
 
 def fwd_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, workspace,
-            workspace_bytes_, stream, ev_start=None, ev_stop=None):
+            workspace_bytes_, stream, ev_start=None, ev_stop=None, rope_style=ATTN_ROPE_HALF):
     """Call attn_fwd (or attn_fwd_timed when events are given) with raw pointers; returns the code."""
     lib = load()
-    args = (q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(causal), dtype, out, lse,
+    args = (q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style), int(causal), dtype, out, lse,
             workspace, workspace_bytes_, stream)
     if ev_start is None and ev_stop is None:
         return lib.attn_fwd(*args)
@@ -96,10 +100,10 @@ def fwd_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, ls
 
 
 def shard_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dtype, out, lse,
-              workspace, workspace_bytes_, stream):
+              workspace, workspace_bytes_, stream, rope_style=ATTN_ROPE_HALF):
     """Call attn_fwd_shard with raw pointers; returns the code."""
-    return load().attn_fwd_shard(q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(causal), int(q_pos0),
-                                 int(k_pos0), dtype, out, lse, workspace, workspace_bytes_, stream)
+    return load().attn_fwd_shard(q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style), int(causal),
+                                 int(q_pos0), int(k_pos0), dtype, out, lse, workspace, workspace_bytes_, stream)
 
 
 def merge_raw(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream):
@@ -107,10 +111,11 @@ def merge_raw(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream):
     return load().attn_merge(o1, lse1, o2, lse2, B, S, H, head_dim, dtype, out, lse, stream)
 
 
-def kv_prepare_raw(k, v, B, S_cap, Hkv, head_dim, rope_theta, key0, key1, cache, cache_bytes, stream):
+def kv_prepare_raw(k, v, B, S_cap, Hkv, head_dim, rope_theta, key0, key1, cache, cache_bytes, stream,
+                   rope_style=ATTN_ROPE_HALF):
     """Call attn_kv_prepare with raw pointers; returns the code."""
-    return load().attn_kv_prepare(k, v, B, S_cap, Hkv, head_dim, float(rope_theta), int(key0), int(key1), cache,
-                                  cache_bytes, stream)
+    return load().attn_kv_prepare(k, v, B, S_cap, Hkv, head_dim, float(rope_theta), int(rope_style), int(key0),
+                                  int(key1), cache, cache_bytes, stream)
 
 
 def decode_workspace_bytes(B, Hq, Hkv, head_dim):
@@ -118,10 +123,10 @@ def decode_workspace_bytes(B, Hq, Hkv, head_dim):
 
 
 def decode_raw(q, cache, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, out, lse, workspace, workspace_bytes_,
-               stream):
+               stream, rope_style=ATTN_ROPE_HALF):
     """Call attn_decode with raw pointers; returns the code."""
-    return load().attn_decode(q, cache, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(q_pos), out, lse,
-                              workspace, workspace_bytes_, stream)
+    return load().attn_decode(q, cache, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(rope_style), int(q_pos),
+                              out, lse, workspace, workspace_bytes_, stream)
 
 
 def bwd_workspace_bytes(B, S, Hq, Hkv, head_dim):
@@ -129,10 +134,10 @@ def bwd_workspace_bytes(B, S, Hq, Hkv, head_dim):
 
 
 def bwd_raw(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, rope_theta, causal, dq, dk, dv, workspace,
-            workspace_bytes_, stream):
+            workspace_bytes_, stream, rope_style=ATTN_ROPE_HALF):
     """Call attn_bwd with raw pointers; returns the code."""
-    return load().attn_bwd(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, float(rope_theta), int(causal), dq, dk,
-                           dv, workspace, workspace_bytes_, stream)
+    return load().attn_bwd(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style),
+                           int(causal), dq, dk, dv, workspace, workspace_bytes_, stream)
 
 
 class Event:

@@ -26,8 +26,12 @@ def _shapes(q, k, v):
     return B, S, Hq, Hkv, D
 
 
+def _rope_style(interleaved):
+    return _lib.ATTN_ROPE_INTERLEAVED if interleaved else _lib.ATTN_ROPE_HALF
+
+
 def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=None, events=None,
-                  q_pos0=0, k_pos0=0):
+                  q_pos0=0, k_pos0=0, interleaved=False):
     """attn_fwd writing into caller-provided out (like q) and lse (B, Hq, S) float32.
 
     workspace: optional uint8 GPU tensor of at least workspace_bytes(...) bytes.
@@ -35,6 +39,7 @@ def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=
     events: optional (start, stop) pair of Event recorded around the attention kernel.
     q_pos0, k_pos0: positions of query row 0 and key row 0 when the call is one shard of a
     longer sequence (attn_fwd_shard); events are not available for shards.
+    interleaved: rotate adjacent dim pairs (2i, 2i+1) instead of (i, i + D/2).
     """
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
@@ -55,21 +60,24 @@ def attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace=None, stream=
             raise ValueError("events are not available for a shard call")
         rc = _lib.shard_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
                             1 if causal else 0, q_pos0, k_pos0, code, out.data_ptr(), lse.data_ptr(),
-                            ws_ptr, ws_bytes, st.cuda_stream)
+                            ws_ptr, ws_bytes, st.cuda_stream, rope_style=_rope_style(interleaved))
         if rc != _lib.ATTN_OK:
             raise _lib.AttnError(rc, "attn_fwd_shard")
         return out, lse
     ev0, ev1 = (events[0].ptr, events[1].ptr) if events is not None else (None, None)
     rc = _lib.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
                       1 if causal else 0, code, out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes,
-                      st.cuda_stream, ev0, ev1)
+                      st.cuda_stream, ev0, ev1, rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_fwd")
     return out, lse
 
 
-def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, events=None, q_pos0=0, k_pos0=0):
+def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, events=None, q_pos0=0, k_pos0=0,
+             interleaved=False):
     """Fused RoPE + causal GQA attention forward.  Returns (out, lse).
+
+    interleaved: adjacent-pair rotary form (dims 2i, 2i+1) instead of the half-split one.
 
     With q_pos0 / k_pos0 the call is one shard of a longer sequence (queries at q_pos0 + i,
     keys at k_pos0 + j); rows that see no key get out 0 and lse -inf, ready for attn_merge.
@@ -77,7 +85,8 @@ def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, even
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events, q_pos0, k_pos0)
+    return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events, q_pos0, k_pos0,
+                         interleaved)
 
 
 def attn_merge(o1, lse1, o2, lse2, out=None, lse=None, stream=None):
@@ -129,7 +138,7 @@ def new_kv_cache(B, S_cap, Hkv, head_dim, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def kv_prepare(k, v, rope_theta, key0, key1, cache, stream=None):
+def kv_prepare(k, v, rope_theta, key0, key1, cache, stream=None, interleaved=False):
     """Rotate and store keys [key0, key1) of k (and their values) into cache (attn_kv_prepare).
 
     k, v: (B, S_cap, Hkv, D) bfloat16 holding valid rows from 64 * (key0 // 64) to key1.
@@ -143,13 +152,14 @@ def kv_prepare(k, v, rope_theta, key0, key1, cache, stream=None):
     B, S_cap, Hkv, D = k.shape
     st = stream if stream is not None else torch.cuda.current_stream(k.device)
     rc = _lib.kv_prepare_raw(k.data_ptr(), v.data_ptr(), B, S_cap, Hkv, D, rope_theta, key0, key1,
-                             cache.data_ptr(), cache.numel(), st.cuda_stream)
+                             cache.data_ptr(), cache.numel(), st.cuda_stream, rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_kv_prepare")
     return cache
 
 
-def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, workspace=None, stream=None):
+def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, workspace=None, stream=None,
+                interleaved=False):
     """One decode step: q (B, Hq, D) bfloat16 at position q_pos against cached keys 0 .. q_pos.
 
     Returns (out (B, Hq, D) bfloat16, lse (B, Hq) float32), equal to row q_pos of attn_fwd.
@@ -171,17 +181,18 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
         if stream is not None:
             workspace.record_stream(st)
     rc = _lib.decode_raw(q.data_ptr(), cache.data_ptr(), B, S_cap, Hq, Hkv, D, rope_theta, q_pos, out.data_ptr(),
-                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream,
+                         rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_decode")
     return out, lse
 
 
 def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None, dv=None, workspace=None,
-             stream=None):
+             stream=None, interleaved=False):
     """Gradients (dq, dk, dv) of attn_fwd's out for the output gradient dout (bf16).
 
-    out, lse: attn_fwd's results for the same q, k, v, rope_theta and causal.
+    out, lse: attn_fwd's results for the same q, k, v, rope_theta, causal and interleaved.
     """
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -204,7 +215,7 @@ def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None,
             workspace.record_stream(st)
     rc = _lib.bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                       B, S, Hq, Hkv, D, rope_theta, 1 if causal else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      workspace.data_ptr(), workspace.numel(), st.cuda_stream)
+                      workspace.data_ptr(), workspace.numel(), st.cuda_stream, rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_bwd")
     return dq, dk, dv

@@ -41,8 +41,11 @@ int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int cau
   return ATTN_OK;
 }
 
-attn::RopeTable rope_table(int d, double rope_theta) {
+bool rope_style_ok(int rope_style) { return rope_style == ATTN_ROPE_HALF || rope_style == ATTN_ROPE_INTERLEAVED; }
+
+attn::RopeTable rope_table(int d, double rope_theta, int rope_style) {
   attn::RopeTable t{};
+  t.interleaved = rope_style == ATTN_ROPE_INTERLEAVED;
   const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < d / 2; ++i) t.rev[i] = std::pow(rope_theta, -(2.0 * i) / d) / two_pi;
   return t;
@@ -120,7 +123,7 @@ hipError_t run_f32(const void *q, const void *k, const void *v, int B, int S, in
 }
 
 int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv, int d,
-             double rope_theta, int causal, int q_pos0, int k_pos0, int dtype, void *out, float *lse,
+             double rope_theta, int rope_style, int causal, int q_pos0, int k_pos0, int dtype, void *out, float *lse,
              void *workspace, size_t workspace_bytes, void *stream, void *ev_start, void *ev_stop) {
   if (!q || !k || !v || !out || !lse) return ATTN_EINVAL;
   // positions (offset + row) stay below 2^30, so every position difference fits an int
@@ -128,12 +131,13 @@ int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, 
     return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
     return ATTN_EINVAL;
+  if (!rope_style_ok(rope_style)) return ATTN_EINVAL;
   const int rc = check_shape(B, S, Hq, Hkv, d, rope_theta, causal, dtype);
   if (rc != ATTN_OK) return rc;
   const size_t need = attn_fwd_workspace_bytes(B, S, Hkv, d, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_EWORKSPACE;
 
-  const attn::RopeTable tab = rope_table(d, rope_theta);
+  const attn::RopeTable tab = rope_table(d, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t err;
@@ -153,7 +157,7 @@ ATTN_EXPORT int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 ATTN_EXPORT const char *attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
-    case ATTN_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size, Hq not a multiple of Hkv, bad rope_theta or causal flag)";
+    case ATTN_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size, Hq not a multiple of Hkv, bad rope_theta, rope_style or causal flag)";
     case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, dtype bf16 or fp32, sizes within limits)";
     case ATTN_EHIP: return "HIP runtime error while recording an event or launching a kernel";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()";
@@ -168,17 +172,17 @@ ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim,
 }
 
 ATTN_EXPORT int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                         int head_dim, double rope_theta, int causal, int dtype, void *out, float *lse,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, 0, 0, dtype, out, lse, workspace,
+                         int head_dim, double rope_theta, int rope_style, int causal, int dtype, void *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, rope_style, causal, 0, 0, dtype, out, lse, workspace,
                   workspace_bytes, stream, nullptr, nullptr);
 }
 
 ATTN_EXPORT int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                               int head_dim, double rope_theta, int causal, int q_pos0, int k_pos0,
-                               int dtype, void *out, float *lse, void *workspace, size_t workspace_bytes,
-                               void *stream) {
-  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dtype, out, lse,
+                               int head_dim, double rope_theta, int rope_style, int causal, int q_pos0,
+                               int k_pos0, int dtype, void *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, rope_style, causal, q_pos0, k_pos0, dtype, out, lse,
                   workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
@@ -213,10 +217,10 @@ ATTN_EXPORT int attn_merge(const void *o1, const float *lse1, const void *o2, co
 }
 
 ATTN_EXPORT int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
-                               int head_dim, double rope_theta, int causal, int dtype, void *out,
-                               float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                               int head_dim, double rope_theta, int rope_style, int causal, int dtype,
+                               void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
                                void *ev_start, void *ev_stop) {
-  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, 0, 0, dtype, out, lse, workspace,
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, rope_style, causal, 0, 0, dtype, out, lse, workspace,
                   workspace_bytes, stream, ev_start, ev_stop);
 }
 
@@ -254,13 +258,13 @@ int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
 }  // namespace
 
 ATTN_EXPORT int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, int Hkv, int head_dim,
-                                double rope_theta, int key0, int key1, void *cache, size_t cache_bytes,
-                                void *stream) {
+                                double rope_theta, int rope_style, int key0, int key1, void *cache,
+                                size_t cache_bytes, void *stream) {
   if (!k || !v || !cache) return ATTN_EINVAL;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(cache, 16)) return ATTN_EINVAL;
   const int rc = check_decode_shape(B, S_cap, Hkv, Hkv, head_dim);
   if (rc != ATTN_OK) return rc;
-  if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.0 || !rope_style_ok(rope_style)) return ATTN_EINVAL;
   if (key0 < 0 || key1 <= key0 || key1 > S_cap) return ATTN_EINVAL;
   if (cache_bytes < attn_fwd_workspace_bytes(B, S_cap, Hkv, head_dim, ATTN_DTYPE_BF16)) return ATTN_EWORKSPACE;
   const size_t s_pad = padded_len(S_cap);
@@ -277,7 +281,7 @@ ATTN_EXPORT int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, 
   pp.tile0 = key0 / kTileKeys;
   pp.n_run = (key1 + kTileKeys - 1) / kTileKeys - pp.tile0;
   pp.k_pos0 = 0;
-  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = head_dim == 64 ? attn::launch_prep_kv<64>(pp, tab, st) : attn::launch_prep_kv<128>(pp, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
@@ -290,13 +294,13 @@ ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_
 }
 
 ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
-                            double rope_theta, int q_pos, void *out, float *lse, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            double rope_theta, int rope_style, int q_pos, void *out, float *lse,
+                            void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !cache || !out || !lse) return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
   const int rc = check_decode_shape(B, S_cap, Hq, Hkv, head_dim);
   if (rc != ATTN_OK) return rc;
-  if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.0 || !rope_style_ok(rope_style)) return ATTN_EINVAL;
   if (q_pos < 0 || q_pos >= S_cap) return ATTN_EINVAL;
   const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, head_dim);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_EWORKSPACE;
@@ -324,7 +328,7 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, 
   p.pm = p.po + rows * head_dim;
   p.pl = p.pm + rows;
   p.q_scale = q_scale(head_dim);
-  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = head_dim == 64 ? attn::launch_decode<64>(p, tab, st) : attn::launch_decode<128>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
@@ -347,12 +351,12 @@ ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int h
 
 ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
                          const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
-                         int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                         int rope_style, int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
                          void *stream) {
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
   for (const void *ptr : {q, k, v, out, dout, (const void *)dq, (const void *)dk, (const void *)dv})
     if (!aligned(ptr, 16)) return ATTN_EINVAL;
-  if (!aligned(lse, 4)) return ATTN_EINVAL;
+  if (!aligned(lse, 4) || !rope_style_ok(rope_style)) return ATTN_EINVAL;
   const int rc = check_shape(B, S, Hq, Hkv, head_dim, rope_theta, causal, ATTN_DTYPE_BF16);
   if (rc != ATTN_OK) return rc;
   const size_t nb = bwd_blocks(S);
@@ -392,7 +396,7 @@ ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void
   p.causal = causal;
   p.scale_log2 = q_scale(head_dim);
   p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)head_dim));
-  const attn::RopeTable tab = rope_table(head_dim, rope_theta);
+  const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = head_dim == 64 ? attn::launch_bwd<64>(p, tab, st) : attn::launch_bwd<128>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;

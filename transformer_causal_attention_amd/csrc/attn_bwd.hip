@@ -121,8 +121,13 @@ __global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable 
     u32x4 kx = {0u, 0u, 0u, 0u}, ky = kx, vx = kx, vy = kx;
     if (r < p.S) {
       const size_t src = (((size_t)b * p.S + r) * p.Hkv + g) * D + 8 * c;
-      kx = *reinterpret_cast<const u32x4 *>(p.k + src);
-      ky = *reinterpret_cast<const u32x4 *>(p.k + src + D / 2);
+      if (tab.interleaved) {  // adjacent-pair form: dims 16c .. 16c+15 as evens and odds
+        const size_t ks = src + 8 * c;
+        deinterleave16(*reinterpret_cast<const u32x4 *>(p.k + ks), *reinterpret_cast<const u32x4 *>(p.k + ks + 8), kx, ky);
+      } else {
+        kx = *reinterpret_cast<const u32x4 *>(p.k + src);
+        ky = *reinterpret_cast<const u32x4 *>(p.k + src + D / 2);
+      }
       vx = *reinterpret_cast<const u32x4 *>(p.v + src);
       vy = *reinterpret_cast<const u32x4 *>(p.v + src + D / 2);
     }
@@ -161,8 +166,13 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
     u32x4 qx = {0u, 0u, 0u, 0u}, qy = qx, gx = qx, gy = qx, ox = qx, oy = qx;
     if (ok) {
       const size_t src = (((size_t)b * p.S + r) * p.Hq + h) * D + 8 * c;
-      qx = *reinterpret_cast<const u32x4 *>(p.q + src);
-      qy = *reinterpret_cast<const u32x4 *>(p.q + src + D / 2);
+      if (tab.interleaved) {  // adjacent-pair form: dims 16c .. 16c+15 as evens and odds
+        const size_t qs = src + 8 * c;
+        deinterleave16(*reinterpret_cast<const u32x4 *>(p.q + qs), *reinterpret_cast<const u32x4 *>(p.q + qs + 8), qx, qy);
+      } else {
+        qx = *reinterpret_cast<const u32x4 *>(p.q + src);
+        qy = *reinterpret_cast<const u32x4 *>(p.q + src + D / 2);
+      }
       gx = *reinterpret_cast<const u32x4 *>(p.dout + src);
       gy = *reinterpret_cast<const u32x4 *>(p.dout + src + D / 2);
       ox = *reinterpret_cast<const u32x4 *>(p.out + src);
@@ -345,9 +355,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable ta
       for (int v = 0; v < 16; ++v) {
         const int key = kb * BR + res_row(v, hh);
         if (key < p.S) {
-          const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D + l32;
+          const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
+          // dk of the adjacent-pair form goes back to the original dim order; dv is never reordered
+          const int il = DV ? 0 : tab.interleaved;
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) dst0[dst + 32 * cb] = (__bf16)acc[cb][v];
+          for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
         }
       }
     }
@@ -465,9 +477,9 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p, RopeTable tab) 
     for (int v = 0; v < 16; ++v) {
       const int row = qb * BR + res_row(v, hh);
       if (row < p.S) {
-        const size_t dst = (((size_t)b * p.S + row) * p.Hq + h) * D + l32;
+        const size_t dst = (((size_t)b * p.S + row) * p.Hq + h) * D;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) p.dq[dst + 32 * cb] = (__bf16)dq[cb][v];
+        for (int cb = 0; cb < NCB; ++cb) p.dq[dst + rope_src_dim(32 * cb + l32, D / 2, tab.interleaved)] = (__bf16)dq[cb][v];
       }
     }
   }

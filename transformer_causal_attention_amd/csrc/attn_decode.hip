@@ -81,10 +81,22 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   const int head = g * p.G + hc;
   u32x4 raw[NKK];
   {
-    const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 8 * hh;
+    if (tab.interleaved) {
+      // adjacent-pair rotary form: dims 32kk + 16hh .. +15, split into evens and odds (the
+      // reordered dims 16kk + 8hh + e and D/2 + 16kk + 8hh + e)
+      const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 16 * hh;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      raw[kk] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < NKK / 2; ++kk) {
+        const u32x4 lo = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 hi = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk + 8) : u32x4{0u, 0u, 0u, 0u};
+        deinterleave16(lo, hi, raw[kk], raw[kk + NKK / 2]);
+      }
+    } else {
+      const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        raw[kk] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   // The (b, g) run of tiles as buffer resources: a load whose (per-lane) offset lies past the

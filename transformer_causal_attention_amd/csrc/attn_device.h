@@ -17,9 +17,38 @@ constexpr int kMaxHalfDim = 64;  // head_dim <= 128
 // Rotary frequencies in revolutions per position: rope_theta^(-2i/d) / (2*pi), i < d/2.
 // Computed on the host in double precision and passed by value, so every index used by
 // the kernels is a compile-time constant or wave-uniform (scalar loads, no scratch).
+//
+// interleaved = 1 selects the adjacent-pair rotary form, where dims (2i, 2i+1) turn together by
+// frequency i (llama3-from-scratch page, the rotary embedding taken as complex numbers) instead
+// of (i, i + d/2).  It equals the half-split rotation applied to the head dims reordered as
+// (x0, x2, .., x_{d-2}, x1, x3, .., x_{d-1}); q and k are reordered alike, so their dot products
+// are unchanged, and the kernels simply read q and k in that order (and write dq, dk back in the
+// original one).  V and the output are not reordered.
 struct RopeTable {
   double rev[kMaxHalfDim];
+  int interleaved;
 };
+
+// 16 consecutive bf16 values (lo = elements 0..7, hi = 8..15) split into the even-indexed
+// ones (ev) and the odd-indexed ones (od), each in order: the reordering of the adjacent-pair
+// rotary form.
+__device__ __forceinline__ void deinterleave16(const u32x4 &lo, const u32x4 &hi, u32x4 &ev, u32x4 &od) {
+  u32x4 e, o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = w < 2 ? lo[2 * w] : hi[2 * w - 4];
+    const uint32_t y = w < 2 ? lo[2 * w + 1] : hi[2 * w - 3];
+    e[w] = (x & 0xffffu) | (y << 16);
+    o[w] = (x >> 16) | (y & 0xffff0000u);
+  }
+  ev = e;
+  od = o;
+}
+
+// Position in the original head dims of reordered dim c (see RopeTable).
+__device__ __forceinline__ int rope_src_dim(int c, int half, int interleaved) {
+  return interleaved ? (c < half ? 2 * c : 2 * (c - half) + 1) : c;
+}
 
 // Everything the bf16 attention kernel needs besides the rotation table.
 struct FwdParams {

@@ -212,13 +212,29 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   };
   auto load_q = [&](u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
     const int my_row = row0 + l32;
-    if (my_row < S) {
+    if (my_row < S && tab.interleaved) {
+      // dims 32kk + 16hh .. +15 of the row; split into evens (raw[kk]) and odds
+      // (raw[kk + NKK/2]) by unpair_q once loaded
+      const __bf16 *src = p.q + (((size_t)b * S + my_row) * p.Hq + head) * D + 16 * hh;
+#pragma unroll
+      for (int kk = 0; kk < NKK / 2; ++kk) {
+        raw[kk] = *reinterpret_cast<const u32x4 *>(src + 32 * kk);
+        raw[kk + NKK / 2] = *reinterpret_cast<const u32x4 *>(src + 32 * kk + 8);
+      }
+    } else if (my_row < S) {
       const __bf16 *src = p.q + (((size_t)b * S + my_row) * p.Hq + head) * D + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) raw[kk] = *reinterpret_cast<const u32x4 *>(src + 16 * kk);
     } else {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) raw[kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // adjacent-pair rotary form: the loaded 16-dim runs become the reordered dims (see RopeTable)
+  auto unpair_q = [&](u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
+    if (tab.interleaved) {
+#pragma unroll
+      for (int kk = 0; kk < NKK / 2; ++kk) deinterleave16(raw[kk], raw[kk + NKK / 2], raw[kk], raw[kk + NKK / 2]);
     }
   };
   auto rotate_q = [&](const u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
@@ -590,11 +606,13 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       build_rot_tab(fq);
       wait_vm_all();
       __syncthreads();
+      unpair_q(raw);
       rotate_q_tab(raw, len0 > 0 ? 0 : 1);
     } else {
       if (tid < D / 2) freq[tid] = tab.rev[tid];
       wait_vm_all();
       __syncthreads();
+      unpair_q(raw);
       rotate_q(raw);
       __syncthreads();  // the frequencies (in the hand-off slot) are no longer read
     }

@@ -42,8 +42,9 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
     for (int c = 0; c < D / 2; ++c) {
       float sn, cs;
       sincos_turns(turn_fraction(p.q_pos0 + row, tab.rev[c]), &sn, &cs);
-      const float x = row < S ? src[c] : 0.f;
-      const float y = row < S ? src[c + D / 2] : 0.f;
+      // pair (c, c + D/2), or (2c, 2c + 1) in the adjacent-pair form
+      const float x = row < S ? src[rope_src_dim(c, D / 2, tab.interleaved)] : 0.f;
+      const float y = row < S ? src[rope_src_dim(c + D / 2, D / 2, tab.interleaved)] : 0.f;
       q[c] = (x * cs - y * sn) * p.q_scale;
       q[c + D / 2] = (y * cs + x * sn) * p.q_scale;
     }
@@ -65,8 +66,8 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
         for (int c = 0; c < D / 2; ++c) {
           float sn, cs;
           sincos_turns(turn_fraction(p.k_pos0 + j, tab.rev[c]), &sn, &cs);
-          const float x = j < S ? src[c] : 0.f;
-          const float y = j < S ? src[c + D / 2] : 0.f;
+          const float x = j < S ? src[rope_src_dim(c, D / 2, tab.interleaved)] : 0.f;
+          const float y = j < S ? src[rope_src_dim(c + D / 2, D / 2, tab.interleaved)] : 0.f;
           ks[t][c] = x * cs - y * sn;
           ks[t][c + D / 2] = y * cs + x * sn;
         }

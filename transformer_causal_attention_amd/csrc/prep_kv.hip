@@ -5,7 +5,9 @@
 // key position plus the row) with angle a = p * theta_i,
 //   k'_i = k_i cos a - k_{i+D/2} sin a,   k'_{i+D/2} = k_{i+D/2} cos a + k_i sin a
 // i.e. x*cos + rotate_half(x)*sin with rotate_half = cat(-x2, x1) (Picotron page, section 1),
-// theta_i = rope_theta^(-2i/D) (PaLM page, section 2.3).  Values are not rotated.
+// theta_i = rope_theta^(-2i/D) (PaLM page, section 2.3).  Values are not rotated.  In the
+// adjacent-pair form the keys are read with their dims reordered (evens, then odds) and then
+// rotated as above.
 //
 // Every query block of the attention kernel re-reads the keys and values of all earlier
 // blocks, so doing this work here once keeps the attention loop free of trigonometry and of
@@ -52,9 +54,15 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
   for (int it = 0; it < NKI; ++it) {
     const int item = tid + 256 * it;
     const int j = min(j0 + item % 64, p.S - 1);
-    const __bf16 *src = ksrc + (size_t)j * src_rs + 8 * (item / 64);
-    kl[it] = *reinterpret_cast<const u32x4 *>(src);
-    kh[it] = *reinterpret_cast<const u32x4 *>(src + D / 2);
+    if (tab.interleaved) {  // dims 16c .. 16c+15, split into evens and odds below
+      const __bf16 *src = ksrc + (size_t)j * src_rs + 16 * (item / 64);
+      kl[it] = *reinterpret_cast<const u32x4 *>(src);
+      kh[it] = *reinterpret_cast<const u32x4 *>(src + 8);
+    } else {
+      const __bf16 *src = ksrc + (size_t)j * src_rs + 8 * (item / 64);
+      kl[it] = *reinterpret_cast<const u32x4 *>(src);
+      kh[it] = *reinterpret_cast<const u32x4 *>(src + D / 2);
+    }
   }
 #pragma unroll
   for (int it = 0; it < NVI; ++it) {
@@ -86,6 +94,8 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
     const int c0 = 8 * cp;
     const int j = j0 + row;
     u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    u32x4 xk = kl[it], yk = kh[it];  // dims 8cp + e and D/2 + 8cp + e (after the reordering)
+    if (tab.interleaved) deinterleave16(kl[it], kh[it], xk, yk);
     if (j < p.S) {  // keys past S stay zero
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -93,8 +103,8 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
         const float t1 = turn_fraction(p.k_pos0 + j, freq[c0 + 2 * w + 1]);
         const float s0 = __builtin_amdgcn_sinf(t0), cs0 = __builtin_amdgcn_cosf(t0);
         const float s1 = __builtin_amdgcn_sinf(t1), cs1 = __builtin_amdgcn_cosf(t1);
-        const float x0 = bf16_lo(kl[it][w]), x1 = bf16_hi(kl[it][w]);
-        const float y0 = bf16_lo(kh[it][w]), y1 = bf16_hi(kh[it][w]);
+        const float x0 = bf16_lo(xk[w]), x1 = bf16_hi(xk[w]);
+        const float y0 = bf16_lo(yk[w]), y1 = bf16_hi(yk[w]);
         lo[w] = pack_bf16x2(x0 * cs0 - y0 * s0, x1 * cs1 - y1 * s1);
         hi[w] = pack_bf16x2(y0 * cs0 + x0 * s0, y1 * cs1 + x1 * s1);
       }
