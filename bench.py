@@ -1,6 +1,6 @@
 """Benchmark of the fused causal RoPE-GQA attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline] [--interleaved]
     python bench.py --ring N | --decode [--batch B] | --backward   (shard composition / decode / backward)
 
 A step is one attn_fwd call (key-rotation pre-pass + fused attention kernel) over the whole
@@ -37,10 +37,10 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 12448.15, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 6267.14, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 33633.96, "WRITE_SIZE_KiB": 16896.0},
-    "long_shard": {"sources_sha256": "c2258cb3437f80a7", "FETCH_SIZE_KiB": 1110042.23, "WRITE_SIZE_KiB": 266241.76},
+    "llama3_8b": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 12464.66, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 6267.64, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 33632.38, "WRITE_SIZE_KiB": 16896.0},
+    "long_shard": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 1110394.74, "WRITE_SIZE_KiB": 266241.44},
 }
 
 
@@ -80,8 +80,8 @@ def sources_sha256():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(w):
-    m = MEASURED_TRAFFIC.get(w.name)
+def measured_traffic(w, interleaved=False):
+    m = MEASURED_TRAFFIC.get(w.name + ("_interleaved" if interleaved else ""))
     if not m or m["sources_sha256"] != sources_sha256():
         return None
     return int(1024 * (m["FETCH_SIZE_KiB"] * PMC_SCALE["FETCH_SIZE"] + m["WRITE_SIZE_KiB"] * PMC_SCALE["WRITE_SIZE"]))
@@ -99,7 +99,7 @@ def copy_calibration(n_bytes=256 << 20, reps=3):
     print(json.dumps({"copy_bytes_each_way": n_bytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, budget_s=20.0, interleaved=False):
     """Time the oracle as it stands on a bounded sample of the workload (whole heads)."""
     import numpy as np
 
@@ -123,7 +123,7 @@ def cpu_baseline(w, budget_s=20.0):
         hs = slice(heads_done, heads_done + n)
         g0, g1 = heads_done // G, (heads_done + n) // G
         t0 = time.perf_counter()
-        attention(qd[:1, :, hs], kd[:1, :, g0:g1], vd[:1, :, g0:g1], w.rope_theta, w.causal)
+        attention(qd[:1, :, hs], kd[:1, :, g0:g1], vd[:1, :, g0:g1], w.rope_theta, w.causal, interleaved=interleaved)
         elapsed += time.perf_counter() - t0
         fl += flops(w.with_(B=1, Hq=n, Hkv=g1 - g0))
         heads_done += n
@@ -345,7 +345,8 @@ def backward_bench(args):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0, sigma) q/k/v and output gradient)",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
-                               f"rope_theta={w.rope_theta:g} causal={w.causal}",
+                               f"rope_theta={w.rope_theta:g} causal={w.causal}"
+                               + (" rope=interleaved" if il else ""),
                    "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
@@ -371,6 +372,8 @@ def main():
                     help="time decode steps (one query per head at position S - 1 over a full KV cache)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size (--decode)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (attn_bwd)")
+    ap.add_argument("--interleaved", action="store_true",
+                    help="forward with the adjacent-pair rotary form (rope_style ATTN_ROPE_INTERLEAVED)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention forward is a single-GPU kernel here "
@@ -404,19 +407,21 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    il = args.interleaved
     for _ in range(args.warmup):
-        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws)
+        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, interleaved=il)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, stream=stream)
+        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, stream=stream, interleaved=il)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     # second pass: the same steps, each with events bound to the attention kernel's dispatch
     evs = [(Event(), Event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, stream=stream, events=evs[i])
+        attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, stream=stream, events=evs[i],
+                      interleaved=il)
     torch.cuda.synchronize()
     kernel_ms = sum(a.elapsed_ms(b) for a, b in evs) / args.steps
 
@@ -445,13 +450,13 @@ def main():
                    "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w, il),
                      "kernel": "attn_fwd_bf16_kernel" if bf16 else "attn_fwd_f32_kernel",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": algorithmic_bytes(w),
                      "sources_sha256": sources_sha256()},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, interleaved=il)
     print(json.dumps(res), flush=True)
 
 
