@@ -1,6 +1,7 @@
 """Benchmark of the fused causal RoPE-GQA attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline] [--interleaved]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline]
+                    [--interleaved] [--non-causal]
     python bench.py --ring N | --decode [--batch B] | --backward   (shard composition / decode / backward)
 
 A step is one attn_fwd call (key-rotation pre-pass + fused attention kernel) over the whole
@@ -372,6 +373,8 @@ def main():
                     help="time decode steps (one query per head at position S - 1 over a full KV cache)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size (--decode)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (attn_bwd)")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="forward without the causal mask (every key visible; FLOPs 4 * B * Hq * S^2 * d)")
     ap.add_argument("--interleaved", action="store_true",
                     help="forward with the adjacent-pair rotary form (rope_style ATTN_ROPE_INTERLEAVED)")
     args = ap.parse_args()
@@ -399,6 +402,8 @@ def main():
     from transformer_causal_attention_amd.workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.non_causal:
+        w = w.with_(causal=False)
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in make_inputs(w))
     out = torch.empty_like(q)
@@ -450,7 +455,7 @@ def main():
                    "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w, il),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w, il) if w.causal else None,
                      "kernel": "attn_fwd_bf16_kernel" if bf16 else "attn_fwd_f32_kernel",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": algorithmic_bytes(w),
                      "sources_sha256": sources_sha256()},
