@@ -1,7 +1,7 @@
 """Benchmark of the fused causal RoPE-GQA attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b] [--no-cpu-baseline]
-                    [--interleaved] [--non-causal]
+                    [--interleaved] [--non-causal] [--cold]
     python bench.py --ring N | --decode [--batch B] | --backward   (shard composition / decode / backward)
 
 A step is one attn_fwd call (key-rotation pre-pass + fused attention kernel) over the whole
@@ -375,6 +375,9 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time the backward pass (attn_bwd)")
     ap.add_argument("--non-causal", action="store_true",
                     help="forward without the causal mask (every key visible; FLOPs 4 * B * Hq * S^2 * d)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the attention kernel with a 512 MiB scratch write before every step "
+                         "(evicts the 256 MB last-level cache), reported as roofline.cold")
     ap.add_argument("--interleaved", action="store_true",
                     help="forward with the adjacent-pair rotary form (rope_style ATTN_ROPE_INTERLEAVED)")
     args = ap.parse_args()
@@ -429,6 +432,23 @@ def main():
                       interleaved=il)
     torch.cuda.synchronize()
     kernel_ms = sum(a.elapsed_ms(b) for a, b in evs) / args.steps
+    cold = None
+    if args.cold:
+        # third pass: before each step a 512 MiB write replaces the last-level cache's contents, so
+        # the attention kernel reads q (and whatever the preparation pass did not just write)
+        # from HBM
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evc = [(Event(), Event()) for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(i & 0xFF)
+            attn_fwd_into(q, k, v, w.rope_theta, w.causal, out, lse, workspace=ws, stream=stream, events=evc[i],
+                          interleaved=il)
+        torch.cuda.synchronize()
+        cold_ms = sum(a.elapsed_ms(b) for a, b in evc) / args.steps
+        cold = {"kernel_ms": round(cold_ms, 5),
+                "achieved_TFLOPs": round(flops(w) / (cold_ms * 1e-3) / 1e12, 2),
+                "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (cold_ms * 1e-3) / 1e9, 1),
+                "flush": "512 MiB device write before each step"}
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fl = flops(w)
@@ -458,8 +478,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w, il) if w.causal else None,
                      "kernel": "attn_fwd_bf16_kernel" if bf16 else "attn_fwd_f32_kernel",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": algorithmic_bytes(w),
-                     "sources_sha256": sources_sha256()},
+                     "sources_sha256": sources_sha256(),
+                     "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (kernel_ms * 1e-3) / 1e9, 1)},
     }
+    if cold is not None:
+        res["roofline"]["cold"] = cold
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, interleaved=il)
     print(json.dumps(res), flush=True)
