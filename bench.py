@@ -346,8 +346,7 @@ def backward_bench(args):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0, sigma) q/k/v and output gradient)",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
-                               f"rope_theta={w.rope_theta:g} causal={w.causal}"
-                               + (" rope=interleaved" if il else ""),
+                               f"rope_theta={w.rope_theta:g} causal={w.causal}",
                    "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
@@ -470,7 +469,8 @@ def main():
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0, sigma) q/k/v)",
         "config": {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
-                               f"rope_theta={w.rope_theta:g} causal={w.causal}",
+                               f"rope_theta={w.rope_theta:g} causal={w.causal}"
+                               + (" rope=interleaved" if il else ""),
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "single GPU",
                    "pct_peak_bf16": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (ms_per_step * 1e-3) / 1e9, 1)},

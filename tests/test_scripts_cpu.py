@@ -1,0 +1,43 @@
+"""Static checks of the repository's scripts on the CPU: every name a function of bench.py or
+__graft_entry__.py reads as a global exists at module level or in builtins (a misspelt or
+out-of-scope name would only fail on a GPU machine), and bench.py refuses more than one GPU."""
+
+import builtins
+import os
+import subprocess
+import symtable
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def unresolved_globals(path):
+    src = open(path, encoding="utf-8").read()
+    top = symtable.symtable(src, path, "exec")
+    module_names = {s.get_name() for s in top.get_symbols() if s.is_assigned() or s.is_imported()}
+    missing = []
+
+    def walk(tab):
+        for child in tab.get_children():
+            for sym in child.get_symbols():
+                if sym.is_global() and sym.is_referenced():
+                    n = sym.get_name()
+                    if n not in module_names and not hasattr(builtins, n):
+                        missing.append((child.get_name(), n))
+            walk(child)
+
+    walk(top)
+    return missing
+
+
+@pytest.mark.parametrize("script", ["bench.py", "__graft_entry__.py"])
+def test_no_unresolved_global_names(script):
+    assert unresolved_globals(os.path.join(ROOT, script)) == []
+
+
+def test_bench_refuses_several_gpus():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
