@@ -61,7 +61,7 @@ def algorithmic_bytes(w):
 
 
 # The sources the attention kernel is compiled from.
-KERNEL_SOURCES = ("attn_device.h", "attn_fwd_bf16.hip", "attn_fwd_f32.hip")
+KERNEL_SOURCES = ("attn_device.h", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_fwd_d256.hip")
 
 
 def sources_sha256():
@@ -476,7 +476,8 @@ def main():
                    "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(w, il) if w.causal else None,
-                     "kernel": "attn_fwd_bf16_kernel" if bf16 else "attn_fwd_f32_kernel",
+                     "kernel": ("attn_fwd_d256_kernel" if w.d == 256 else "attn_fwd_bf16_kernel") if bf16
+                     else "attn_fwd_f32_kernel",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": algorithmic_bytes(w),
                      "sources_sha256": sources_sha256(),
                      "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (kernel_ms * 1e-3) / 1e9, 1)},

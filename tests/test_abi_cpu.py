@@ -65,6 +65,7 @@ def test_workspace_bytes():
     assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 2 * 64 * 64 * 2
     assert _lib.workspace_bytes(1, 64, 1, 64, 1) == 0  # fp32 needs none
     assert _lib.workspace_bytes(1, 64, 1, 96, 0) == 0  # unsupported -> 0
+    assert _lib.workspace_bytes(1, 100, 1, 256, 0) == 2 * 128 * 256 * 2  # head_dim 256 (bf16 forward)
     assert _lib.workspace_bytes(0, 64, 1, 64, 0) == 0
 
 
@@ -95,8 +96,8 @@ def test_invalid_arguments(over):
 
 
 @pytest.mark.parametrize("over", [
-    dict(d=96), dict(d=256), dict(d=32), dict(d=0), dict(dtype=2), dict(dtype=-1),
-    dict(S=(1 << 28) + 1),
+    dict(d=96), dict(d=512), dict(d=256, dtype=1), dict(d=32), dict(d=0), dict(dtype=2), dict(dtype=-1),
+    dict(S=(1 << 28) + 1), dict(d=256, S=(1 << 22) + 1),
 ])
 def test_unsupported(over):
     assert call(**over) == _lib.ATTN_EUNSUPPORTED
@@ -163,7 +164,7 @@ def test_merge_invalid_arguments(over):
     assert merge_call(**over) == _lib.ATTN_EINVAL
 
 
-@pytest.mark.parametrize("over", [dict(d=96), dict(d=256), dict(dtype=2), dict(dtype=-1)])
+@pytest.mark.parametrize("over", [dict(d=96), dict(d=512), dict(dtype=2), dict(dtype=-1)])
 def test_merge_unsupported(over):
     assert merge_call(**over) == _lib.ATTN_EUNSUPPORTED
 
@@ -195,6 +196,7 @@ def prep_call(**over):
     (dict(key0=-1), _lib.ATTN_EINVAL), (dict(key0=5, key1=5), _lib.ATTN_EINVAL),
     (dict(key1=257), _lib.ATTN_EINVAL), (dict(key0=300, key1=301), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1, key1=1), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=256), _lib.ATTN_EUNSUPPORTED),
     (dict(cb=2 * 2 * 256 * 64 * 2 - 1), _lib.ATTN_EWORKSPACE), (dict(rope=3), _lib.ATTN_EINVAL),
 ])
 def test_kv_prepare_rejections(over, code):
@@ -214,7 +216,7 @@ def decode_call(**over):
     (dict(lse=P + 1), _lib.ATTN_EINVAL), (dict(lse=None), _lib.ATTN_EINVAL),
     (dict(Hq=6, Hkv=4), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(theta=-2.0), _lib.ATTN_EINVAL),
     (dict(pos=-1), _lib.ATTN_EINVAL), (dict(pos=256), _lib.ATTN_EINVAL), (dict(rope=-1), _lib.ATTN_EINVAL),
-    (dict(d=32), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=32), _lib.ATTN_EUNSUPPORTED), (dict(d=256), _lib.ATTN_EUNSUPPORTED),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=64), _lib.ATTN_EWORKSPACE), (dict(ws=P + 4), _lib.ATTN_EWORKSPACE),
 ])
 def test_decode_rejections(over, code):
@@ -227,6 +229,7 @@ def test_bwd_workspace_bytes():
     assert _lib.bwd_workspace_bytes(2, 100, 8, 2, 128) == (3 * 2 * 2 + 4 * 2 * 8) * nb * 32 * 128 * 2 + 2 * 2 * 8 * nb * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 64) == (3 + 4 * 4) * 2 * 32 * 64 * 2 + 2 * 4 * 2 * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 96) == 0
+    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 256) == 0  # the backward covers head_dim 64 and 128
     assert _lib.bwd_workspace_bytes(1, 64, 6, 4, 64) == 0
 
 
@@ -247,6 +250,7 @@ def bwd_call(**over):
     (dict(Hq=3, Hkv=2), _lib.ATTN_EINVAL), (dict(causal=2), _lib.ATTN_EINVAL), (dict(theta=float("inf")), _lib.ATTN_EINVAL),
     (dict(rope=2), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=256), _lib.ATTN_EUNSUPPORTED),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=100), _lib.ATTN_EWORKSPACE), (dict(ws=P + 8), _lib.ATTN_EWORKSPACE),
 ])
 def test_bwd_rejections(over, code):

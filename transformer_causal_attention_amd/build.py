@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "prep_kv.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_merge.hip", "attn_decode.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "prep_kv.hip", "attn_fwd_bf16.hip", "attn_fwd_d256.hip", "attn_fwd_f32.hip", "attn_merge.hip",
+           "attn_decode.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

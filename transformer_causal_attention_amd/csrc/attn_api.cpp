@@ -29,7 +29,7 @@ int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int cau
   if (!std::isfinite(rope_theta) || rope_theta <= 0.0) return ATTN_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_EINVAL;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP32) return ATTN_EUNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128 && !(d == 256 && dtype == ATTN_DTYPE_BF16)) return ATTN_EUNSUPPORTED;
   // index arithmetic in the kernels: row/key positions in int, offsets in size_t,
   // workgroup counts below 2^31
   if (S > (1 << 28)) return ATTN_EUNSUPPORTED;
@@ -95,8 +95,13 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.delta = q_pos0 - k_pos0;
   p.q_scale = q_scale(D);
 
-  return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
-                : attn::launch_attn_bf16<D, false>(p, tab, st, e0, e1);
+  if constexpr (D == 256) {
+    p.n_row_blocks = (S + 31) / 32;  // one wave per 32 rows of one head
+    return causal ? attn::launch_attn_d256<true>(p, tab, st, e0, e1) : attn::launch_attn_d256<false>(p, tab, st, e0, e1);
+  } else {
+    return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
+                  : attn::launch_attn_bf16<D, false>(p, tab, st, e0, e1);
+  }
 }
 
 template <int D>
@@ -134,6 +139,8 @@ int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, 
   if (!rope_style_ok(rope_style)) return ATTN_EINVAL;
   const int rc = check_shape(B, S, Hq, Hkv, d, rope_theta, causal, dtype);
   if (rc != ATTN_OK) return rc;
+  // head_dim 256 addresses one (b, K/V head) run of prepared tiles with 32-bit offsets
+  if (d == 256 && (double)padded_len(S) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
   const size_t need = attn_fwd_workspace_bytes(B, S, Hkv, d, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_EWORKSPACE;
 
@@ -142,8 +149,9 @@ int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, 
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
   hipError_t err;
   if (dtype == ATTN_DTYPE_BF16)
-    err = d == 64 ? run_bf16<64>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1)
-                  : run_bf16<128>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1);
+    err = d == 64    ? run_bf16<64>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1)
+          : d == 128 ? run_bf16<128>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1)
+                     : run_bf16<256>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, workspace, st, e0, e1);
   else
     err = d == 64 ? run_f32<64>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, st, e0, e1)
                   : run_f32<128>(q, k, v, B, S, Hq, Hkv, tab, causal, q_pos0, k_pos0, out, lse, st, e0, e1);
@@ -167,7 +175,7 @@ ATTN_EXPORT const char *attn_strerror(int code) {
 
 ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype) {
   if (dtype != ATTN_DTYPE_BF16) return 0;
-  if (B < 1 || S < 1 || Hkv < 1 || (head_dim != 64 && head_dim != 128) || S > (1 << 28)) return 0;
+  if (B < 1 || S < 1 || Hkv < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256) || S > (1 << 28)) return 0;
   return 2 * (size_t)B * Hkv * padded_len(S) * head_dim * 2;  // rotated K and transposed V
 }
 
@@ -194,7 +202,7 @@ ATTN_EXPORT int attn_merge(const void *o1, const float *lse1, const void *o2, co
     return ATTN_EINVAL;
   if (B < 1 || S < 1 || H < 1) return ATTN_EINVAL;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP32) return ATTN_EUNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return ATTN_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_EUNSUPPORTED;
   const double rows = (double)B * S * H;
   if (rows * (head_dim / 4) >= 2147483647.0 * 256.0 || rows * head_dim > 4.0e15) return ATTN_EUNSUPPORTED;
   attn::MergeParams p;
@@ -210,9 +218,13 @@ ATTN_EXPORT int attn_merge(const void *o1, const float *lse1, const void *o2, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (dtype == ATTN_DTYPE_BF16)
-    err = head_dim == 64 ? attn::launch_merge<__bf16, 64>(p, st) : attn::launch_merge<__bf16, 128>(p, st);
+    err = head_dim == 64    ? attn::launch_merge<__bf16, 64>(p, st)
+          : head_dim == 128 ? attn::launch_merge<__bf16, 128>(p, st)
+                            : attn::launch_merge<__bf16, 256>(p, st);
   else
-    err = head_dim == 64 ? attn::launch_merge<float, 64>(p, st) : attn::launch_merge<float, 128>(p, st);
+    err = head_dim == 64    ? attn::launch_merge<float, 64>(p, st)
+          : head_dim == 128 ? attn::launch_merge<float, 128>(p, st)
+                            : attn::launch_merge<float, 256>(p, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -343,7 +355,7 @@ size_t bwd_blocks(int S) { return ((size_t)S + kBwdRows - 1) / kBwdRows; }
 }  // namespace
 
 ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim) {
-  if (check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
+  if (head_dim == 256 || check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
   const size_t nb = bwd_blocks(S);
   const size_t tile = (size_t)kBwdRows * head_dim * 2;
   return 3 * (size_t)B * Hkv * nb * tile + 4 * (size_t)B * Hq * nb * tile + 2 * (size_t)B * Hq * nb * kBwdRows * 4;
@@ -357,6 +369,7 @@ ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void
   for (const void *ptr : {q, k, v, out, dout, (const void *)dq, (const void *)dk, (const void *)dv})
     if (!aligned(ptr, 16)) return ATTN_EINVAL;
   if (!aligned(lse, 4) || !rope_style_ok(rope_style)) return ATTN_EINVAL;
+  if (head_dim == 256) return ATTN_EUNSUPPORTED;  // the backward kernels cover head_dim 64 and 128
   const int rc = check_shape(B, S, Hq, Hkv, head_dim, rope_theta, causal, ATTN_DTYPE_BF16);
   if (rc != ATTN_OK) return rc;
   const size_t nb = bwd_blocks(S);

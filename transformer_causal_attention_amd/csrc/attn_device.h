@@ -12,7 +12,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace attn {
 
-constexpr int kMaxHalfDim = 64;  // head_dim <= 128
+constexpr int kMaxHalfDim = 128;  // head_dim <= 256
 
 // Rotary frequencies in revolutions per position: rope_theta^(-2i/d) / (2*pi), i < d/2.
 // Computed on the host in double precision and passed by value, so every index used by

@@ -14,6 +14,11 @@ template <int D, bool CAUSAL>
 hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// head_dim 256: one wave per 32 query rows, prepared K/V streamed into registers
+template <bool CAUSAL>
+hipError_t launch_attn_d256(const FwdParams &p, const RopeTable &tab, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop);
+
 template <int D, bool CAUSAL>
 hipError_t launch_attn_f32(const F32Params &p, const RopeTable &tab, hipStream_t stream,
                            hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -54,7 +54,7 @@ __device__ __forceinline__ void store16<float>(void *p, const float (&x)[4]) {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_merge_kernel(MergeParams p) {
   constexpr int E = 16 / sizeof(T);  // elements per thread
-  constexpr int TPR = D / E;         // threads per row (16 or 32: within one wave)
+  constexpr int TPR = D / E;         // threads per row (8 to 64: within one wave)
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = t / TPR;     // (b, s, h) in the (B, S, H) order of o
   if (row >= p.rows) return;
@@ -98,5 +98,7 @@ template hipError_t launch_merge<__bf16, 64>(const MergeParams &, hipStream_t);
 template hipError_t launch_merge<__bf16, 128>(const MergeParams &, hipStream_t);
 template hipError_t launch_merge<float, 64>(const MergeParams &, hipStream_t);
 template hipError_t launch_merge<float, 128>(const MergeParams &, hipStream_t);
+template hipError_t launch_merge<__bf16, 256>(const MergeParams &, hipStream_t);
+template hipError_t launch_merge<float, 256>(const MergeParams &, hipStream_t);
 
 }  // namespace attn

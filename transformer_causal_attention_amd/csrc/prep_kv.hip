@@ -141,5 +141,6 @@ hipError_t launch_prep_kv(const PrepParams &p, const RopeTable &tab, hipStream_t
 
 template hipError_t launch_prep_kv<64>(const PrepParams &, const RopeTable &, hipStream_t);
 template hipError_t launch_prep_kv<128>(const PrepParams &, const RopeTable &, hipStream_t);
+template hipError_t launch_prep_kv<256>(const PrepParams &, const RopeTable &, hipStream_t);
 
 }  // namespace attn

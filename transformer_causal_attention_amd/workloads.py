@@ -7,8 +7,9 @@ Shapes come from the pages' models: the Llama-3-8B attention layer (32 query hea
 K/V heads, head_dim 128; llama3-from-scratch page, "model configuration parameters"), the
 PaLM multi-query default (8 heads of dim 64 sharing one K/V head, batch 8, sequence 1024;
 PaLM page, sections 2.5 and 4), a SmolLM-1.7B-shaped MHA layer at Picotron's micro-batch 4
-and sequence 1024 (Picotron page, "configuration and usage"), and a 32K-token single-GPU
-shard of a sequence-parallel run (Megatron-DeepSpeed page, "32K long-sequence training").
+and sequence 1024 (Picotron page, "configuration and usage"), a 32K-token single-GPU
+shard of a sequence-parallel run (Megatron-DeepSpeed page, "32K long-sequence training"), and
+the head size 256 of PaLM's 540B configuration (PaLM page, section 3).
 The pages train on text corpora that are not available here; attention inputs are the
 projected q/k/v activations, so seeded Gaussians of the same shapes stand in for them.
 
@@ -46,6 +47,9 @@ WORKLOADS = {
     "palm_mqa": Workload("palm_mqa", 8, 1024, 8, 1, 64, "bf16", 1.0, 10000.0, True, 3),
     "smollm_mha": Workload("smollm_mha", 4, 1024, 32, 32, 64, "bf16", 0.5, 10000.0, True, 4),
     "long_shard": Workload("long_shard", 1, 32768, 32, 8, 128, "bf16", 1.0, 500000.0, True, 5),
+    # head size of the PaLM page's largest configuration (section 3: 48 heads of 256, one
+    # shared K/V head) at the page's example sequence length
+    "palm540b_d256": Workload("palm540b_d256", 1, 2048, 48, 1, 256, "bf16", 1.0, 10000.0, True, 6),
 }
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
