@@ -96,7 +96,6 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.q_scale = q_scale(D);
 
   if constexpr (D == 256) {
-    p.n_row_blocks = (S + 31) / 32;  // one wave per 32 rows of one head
     return causal ? attn::launch_attn_d256<true>(p, tab, st, e0, e1) : attn::launch_attn_d256<false>(p, tab, st, e0, e1);
   } else {
     return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
