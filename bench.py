@@ -38,10 +38,11 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 12464.66, "WRITE_SIZE_KiB": 16640.0},
-    "palm_mqa": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 6267.64, "WRITE_SIZE_KiB": 8448.0},
-    "smollm_mha": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 33632.38, "WRITE_SIZE_KiB": 16896.0},
-    "long_shard": {"sources_sha256": "3366db718d2bca8f", "FETCH_SIZE_KiB": 1110394.74, "WRITE_SIZE_KiB": 266241.44},
+    "llama3_8b": {"sources_sha256": "77399b7543174843", "FETCH_SIZE_KiB": 12464.66, "WRITE_SIZE_KiB": 16640.0},
+    "palm_mqa": {"sources_sha256": "77399b7543174843", "FETCH_SIZE_KiB": 6267.64, "WRITE_SIZE_KiB": 8448.0},
+    "smollm_mha": {"sources_sha256": "77399b7543174843", "FETCH_SIZE_KiB": 33614.9, "WRITE_SIZE_KiB": 16896.0},
+    "long_shard": {"sources_sha256": "77399b7543174843", "FETCH_SIZE_KiB": 1110346.05, "WRITE_SIZE_KiB": 266240.86},
+    "palm540b_d256": {"sources_sha256": "c588ed9b484f859e", "FETCH_SIZE_KiB": 37930.79, "WRITE_SIZE_KiB": 49603.92},
 }
 
 
@@ -60,18 +61,19 @@ def algorithmic_bytes(w):
     return (2 * w.B * w.S * w.Hq * w.d + 2 * w.B * w.S * w.Hkv * w.d) * el + 4 * w.B * w.Hq * w.S
 
 
-# The sources the attention kernel is compiled from.
-KERNEL_SOURCES = ("attn_device.h", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_fwd_d256.hip")
+# The sources each attention kernel is compiled from (head_dim 256 has a kernel of its own).
+KERNEL_SOURCES = ("attn_device.h", "attn_fwd_bf16.hip", "attn_fwd_f32.hip")
+KERNEL_SOURCES_D256 = ("attn_device.h", "attn_fwd_d256.hip")
 
 
-def sources_sha256():
-    """Hash of the code (comments and blank space left out) of the attention kernel's sources, so
-    that stored counter readings expire when that kernel changes."""
+def sources_sha256(d=128):
+    """Hash of the code (comments and blank space left out) of the sources of the attention kernel
+    that runs head_dim d, so that stored counter readings expire when that kernel changes."""
     import hashlib
     import re
 
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES_D256 if d == 256 else KERNEL_SOURCES:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -83,7 +85,7 @@ def sources_sha256():
 
 def measured_traffic(w, interleaved=False):
     m = MEASURED_TRAFFIC.get(w.name + ("_interleaved" if interleaved else ""))
-    if not m or m["sources_sha256"] != sources_sha256():
+    if not m or m["sources_sha256"] != sources_sha256(w.d):
         return None
     return int(1024 * (m["FETCH_SIZE_KiB"] * PMC_SCALE["FETCH_SIZE"] + m["WRITE_SIZE_KiB"] * PMC_SCALE["WRITE_SIZE"]))
 
@@ -479,7 +481,7 @@ def main():
                      "kernel": ("attn_fwd_d256_kernel" if w.d == 256 else "attn_fwd_bf16_kernel") if bf16
                      else "attn_fwd_f32_kernel",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": algorithmic_bytes(w),
-                     "sources_sha256": sources_sha256(),
+                     "sources_sha256": sources_sha256(w.d),
                      "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (kernel_ms * 1e-3) / 1e9, 1)},
     }
     if cold is not None:
