@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
 // current ones; the dv kernel needs neither dP nor dout in "c" layout.
 
 template <int D, bool DV>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable tab) {
+__global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdParams p, RopeTable ta
 // dq.  One wave per (b, h, query-block pair).
 
 template <int D>
-__global__ void __launch_bounds__(64) bwd_dq_kernel(BwdParams p, RopeTable tab) {
+__global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
