@@ -58,7 +58,8 @@ extern "C" {
 #define ATTN_EINVAL (-1)       /* null or misaligned pointer, B/S/Hq/Hkv < 1, Hq % Hkv != 0,
                                   rope_theta not finite or <= 0, rope_style or causal not
                                   0/1 */
-#define ATTN_EUNSUPPORTED (-2) /* head_dim not 64 or 128, unknown dtype, sizes too large */
+#define ATTN_EUNSUPPORTED (-2) /* head_dim not supported by the call (see each call), unknown
+                                  dtype, sizes too large */
 #define ATTN_EHIP (-3)         /* the HIP runtime rejected an event record or kernel launch */
 #define ATTN_EWORKSPACE (-4)   /* workspace pointer null while needed, or workspace too small */
 
@@ -84,7 +85,8 @@ size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
  *   k, v       device, (B, S, Hkv, head_dim) contiguous, same type, 16-byte aligned
  *   B, S       batch rows and sequence length (>= 1); positions are 0 .. S-1 in every row
  *   Hq, Hkv    query heads and K/V heads; Hq must be a multiple of Hkv
- *   head_dim   64 or 128 (even, split into two rotation halves)
+ *   head_dim   64 or 128; also 256 for bf16 (the PaLM page's 540B head size, section 3),
+ *              which runs a kernel of its own (split into two rotation halves in every case)
  *   rope_theta rotary base (> 0, finite); frequencies rope_theta^(-2i/head_dim)
  *   rope_style ATTN_ROPE_HALF or ATTN_ROPE_INTERLEAVED: which dims form a rotated pair
  *   causal     1: key j is visible to query i iff j <= i;  0: every key is visible
@@ -144,7 +146,7 @@ int attn_fwd_shard(const void *q, const void *k, const void *v, int B, int S, in
  *   out may be o1 or o2 and lse may be lse1 or lse2 (in-place accumulation); other overlaps
  *   are not allowed.  Computed in float32 and rounded to nearest even into `dtype`.
  * Returns ATTN_OK, ATTN_EINVAL (null or misaligned pointer, B/S/H < 1) or ATTN_EUNSUPPORTED
- * (head_dim not 64 or 128, unknown dtype, sizes too large), ATTN_EHIP on a launch error.
+ * (head_dim not 64, 128 or 256, unknown dtype, sizes too large), ATTN_EHIP on a launch error.
  */
 int attn_merge(const void *o1, const float *lse1, const void *o2, const float *lse2, int B, int S,
                int H, int head_dim, int dtype, void *out, float *lse, void *stream);
