@@ -94,6 +94,16 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.q_pos0 = q_pos0;
   p.delta = q_pos0 - k_pos0;
   p.q_scale = q_scale(D);
+  // head_dim 64 keeps its LDS small enough for each wave group to run a unit of its own: when
+  // the (unit, pair) items outnumber the CUs, pairs of units share a workgroup and the grid runs
+  // in one round instead of two
+  p.dual = 0;
+  if (D == 64 && p.n_units % 2 == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p.dual = (long long)p.n_units * p.n_pairs > cus ? 1 : 0;
+  }
 
   if constexpr (D == 256) {
     return causal ? attn::launch_attn_d256<true>(p, tab, st, e0, e1) : attn::launch_attn_d256<false>(p, tab, st, e0, e1);

@@ -66,6 +66,7 @@ struct FwdParams {
   int q_pos0;        // position of query row 0 (a sequence shard's offset; 0 otherwise)
   int delta;         // q_pos0 - k_pos0: key j is visible to query i iff j <= i + delta (causal)
   float q_scale;     // log2(e) / sqrt(D): scores come out in the base-2 domain
+  int dual;          // head_dim 64: each workgroup runs two units (one per wave group)
 };
 
 struct F32Params {

@@ -100,7 +100,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 
 constexpr int kReadsAhead = 6;  // LDS operand reads kept in flight ahead of the MFMAs
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DUAL>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;              // MFMA steps over head_dim
   constexpr int NCB = D / 32;              // 32-column blocks of the output
@@ -124,10 +124,12 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- work: unit (b, g, head group) and row-block pair
+  // ---- work: unit (b, g, head group) and row-block pair.  With DUAL the two groups take two
+  // units (2u', 2u'+1) of the same pair and each runs the whole pair of its own unit: for grids
+  // with more (unit, pair) items than CUs, one round of workgroups instead of two.
   const int HG = p.G / p.hpw;
-  const int u = blockIdx.x % p.n_units;
-  const int pi = blockIdx.x / p.n_units;
+  const int u = DUAL ? 2 * (int)(blockIdx.x % (p.n_units / 2)) + grp : (int)(blockIdx.x % p.n_units);
+  const int pi = DUAL ? (int)(blockIdx.x / (p.n_units / 2)) : (int)(blockIdx.x / p.n_units);
   const int hg = u % HG;
   const int bg = u / HG;
   const int g = bg % p.Hkv;
@@ -152,10 +154,12 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   // the compiler copy them every step): at A's switch the tile of block r_hi's first key tile
   // also adds the P.V product of block r_lo's last one, and the last tile's P.V product is
   // added after the loop.
-  const int x = two ? (t_hi - t_lo) / 2 : t_hi / 2;  // tiles of block r_hi run by group A
-  const int len0 = (grp == 0 && two) ? t_lo : 0;
-  const int k1s = grp == 0 ? 0 : x;
-  const int n_mine = len0 + (grp == 0 ? x : t_hi - x);
+  // (DUAL: each group runs both blocks of its own unit, as group A with x = t_hi)
+  const bool runs_lo = DUAL || grp == 0;
+  const int x = DUAL ? t_hi : (two ? (t_hi - t_lo) / 2 : t_hi / 2);  // tiles of block r_hi run by group A
+  const int len0 = (runs_lo && two) ? t_lo : 0;
+  const int k1s = runs_lo ? 0 : x;
+  const int n_mine = len0 + (runs_lo ? x : t_hi - x);
   // rounded up to even (the loop body is two steps; steps after a group's last tile only wait
   // at the barrier)
   const int n_iter = (max((two ? t_lo : 0) + x, t_hi - x) + 1) & ~1;
@@ -190,6 +194,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 
   // ---- state of this wave's 32 rows
   bf16x8 qf[NKK];
+  u32x4 raw_hi[DUAL ? NKK : 1];  // DUAL: block r_hi's queries as loaded, rotated at the switch
   float m_run = 0.f;        // reference the probabilities are taken against (base-2 scores,
                             // always a bf16 value, so that the MFMA below subtracts it exactly)
   // One more k-step of the score product subtracts the reference: row k = 0 of the key operand
@@ -559,8 +564,13 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         l_lo = l_run;
         m_lo = m_run;
         seg_rows(1);
+        if constexpr (DUAL) {
+          unpair_q(raw_hi);
+          rotate_q(raw_hi);
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(q_slot() + kk * 1024);
+          for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8 *>(q_slot() + kk * 1024);
+        }
         l_run = 0.f;
         set_ref(0.f);  // provisional, replaced by the first tile's exact maximum
         cur_seg = 1;
@@ -595,12 +605,23 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         for (int z = 0; z < 2; ++z) fq[j][z] = tab.rev[tab_freq_index(j, z)];
     }
     u32x4 raw[NKK];
+    if constexpr (DUAL) {
+      if (len0 > 0) {  // block r_hi's queries come in now and wait in registers for the switch
+        seg_rows(1);
+        load_q(raw_hi);
+        seg_rows(0);
+      }
+    }
     load_q(raw);
     if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
     {
       u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
 #pragma unroll
       for (int r = 0; r < 2 * TB / 16 / 512; ++r) z1[tid + 512 * r] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // (DUAL keeps the frequencies in LDS for the rotation at the switch: no hand-off slot)
+    if (DUAL || !shared_tab) {
+      if (tid < D / 2) freq[tid] = tab.rev[tid];
     }
     if (shared_tab) {
       build_rot_tab(fq);
@@ -609,17 +630,16 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       unpair_q(raw);
       rotate_q_tab(raw, len0 > 0 ? 0 : 1);
     } else {
-      if (tid < D / 2) freq[tid] = tab.rev[tid];
       wait_vm_all();
       __syncthreads();
       unpair_q(raw);
       rotate_q(raw);
-      __syncthreads();  // the frequencies (in the hand-off slot) are no longer read
+      if (!DUAL) __syncthreads();  // the frequencies (in the hand-off slot) are no longer read
     }
     reset_seg();
-    // group A's block r_lo sees no key at all (a shard of later keys): its rows are empty
-    if (grp == 0 && two && t_lo == 0) store_seg(r_lo * RPB + sub * 32, 0.f, 0.f);
-    if (grp == 1) {
+    // block r_lo sees no key at all (a shard of later keys): its rows are empty
+    if (runs_lo && two && t_lo == 0) store_seg(r_lo * RPB + sub * 32, 0.f, 0.f);
+    if (!DUAL && grp == 1) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) *reinterpret_cast<bf16x8 *>(q_slot() + kk * 1024) = qf[kk];
     }
@@ -644,7 +664,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   // done the tile buffers are free: per-wave accumulators of group A go to ldsk0 (waves 0, 1)
   // and ldsk1 (waves 2, 3), maxima and sums to ldsv0; B's finished rows go to ldsv1.
   __syncthreads();  // every wave's last P.V product has read its V^T tile
-  if (x > 0) {
+  if (!DUAL && x > 0) {
     float *mo = reinterpret_cast<float *>(gw < 2 ? ldsk0 : ldsk1) + (gw & 1) * NCB * 16 * 64;
     float *mm = reinterpret_cast<float *>(ldsv0);
     // accumulators as [cb][v / 4][lane][v % 4]: one 16-byte access per lane and 4 registers
@@ -682,17 +702,18 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       m_run = m_new;
     }
   }
-  // Group B's rows of block r_hi leave through LDS: each wave writes its 32 rows x D output
-  // (bf16) to ldsv1 as rows of D / 8 16-byte chunks, chunk c of row r at position c ^ (r % (D / 8))
-  // (so a store instruction's 32 rows spread over the banks), and then all eight waves copy
-  // whole rows to HBM with 16-byte stores, D * 2 contiguous bytes per (row, head).
+  // Group B's rows of block r_hi (with DUAL both groups' rows, A's in ldsv0) leave through
+  // LDS: each wave writes its 32 rows x D output (bf16) to ldsv1 as rows of D / 8 16-byte chunks,
+  // chunk c of row r at position c ^ (r % (D / 8)) (so a store instruction's 32 rows spread over
+  // the banks), and then all eight waves copy whole rows to HBM with 16-byte stores, D * 2
+  // contiguous bytes per (row, head).
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int WB = 32 * D * 2;    // staged bytes per wave
-  if (grp == 1) {
+  if (DUAL || grp == 1) {
     const float l_tot = l_run + xor32(l_run);
     const int my_row = row0 + l32;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row with no visible key: out 0
-    char *st = ldsv1 + gw * WB + l32 * (D * 2) + 8 * hh;
+    char *st = (grp ? ldsv1 : ldsv0) + gw * WB + l32 * (D * 2) + 8 * hh;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -708,21 +729,36 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 16 * D / 512; ++k) {
-    const int c = tid + 512 * k;      // chunk of the 4 staged waves' rows
-    const int w = c / (4 * D), r = (c % (4 * D)) / CPR, ch = c % CPR;
-    const int row = r_hi * RPB + (w / p.hpw) * 32 + r;
-    const int hd = g * p.G + hg * p.hpw + (w % p.hpw);
-    const u32x4 val = *reinterpret_cast<const u32x4 *>(ldsv1 + w * WB + r * (D * 2) + ((ch ^ (r % CPR)) * 16));
-    if (row < S) *reinterpret_cast<u32x4 *>(p.out + (((size_t)b * S + row) * p.Hq + hd) * D + 8 * ch) = val;
+  for (int sg = DUAL ? 0 : 1; sg < 2; ++sg) {  // staged group: its unit, buffer and rows
+    const int su = DUAL ? 2 * (int)(blockIdx.x % (p.n_units / 2)) + sg : u;
+    const int shg = su % HG, sbg = su / HG;
+    const int sgk = sbg % p.Hkv, sb = sbg / p.Hkv;
+    const char *sbuf = sg ? ldsv1 : ldsv0;
+#pragma unroll
+    for (int k = 0; k < 16 * D / 512; ++k) {
+      const int c = tid + 512 * k;      // chunk of the 4 staged waves' rows
+      const int w = c / (4 * D), r = (c % (4 * D)) / CPR, ch = c % CPR;
+      const int row = r_hi * RPB + (w / p.hpw) * 32 + r;
+      const int hd = sgk * p.G + shg * p.hpw + (w % p.hpw);
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(sbuf + w * WB + r * (D * 2) + ((ch ^ (r % CPR)) * 16));
+      if (row < S) *reinterpret_cast<u32x4 *>(p.out + (((size_t)sb * S + row) * p.Hq + hd) * D + 8 * ch) = val;
+    }
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if constexpr (D == 64) {
+    if (p.dual) {  // two units per workgroup (the host checks that n_units is even)
+      const long long blocks = (long long)(p.n_units / 2) * p.n_pairs;
+      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(512), 0, stream,
+                            ev_start, ev_stop, 0, p, tab);
+      return hipGetLastError();
+    }
+  }
   const long long blocks = (long long)p.n_units * p.n_pairs;
-  hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0, stream,
+  hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)blocks), dim3(512), 0, stream,
                         ev_start, ev_stop, 0, p, tab);
   return hipGetLastError();
 }
