@@ -156,7 +156,8 @@ int attn_merge(const void *o1, const float *lse1, const void *o2, const float *l
  * token at a time; section 2.5 notes that sharing one K/V head makes that step cheaper).
  * A key/value cache of capacity S_cap keeps rotated keys and transposed values in the
  * tile layout attn_fwd prepares internally, so each new token re-prepares only its own
- * 64-key tile and attn_decode reads every cached key and value once.  bf16 only.
+ * 64-key tile and attn_decode reads every cached key and value once.  bf16 only; head_dim 64,
+ * 128 or 256.
  *
  * attn_kv_prepare: rotate keys [key0, key1) of k at their own positions and store them, with
  * the matching values, into `cache`.  Whole 64-key tiles are rewritten: the tile holding key0
@@ -168,7 +169,7 @@ int attn_merge(const void *o1, const float *lse1, const void *o2, const float *l
  *   rope_style ATTN_ROPE_HALF or ATTN_ROPE_INTERLEAVED, as for attn_fwd
  *   0 <= key0 < key1 <= S_cap
  * Returns ATTN_OK, ATTN_EINVAL (null or misaligned pointer, bad sizes or key range, theta not
- * finite and > 0, bad rope_style), ATTN_EUNSUPPORTED (head_dim not 64 or 128, sizes too large),
+ * finite and > 0, bad rope_style), ATTN_EUNSUPPORTED (head_dim not 64, 128 or 256, sizes too large),
  * ATTN_EWORKSPACE (cache too small) or ATTN_EHIP (launch error).
  */
 int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, int Hkv, int head_dim,

@@ -176,6 +176,10 @@ def test_decode_workspace_bytes():
     assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 64 * 128 * 66 * 4
     assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 256 * 128 * 66 * 4
     assert _lib.decode_workspace_bytes(2048, 8, 1, 64) == 2048 * 8 * 66 * 4  # one split
+    # head_dim 256: two-wave workgroups, so half as many splits (512 workgroups)
+    assert _lib.decode_workspace_bytes(1, 48, 1, 256) == 48 * 256 * 258 * 4
+    assert _lib.decode_workspace_bytes(4, 16, 16, 128) == 64 * 16 * 130 * 4
+    assert _lib.decode_workspace_bytes(4, 16, 16, 256) == 64 * 8 * 258 * 4
     assert _lib.decode_workspace_bytes(1, 32, 8, 96) == 0
     assert _lib.decode_workspace_bytes(1, 6, 4, 64) == 0
     assert _lib.decode_workspace_bytes(0, 8, 1, 64) == 0
@@ -196,7 +200,7 @@ def prep_call(**over):
     (dict(key0=-1), _lib.ATTN_EINVAL), (dict(key0=5, key1=5), _lib.ATTN_EINVAL),
     (dict(key1=257), _lib.ATTN_EINVAL), (dict(key0=300, key1=301), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1, key1=1), _lib.ATTN_EUNSUPPORTED),
-    (dict(d=256), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=512), _lib.ATTN_EUNSUPPORTED), (dict(d=256, S=(1 << 22) + 1, key1=1), _lib.ATTN_EUNSUPPORTED),
     (dict(cb=2 * 2 * 256 * 64 * 2 - 1), _lib.ATTN_EWORKSPACE), (dict(rope=3), _lib.ATTN_EINVAL),
 ])
 def test_kv_prepare_rejections(over, code):
@@ -216,7 +220,8 @@ def decode_call(**over):
     (dict(lse=P + 1), _lib.ATTN_EINVAL), (dict(lse=None), _lib.ATTN_EINVAL),
     (dict(Hq=6, Hkv=4), _lib.ATTN_EINVAL), (dict(B=0), _lib.ATTN_EINVAL), (dict(theta=-2.0), _lib.ATTN_EINVAL),
     (dict(pos=-1), _lib.ATTN_EINVAL), (dict(pos=256), _lib.ATTN_EINVAL), (dict(rope=-1), _lib.ATTN_EINVAL),
-    (dict(d=32), _lib.ATTN_EUNSUPPORTED), (dict(d=256), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=32), _lib.ATTN_EUNSUPPORTED), (dict(d=512), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=256, wsb=64), _lib.ATTN_EWORKSPACE),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=64), _lib.ATTN_EWORKSPACE), (dict(ws=P + 4), _lib.ATTN_EWORKSPACE),
 ])
 def test_decode_rejections(over, code):

@@ -52,6 +52,8 @@ SHAPES = [
     (2, 300, 8, 2, 128, 10000.0),     # ragged capacity
     (1, 200, 128, 2, 64, 10000.0),    # 64 heads per K/V head: two head blocks
     (3, 130, 40, 1, 128, 10000.0),    # 40 heads on one K/V head: a partial head block
+    (2, 1500, 48, 1, 256, 10000.0),   # PaLM-540B heads: 48 on one K/V head, head_dim 256
+    (2, 300, 8, 2, 256, 10000.0),     # head_dim 256, grouped
 ]
 
 
@@ -95,10 +97,11 @@ def test_decode_incremental_append():
             check_row(q, k, v, w, pos, out, lse, f"{w} append {pos}")
 
 
-def test_decode_matches_forward_rows():
+@pytest.mark.parametrize("d", [64, 256])
+def test_decode_matches_forward_rows(d):
     """Decode at every position of a short sequence equals the forward's rows (both bf16
     paths against each other, within twice the oracle tolerance)."""
-    B, S, Hq, Hkv, d = 1, 130, 8, 2, 64
+    B, S, Hq, Hkv = 1, 130, 8, 2
     w = w_of(B, S, Hq, Hkv, d, seed=21)
     q, k, v = make_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -116,7 +119,7 @@ def test_decode_matches_forward_rows():
     assert worst <= 2 * TOL
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_decode_staircase_scores(d):
     """Every 64-key tile scores about 68 (natural units) above the one before, so each tile and
     each key split is rescaled by its successor.  Inputs sit in the lowest-frequency rotation

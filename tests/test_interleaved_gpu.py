@@ -97,7 +97,7 @@ def test_shard_offsets(dtype):
         assert eo <= TOL[dtype] and el <= TOL[dtype]
 
 
-@pytest.mark.parametrize("shape", [(1, 300, 8, 2, 128), (2, 130, 8, 1, 64)], ids=lambda s: "B{}S{}H{}/{}d{}".format(*s))
+@pytest.mark.parametrize("shape", [(1, 300, 8, 2, 128), (2, 130, 8, 1, 64), (1, 260, 48, 1, 256)], ids=lambda s: "B{}S{}H{}/{}d{}".format(*s))
 def test_decode(shape):
     B, S, Hq, Hkv, d = shape
     w = w_of(B, S, Hq, Hkv, d, "bf16", seed=S)

@@ -253,22 +253,23 @@ ATTN_EXPORT void *attn_event_create(void) {
 
 namespace {
 
-// Decode splits: about kDecodeWaves one-wave workgroups over (b, K/V head, head block, key
-// range), i.e. four per CU, one per SIMD, and at least kDecodeMinHalves 32-key half tiles per
-// key range so that each wave's loads fill its pipeline.
+// Decode splits: about kDecodeWaves waves over (b, K/V head, head block, key range), i.e. four
+// per CU, one per SIMD, and at least kDecodeMinHalves 32-key half tiles per key range so that
+// each wave's loads fill its pipeline.  A workgroup is one wave, two at head_dim 256.
 constexpr int kDecodeWaves = 1024;
 constexpr int kDecodeMinHalves = 4;
 
 int decode_hblk(int G) { return (G + 31) / 32; }
 
-int decode_max_splits(int B, int Hkv, int G) {
+int decode_max_splits(int B, int Hkv, int G, int d) {
   const long long units = (long long)B * Hkv * decode_hblk(G);
-  return (int)std::max<long long>(1, (kDecodeWaves + units - 1) / units);
+  const long long wgs = kDecodeWaves / (d == 256 ? 2 : 1);
+  return (int)std::max<long long>(1, (wgs + units - 1) / units);
 }
 
 int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
   if (B < 1 || S_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_EINVAL;
-  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_EUNSUPPORTED;
   if (S_cap > (1 << 28) || (double)Hkv * d > (double)(1 << 24)) return ATTN_EUNSUPPORTED;
   // one (b, g) tile run of the cache is addressed with 32-bit offsets
   if ((double)padded_len(S_cap) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
@@ -304,13 +305,15 @@ ATTN_EXPORT int attn_kv_prepare(const void *k, const void *v, int B, int S_cap, 
   pp.k_pos0 = 0;
   const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t err = head_dim == 64 ? attn::launch_prep_kv<64>(pp, tab, st) : attn::launch_prep_kv<128>(pp, tab, st);
+  const hipError_t err = head_dim == 64    ? attn::launch_prep_kv<64>(pp, tab, st)
+                         : head_dim == 128 ? attn::launch_prep_kv<128>(pp, tab, st)
+                                           : attn::launch_prep_kv<256>(pp, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
 ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim) {
   if (check_decode_shape(B, 1, Hq, Hkv, head_dim) != ATTN_OK) return 0;
-  const size_t rows = (size_t)B * Hq * decode_max_splits(B, Hkv, Hq / Hkv);
+  const size_t rows = (size_t)B * Hq * decode_max_splits(B, Hkv, Hq / Hkv, head_dim);
   return rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
@@ -341,7 +344,7 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, 
   p.q_pos = q_pos;
   p.n_hblk = decode_hblk(G);
   const int halves = (q_pos + 1 + 31) / 32;
-  const int max_split = std::max(1, std::min(decode_max_splits(B, Hkv, G), halves / kDecodeMinHalves));
+  const int max_split = std::max(1, std::min(decode_max_splits(B, Hkv, G, head_dim), halves / kDecodeMinHalves));
   p.halves_per_split = (halves + max_split - 1) / max_split;
   p.n_split = (halves + p.halves_per_split - 1) / p.halves_per_split;
   const size_t rows = (size_t)B * Hq * p.n_split;
@@ -351,7 +354,9 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, 
   p.q_scale = q_scale(head_dim);
   const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t err = head_dim == 64 ? attn::launch_decode<64>(p, tab, st) : attn::launch_decode<128>(p, tab, st);
+  const hipError_t err = head_dim == 64    ? attn::launch_decode<64>(p, tab, st)
+                         : head_dim == 128 ? attn::launch_decode<128>(p, tab, st)
+                                           : attn::launch_decode<256>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

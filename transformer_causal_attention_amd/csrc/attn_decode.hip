@@ -14,9 +14,13 @@
 // split over waves (split-K); each leaves a partial (o, m, l) for its keys, and a second kernel
 // joins the partials by their maxima.
 //
-// A workgroup is one wave holding the (up to) 32 query heads of a head block, the G heads that
-// share the K/V head, 32 at a time, as the columns of the MFMA operand Q^T: S^T = K Q^T puts one
-// head per lane and each loaded half tile serves every head of the block.
+// A workgroup holds the (up to) 32 query heads of a head block, the G heads that share the K/V
+// head, 32 at a time, as the columns of the MFMA operand Q^T: S^T = K Q^T puts one head per lane
+// and each loaded half tile serves every head of the block.  Up to head_dim 128 the workgroup is
+// one wave.  At head_dim 256 the operands of one wave would not fit its registers, so the
+// workgroup is two waves that split the dimensions: each takes half of the rotary pairs for the
+// scores and half of the value columns for the output, the two partial score tiles are added
+// through LDS, and both waves then run the same softmax on the same sums.
 
 #include "attn_device.h"
 
@@ -50,21 +54,43 @@ __device__ __forceinline__ f32x16 dec_mfma(const bf16x8 &a, const bf16x8 &b, con
 }  // namespace
 
 template <int D, int PD>
-__global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTable tab) {
-  constexpr int NKK = D / 16;
-  constexpr int NCB = D / 32;
-  constexpr int TB = DBN * D * 2;  // bytes of one K or V^T tile
+__global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(DecodeParams p, RopeTable tab) {
+  constexpr int NW = D == 256 ? 2 : 1;  // waves per workgroup, splitting the dimensions
+  constexpr int NKK = D / 16;           // k-steps of the full score product
+  constexpr int NKW = NKK / NW;         // k-steps of this wave: NKW / 2 rotary pairs of chunks
+  constexpr int NCB = D / 32 / NW;      // output column blocks of this wave
+  constexpr int TB = DBN * D * 2;       // bytes of one K or V^T tile
+  // partial score tiles of the two waves, double-buffered: [buffer][wave][quad][lane][4]
+  __shared__ __attribute__((aligned(16))) float xs[NW > 1 ? 2 : 1][NW][4][64][4];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  // chunk pair j of this wave (j < NKW / 2) is the full product's pair wv * NKW / 2 + j; its two
+  // chunks are k-steps kk_of(j) and kk_of(j) + NKK / 2 (the dimensions a rotation mixes)
+  auto kk_of = [&](int j) __attribute__((always_inline)) {
+    return (j / (NKW / 2)) * (NKK / 2) + wv * (NKW / 2) + j % (NKW / 2);
+  };
 
-  // workgroup -> (b, g, head block, split)
-  int w = blockIdx.x;
+  // workgroup -> (key range u = (b, g, split), head block).  With one head block, u is the
+  // workgroup index.  With several, the head blocks of one key range read the same tiles: the
+  // workgroups are dealt to the 8 XCDs round robin (workgroup i to XCD i % 8), so u's head
+  // blocks are given indices 8 apart, i.e. neighbours on one XCD, and all but the first read
+  // the tiles from that XCD's L2.  The grid is rounded up to whole groups of 8 key ranges and
+  // the workgroups past the last range leave at once (before any barrier).
+  int w, hb;
+  if (p.n_hblk == 1) {
+    w = blockIdx.x;
+    hb = 0;
+  } else {
+    const int j = blockIdx.x / 8;
+    hb = j % p.n_hblk;
+    w = 8 * (j / p.n_hblk) + blockIdx.x % 8;
+    if (w >= p.B * p.Hkv * p.n_split) return;
+  }
   const int split = w % p.n_split;
   w /= p.n_split;
-  const int hb = w % p.n_hblk;
-  w /= p.n_hblk;
   const int g = w % p.Hkv;
   const int b = w / p.Hkv;
 
@@ -74,28 +100,29 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   const int key_end = min(key_end0, 32 * h_end);  // first key past this split's range
 
   // Q^T operand: lane l holds head column l % 32 (zeros past the group), dimensions 16kk + 8hh
-  // + e, rotated at q_pos and scaled by log2(e)/sqrt(D).  Loaded before the cache so that the
-  // rotation only waits for these loads.
+  // + e of this wave's k-steps, rotated at q_pos and scaled by log2(e)/sqrt(D).  Loaded before
+  // the cache so that the rotation only waits for these loads.
   const int hc = hb * 32 + l32;  // head within the group
   const bool head_ok = hc < p.G;
   const int head = g * p.G + hc;
-  u32x4 raw[NKK];
+  u32x4 raw[NKW];
   {
     if (tab.interleaved) {
       // adjacent-pair rotary form: dims 32kk + 16hh .. +15, split into evens and odds (the
       // reordered dims 16kk + 8hh + e and D/2 + 16kk + 8hh + e)
       const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 16 * hh;
 #pragma unroll
-      for (int kk = 0; kk < NKK / 2; ++kk) {
+      for (int j = 0; j < NKW / 2; ++j) {
+        const int kk = kk_of(j);
         const u32x4 lo = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
         const u32x4 hi = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk + 8) : u32x4{0u, 0u, 0u, 0u};
-        deinterleave16(lo, hi, raw[kk], raw[kk + NKK / 2]);
+        deinterleave16(lo, hi, raw[j], raw[j + NKW / 2]);
       }
     } else {
       const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 8 * hh;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        raw[kk] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NKW; ++j)
+        raw[j] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk_of(j)) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -111,19 +138,20 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   // half tile h = 2t + jb: keys 64t + 32jb .. +31.  K operand chunk kk: [chunk 2kk+hh][key][8];
   // V^T operand (tt, cb): key group 4jb + 2tt + hh, column 32cb + l32.
   const int k_lane = hh * 1024 + l32 * 16;
-  const int v_lane = hh * 16 * D + l32 * 16;
+  const int v_lane = hh * 16 * D + l32 * 16 + wv * NCB * 512;
   auto half_base = [&](int h) __attribute__((always_inline)) {
     return h < h_end ? (h >> 1) * TB + (h & 1) * 512 : kPastEnd;
   };
   auto half_vbase = [&](int h) __attribute__((always_inline)) {
     return h < h_end ? (h >> 1) * TB + (h & 1) * 4 * 16 * D : kPastEnd;
   };
-  bf16x8 kq[PD][NKK], vq[PD][2][NCB];
+  bf16x8 kq[PD][NKW], vq[PD][2][NCB];
   auto load_half = [&](int h, int r) __attribute__((always_inline)) {
     const int kb = half_base(h), vb = half_vbase(h);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      kq[r][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kbuf, kb + k_lane + kk * 2048, 0, 0));
+    for (int j = 0; j < NKW; ++j)
+      kq[r][j] =
+          __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kbuf, kb + k_lane + kk_of(j) * 2048, 0, 0));
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -134,29 +162,30 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
 #pragma unroll
   for (int r = 0; r < PD; ++r) load_half(h_begin + r, r);
 
-  bf16x8 qf[NKK];
+  bf16x8 qf[NKW];
 #pragma unroll
-  for (int kk = 0; kk < NKK / 2; ++kk) {
+  for (int j = 0; j < NKW / 2; ++j) {
+    const int kk = kk_of(j);
     u32x4 olo, ohi;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) {
+    for (int ww = 0; ww < 4; ++ww) {
       float r[2][2];
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
-        const int e = 2 * wv + z;
+        const int e = 2 * ww + z;
         const float t = turn_fraction(p.q_pos, tab.rev[16 * kk + 8 * hh + e]);
         const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);  // turns
-        const uint32_t lo = raw[kk][wv], hi = raw[kk + NKK / 2][wv];
+        const uint32_t lo = raw[j][ww], hi = raw[j + NKW / 2][ww];
         const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
         const float yv = z ? bf16_hi(hi) : bf16_lo(hi);
         r[0][z] = (xv * cs - yv * sn) * p.q_scale;
         r[1][z] = (yv * cs + xv * sn) * p.q_scale;
       }
-      olo[wv] = pack_bf16x2(r[0][0], r[0][1]);
-      ohi[wv] = pack_bf16x2(r[1][0], r[1][1]);
+      olo[ww] = pack_bf16x2(r[0][0], r[0][1]);
+      ohi[ww] = pack_bf16x2(r[1][0], r[1][1]);
     }
-    qf[kk] = __builtin_bit_cast(bf16x8, olo);
-    qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, ohi);
+    qf[j] = __builtin_bit_cast(bf16x8, olo);
+    qf[j + NKW / 2] = __builtin_bit_cast(bf16x8, ohi);
   }
 
   f32x16 o[NCB];
@@ -166,7 +195,8 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   float l_run = 0.f;        // this lane half's share of the running sum
 
   // Steps past h_end (padding to a multiple of PD) load zeros and have every key masked, so the
-  // loop body needs no branch around its loads.
+  // loop body needs no branch around its loads.  Both waves of a workgroup see the same key
+  // range, so they meet at the same barriers.
   const int n_steps = (h_end - h_begin + PD - 1) / PD * PD;
   for (int s0 = 0; s0 < n_steps; s0 += PD) {
 #pragma unroll
@@ -174,7 +204,24 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
       const int h = h_begin + s0 + r;
       f32x16 sc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) sc = dec_mfma(kq[r][kk], qf[kk], sc);
+      for (int j = 0; j < NKW; ++j) sc = dec_mfma(kq[r][j], qf[j], sc);
+      if constexpr (NW > 1) {
+        // add the other wave's partial scores; the buffer alternates with the step, so a write
+        // of the next step cannot overtake the other wave's read of this one (it has passed the
+        // next barrier only after that read)
+        const int buf = (s0 + r) & 1;
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          *reinterpret_cast<f32x4 *>(xs[buf][wv][v4][lane]) =
+              f32x4{sc[4 * v4], sc[4 * v4 + 1], sc[4 * v4 + 2], sc[4 * v4 + 3]};
+        __syncthreads();
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(xs[buf][wv ^ 1][v4][lane]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * v4 + e] += t[e];
+        }
+      }
       // keys of this half: 32h + 8(v>>2) + 4hh + (v&3)
       if (32 * h + 31 >= key_end) {
 #pragma unroll
@@ -218,7 +265,7 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
   // m and l per head
   if (head_ok) {
     const size_t prow = (unit * p.n_split + split) * p.G + hc;
-    float *po = p.po + prow * D;
+    float *po = p.po + prow * D + wv * NCB * 32;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -227,7 +274,7 @@ __global__ void __launch_bounds__(64) attn_decode_kernel(DecodeParams p, RopeTab
             f32x4{o[cb][4 * v4], o[cb][4 * v4 + 1], o[cb][4 * v4 + 2], o[cb][4 * v4 + 3]};
   }
   const float l_tot = l_run + dec_xor32(l_run);
-  if (hh == 0 && head_ok) {
+  if (wv == 0 && hh == 0 && head_ok) {  // both waves hold the same m and l
     const size_t prow = (unit * p.n_split + split) * p.G + hc;
     p.pm[prow] = m_run;
     p.pl[prow] = l_tot;
@@ -291,8 +338,10 @@ __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_decode(const DecodeParams &p, const RopeTable &tab, hipStream_t stream) {
-  const long long wgs = (long long)p.B * p.Hkv * p.n_hblk * p.n_split;
-  hipLaunchKernelGGL((attn_decode_kernel<D, kDecodeDepth>), dim3((unsigned)wgs), dim3(64), 0, stream, p, tab);
+  const long long ranges = (long long)p.B * p.Hkv * p.n_split;
+  const long long wgs = p.n_hblk == 1 ? ranges : (ranges + 7) / 8 * 8 * p.n_hblk;
+  hipLaunchKernelGGL((attn_decode_kernel<D, kDecodeDepth>), dim3((unsigned)wgs), dim3(D == 256 ? 128 : 64), 0, stream,
+                     p, tab);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(attn_decode_join_kernel<D>, dim3((unsigned)((long long)p.B * p.Hq)), dim3(256), 0, stream, p);
@@ -301,5 +350,6 @@ hipError_t launch_decode(const DecodeParams &p, const RopeTable &tab, hipStream_
 
 template hipError_t launch_decode<64>(const DecodeParams &, const RopeTable &, hipStream_t);
 template hipError_t launch_decode<128>(const DecodeParams &, const RopeTable &, hipStream_t);
+template hipError_t launch_decode<256>(const DecodeParams &, const RopeTable &, hipStream_t);
 
 }  // namespace attn
