@@ -283,13 +283,15 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
 
 // Joins the splits of every (b, head): m = max m_i, l = sum l_i 2^(m_i - m),
 // out = sum o_i 2^(m_i - m) / l (bf16), lse = ln 2 * (m + log2 l).  One 256-thread workgroup
-// per (b, head): the n_split partial rows are read in parallel, R = 256 / (D/4) rows at a time
-// with D/4 threads (16 bytes each) per row, and the R partial sums are added through LDS.
+// per (b, head): R = 256 / (D/4) row groups of D/4 threads (16 bytes of a row each) take the
+// splits sg, sg + R, ..., each group merging its rows with a running maximum, so that m, l and
+// o of a row are loaded together (one trip to memory when n_split <= R); the R partial results
+// are then joined by their maxima through LDS.
 template <int D>
 __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
   constexpr int TPR = D / 4;      // threads per partial row
-  constexpr int R = 256 / TPR;    // rows read at once
-  __shared__ float red_m[4];
+  constexpr int R = 256 / TPR;    // row groups
+  __shared__ float red_m[R];
   __shared__ float red_l[R];
   __shared__ __attribute__((aligned(16))) float red_o[R][D];
   const int tid = threadIdx.x;
@@ -301,38 +303,43 @@ __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
   const size_t unit = (size_t)b * p.Hkv + g;
   auto row = [&](int s) __attribute__((always_inline)) { return (unit * p.n_split + s) * p.G + hc; };
 
-  float m = -INFINITY;
-  for (int s = tid; s < p.n_split; s += 256) m = fmaxf(m, p.pm[row(s)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) red_m[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
   const int sg = tid / TPR;  // row group
   const int c4 = tid % TPR;  // dimensions 4 c4 .. 4 c4 + 3
+  // every split has a visible key (its first), so each m_i is finite; a group without rows
+  // keeps m = -inf and contributes 2^(-inf) = 0 below
+  float m = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
   for (int s = sg; s < p.n_split; s += R) {
     const size_t r = row(s);
-    const float c = __builtin_amdgcn_exp2f(p.pm[r] - m);
-    acc += *reinterpret_cast<const f32x4 *>(p.po + r * D + 4 * c4) * c;
-    l += p.pl[r] * c;
+    const float ms = p.pm[r], ls = p.pl[r];
+    const f32x4 os = *reinterpret_cast<const f32x4 *>(p.po + r * D + 4 * c4);
+    const float mn = fmaxf(m, ms);
+    const float a = __builtin_amdgcn_exp2f(m - mn), c = __builtin_amdgcn_exp2f(ms - mn);
+    acc = acc * a + os * c;
+    l = l * a + ls * c;
+    m = mn;
   }
   *reinterpret_cast<f32x4 *>(&red_o[sg][4 * c4]) = acc;
-  if (c4 == 0) red_l[sg] = l;
+  if (c4 == 0) {
+    red_m[sg] = m;
+    red_l[sg] = l;
+  }
   __syncthreads();
   if (tid < D / 2) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < R; ++i) mt = fmaxf(mt, red_m[i]);
     float o0 = 0.f, o1 = 0.f, lt = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      o0 += red_o[i][2 * tid];
-      o1 += red_o[i][2 * tid + 1];
-      lt += red_l[i];
+      const float c = __builtin_amdgcn_exp2f(red_m[i] - mt);
+      o0 += red_o[i][2 * tid] * c;
+      o1 += red_o[i][2 * tid + 1] * c;
+      lt += red_l[i] * c;
     }
     const float inv = 1.0f / lt;
     *reinterpret_cast<uint32_t *>(p.out + ((size_t)b * p.Hq + head) * D + 2 * tid) = pack_bf16x2(o0 * inv, o1 * inv);
-    if (tid == 0) p.lse[(size_t)b * p.Hq + head] = (m + __log2f(lt)) * 0.69314718055994531f;
+    if (tid == 0) p.lse[(size_t)b * p.Hq + head] = (mt + __log2f(lt)) * 0.69314718055994531f;
   }
 }
 
