@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
   __shared__ __attribute__((aligned(16))) float xs[NW > 1 ? 2 : 1][NW][4][64][4];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   // chunk pair j of this wave (j < NKW / 2) is the full product's pair wv * NKW / 2 + j; its two
@@ -105,26 +105,29 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
   const int hc = hb * 32 + l32;  // head within the group
   const bool head_ok = hc < p.G;
   const int head = g * p.G + hc;
+  // Lanes past the group load head 0 of the row (in bounds) and compute with it: every value a
+  // lane holds belongs to its own head column, and those columns are never written.  The loads
+  // are not consumed before the cache loads are issued, so the rotation's wait counts them
+  // alone.
   u32x4 raw[NKW];
   {
+    const int row_head = head_ok ? head : 0;
     if (tab.interleaved) {
-      // adjacent-pair rotary form: dims 32kk + 16hh .. +15, split into evens and odds (the
-      // reordered dims 16kk + 8hh + e and D/2 + 16kk + 8hh + e)
-      const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 16 * hh;
+      // adjacent-pair rotary form: dims 32kk + 16hh .. +15 (two 16-byte runs, split into evens
+      // and odds after the cache loads are issued)
+      const __bf16 *src = p.q + ((size_t)b * p.Hq + row_head) * D + 16 * hh;
 #pragma unroll
       for (int j = 0; j < NKW / 2; ++j) {
-        const int kk = kk_of(j);
-        const u32x4 lo = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 hi = head_ok ? *reinterpret_cast<const u32x4 *>(src + 32 * kk + 8) : u32x4{0u, 0u, 0u, 0u};
-        deinterleave16(lo, hi, raw[j], raw[j + NKW / 2]);
+        raw[j] = *reinterpret_cast<const u32x4 *>(src + 32 * kk_of(j));
+        raw[j + NKW / 2] = *reinterpret_cast<const u32x4 *>(src + 32 * kk_of(j) + 8);
       }
     } else {
-      const __bf16 *src = p.q + ((size_t)b * p.Hq + (head_ok ? head : 0)) * D + 8 * hh;
+      const __bf16 *src = p.q + ((size_t)b * p.Hq + row_head) * D + 8 * hh;
 #pragma unroll
-      for (int j = 0; j < NKW; ++j)
-        raw[j] = head_ok ? *reinterpret_cast<const u32x4 *>(src + 16 * kk_of(j)) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NKW; ++j) raw[j] = *reinterpret_cast<const u32x4 *>(src + 16 * kk_of(j));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // the query loads go out before the cache's
 
   // The (b, g) run of tiles as buffer resources: a load whose (per-lane) offset lies past the
   // end returns zeros without a memory access, which is how the padded steps after h_end read
@@ -159,9 +162,23 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
         vq[r][tt][cb] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vbuf, vb + v_lane + tt * 2 * 16 * D + cb * 512, 0, 0));
   };
+  // The loop's first wait is shared by its entry and its back edge, so the entry issues the
+  // half tiles in the loop's order, each behind a scheduling barrier: left to the scheduler,
+  // half 0's first operand can be issued last, and that wait then drains every load.
 #pragma unroll
-  for (int r = 0; r < PD; ++r) load_half(h_begin + r, r);
+  for (int r = 0; r < PD; ++r) {
+    load_half(h_begin + r, r);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
+  if (tab.interleaved) {
+    // the evens are the reordered dims 16kk + 8hh + e, the odds D/2 + 16kk + 8hh + e
+#pragma unroll
+    for (int j = 0; j < NKW / 2; ++j) {
+      const u32x4 lo = raw[j], hi = raw[j + NKW / 2];
+      deinterleave16(lo, hi, raw[j], raw[j + NKW / 2]);
+    }
+  }
   bf16x8 qf[NKW];
 #pragma unroll
   for (int j = 0; j < NKW / 2; ++j) {
@@ -173,7 +190,10 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
         const int e = 2 * ww + z;
-        const float t = turn_fraction(p.q_pos, tab.rev[16 * kk + 8 * hh + e]);
+        // both lane halves' frequencies at wave-uniform indices (scalar loads, which the
+        // cache loads in flight do not hold up), then this lane's
+        const double f0 = tab.rev[16 * kk + e], f1 = tab.rev[16 * kk + 8 + e];
+        const float t = turn_fraction(p.q_pos, hh ? f1 : f0);
         const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);  // turns
         const uint32_t lo = raw[j][ww], hi = raw[j + NKW / 2][ww];
         const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
