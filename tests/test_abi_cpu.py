@@ -171,13 +171,15 @@ def test_merge_unsupported(over):
 
 def test_decode_workspace_bytes():
     # partial (o, m, l) float32 rows: B * Hq heads * splits, with
-    # splits = ceil(1024 / (B * Hkv * ceil(G / 32))) at most
-    assert _lib.decode_workspace_bytes(1, 32, 8, 128) == 32 * 128 * 130 * 4
-    assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 64 * 128 * 66 * 4
-    assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 256 * 128 * 66 * 4
+    # splits = min(64, ceil(1024 / (B * Hkv * ceil(G / 32)))) at most
+    assert _lib.decode_workspace_bytes(1, 32, 8, 128) == 32 * 64 * 130 * 4
+    assert _lib.decode_workspace_bytes(8, 8, 1, 64) == 64 * 64 * 66 * 4
+    assert _lib.decode_workspace_bytes(4, 32, 8, 128) == 128 * 32 * 130 * 4  # below the cap
+    assert _lib.decode_workspace_bytes(2, 128, 2, 64) == 256 * 64 * 66 * 4  # 2 head blocks: 8 units
     assert _lib.decode_workspace_bytes(2048, 8, 1, 64) == 2048 * 8 * 66 * 4  # one split
     # head_dim 256: two-wave workgroups, so half as many splits (512 workgroups)
-    assert _lib.decode_workspace_bytes(1, 48, 1, 256) == 48 * 256 * 258 * 4
+    assert _lib.decode_workspace_bytes(1, 48, 1, 256) == 48 * 64 * 258 * 4  # capped at 64
+    assert _lib.decode_workspace_bytes(16, 48, 1, 256) == 16 * 48 * 16 * 258 * 4
     assert _lib.decode_workspace_bytes(4, 16, 16, 128) == 64 * 16 * 130 * 4
     assert _lib.decode_workspace_bytes(4, 16, 16, 256) == 64 * 8 * 258 * 4
     assert _lib.decode_workspace_bytes(1, 32, 8, 96) == 0

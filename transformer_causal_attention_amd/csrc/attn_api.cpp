@@ -254,17 +254,21 @@ ATTN_EXPORT void *attn_event_create(void) {
 namespace {
 
 // Decode splits: about kDecodeWaves waves over (b, K/V head, head block, key range), i.e. four
-// per CU, one per SIMD, and at least kDecodeMinHalves 32-key half tiles per key range so that
-// each wave's loads fill its pipeline.  A workgroup is one wave, two at head_dim 256.
+// per CU, one per SIMD, at least kDecodeMinHalves 32-key half tiles per key range so that each
+// wave's loads fill its pipeline, and at most kDecodeMaxSplits ranges per (b, K/V head, head
+// block), past which the join's rows and the ranges' start-up cost more than the extra waves
+// gain (measured: a 32K cache at batch 1 and Llama-3-8B heads decodes faster with 64 ranges of
+// 512 keys than with 128 of 256).  A workgroup is one wave, two at head_dim 256.
 constexpr int kDecodeWaves = 1024;
 constexpr int kDecodeMinHalves = 4;
+constexpr int kDecodeMaxSplits = 64;
 
 int decode_hblk(int G) { return (G + 31) / 32; }
 
 int decode_max_splits(int B, int Hkv, int G, int d) {
   const long long units = (long long)B * Hkv * decode_hblk(G);
   const long long wgs = kDecodeWaves / (d == 256 ? 2 : 1);
-  return (int)std::max<long long>(1, (wgs + units - 1) / units);
+  return (int)std::max<long long>(1, std::min<long long>(kDecodeMaxSplits, (wgs + units - 1) / units));
 }
 
 int check_decode_shape(int B, int S_cap, int Hq, int Hkv, int d) {
