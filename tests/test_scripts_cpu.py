@@ -41,3 +41,18 @@ def test_bench_refuses_several_gpus():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_cpu_baseline_record():
+    """The oracle's timing record: its fields, a positive rate, and a sample description that
+    counts the whole passes over the row when one pass is shorter than the budget."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from transformer_causal_attention_amd.workloads import Workload
+
+    w = Workload("tiny", 1, 96, 4, 2, 64, "bf16", 1.0, 10000.0, True, 1)
+    r = bench.cpu_baseline(w, budget_s=0.4)
+    assert set(r) == {"value", "unit", "cores", "kind", "sample", "seconds"}
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
+    assert r["value"] > 0 and r["seconds"] >= 0.2
+    assert "whole passes" in r["sample"] and "tiny" in r["sample"]
