@@ -1,6 +1,6 @@
 """Static checks of the repository's scripts on the CPU: every name a function of bench.py or
 __graft_entry__.py reads as a global exists at module level or in builtins (a misspelt or
-out-of-scope name would only fail on a GPU machine), and bench.py refuses more than one GPU."""
+out-of-scope name would only fail where a GPU runs it), and bench.py refuses more than one GPU."""
 
 import builtins
 import os
