@@ -28,8 +28,10 @@
  *     style (Picotron page, "context parallelism and ring attention").
  *
  * Threading and ownership: every buffer is allocated and owned by the caller; the library
- * allocates no device memory and keeps no mutable global state, so concurrent calls on
- * different streams are safe as long as their output and workspace buffers do not overlap.
+ * allocates no device memory.  Its only mutable global state is a call counter (atomic) that
+ * tags the tiles of one-launch forward calls and a per-head_dim cache of the kernel's
+ * occupancy, so concurrent calls on different streams are safe as long as their output and
+ * workspace buffers do not overlap.
  * Calls are asynchronous: they enqueue work on `stream` and return without synchronising.
  * Every argument is validated on the host before any HIP runtime call; on an error code
  * nothing has been enqueued.  No C++ exception crosses this interface.
@@ -73,8 +75,22 @@ const char *attn_strerror(int code);
  * Bytes of device workspace attn_fwd needs for these sizes (0 when none is needed).
  * For bf16 it holds two equal halves of B * Hkv * (S rounded up to 64) * d bf16 elements: the
  * rotated keys, then the values transposed per 64-key tile (a private layout, rewritten on
- * every call).
+ * every call).  For head_dim 64 and 128 a flag area follows: one 8-byte tag per half of each
+ * 64-key tile, then a 4-byte status word, padded to a multiple of 256 bytes.
  * Returns 0 as well for arguments attn_fwd would reject.
+ *
+ * How the bf16 forward runs (head_dim 64 and 128).  When every workgroup of the attention
+ * kernel fits on the GPU at once, one kernel does everything: each workgroup first rotates the
+ * keys (or transposes the values) of a few tiles, writes them through to device scope, tags
+ * their flags with a value unique to the call, and then waits until the tiles it reads carry
+ * that tag.  Otherwise a separate preparation kernel runs first.  Both give bit-identical
+ * results.  The wait is bounded (a fraction of a second); a workgroup whose wait runs out
+ * writes NaN to its rows of out and lse and sets the status word to 1 (the library never
+ * clears it; a caller who wants to check it zeroes it before the call).  Nothing needs
+ * zeroing otherwise: tags left by earlier calls, or any other bytes, are never mistaken for
+ * the current call's.  Environment variables, for diagnostics: ATTN_FWD_PATH = "split" forces
+ * the separate preparation kernel, "fused" the single kernel wherever the grid fits;
+ * ATTN_FWD_FORCE_TIMEOUT = "1" makes every wait of the single kernel run out after a few polls.
  */
 size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype);
 

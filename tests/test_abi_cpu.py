@@ -58,11 +58,18 @@ def test_version_and_strerror():
     assert "unknown" in _lib.strerror(12345)
 
 
+def _flag_area(B, S, Hkv):
+    # one 8-byte tag per tile half, then a 4-byte status word, padded to 256 bytes
+    n = B * Hkv * ((S + 63) // 64) * 2
+    return (n * 8 + 16 + 255) // 256 * 256
+
+
 def test_workspace_bytes():
-    # bf16: rotated keys and transposed values, each (B, Hkv, S rounded up to 64, D) bf16
-    assert _lib.workspace_bytes(1, 2048, 8, 128, 0) == 2 * 1 * 8 * 2048 * 128 * 2
-    assert _lib.workspace_bytes(2, 100, 3, 64, 0) == 2 * 2 * 3 * 128 * 64 * 2
-    assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 2 * 64 * 64 * 2
+    # bf16: rotated keys and transposed values, each (B, Hkv, S rounded up to 64, D) bf16, then
+    # the one-launch form's flag area (not at head_dim 256, which has no such form)
+    assert _lib.workspace_bytes(1, 2048, 8, 128, 0) == 2 * 1 * 8 * 2048 * 128 * 2 + _flag_area(1, 2048, 8)
+    assert _lib.workspace_bytes(2, 100, 3, 64, 0) == 2 * 2 * 3 * 128 * 64 * 2 + _flag_area(2, 100, 3)
+    assert _lib.workspace_bytes(1, 1, 1, 64, 0) == 2 * 64 * 64 * 2 + _flag_area(1, 1, 1)
     assert _lib.workspace_bytes(1, 64, 1, 64, 1) == 0  # fp32 needs none
     assert _lib.workspace_bytes(1, 64, 1, 96, 0) == 0  # unsupported -> 0
     assert _lib.workspace_bytes(1, 100, 1, 256, 0) == 2 * 128 * 256 * 2  # head_dim 256 (bf16 forward)

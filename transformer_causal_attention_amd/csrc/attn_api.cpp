@@ -5,8 +5,13 @@
 #include "attn.h"
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <random>
 
 #include "attn_launch.h"
 
@@ -17,6 +22,61 @@ namespace {
 constexpr int kTileKeys = 64;  // key tile of the bf16 kernel; prepared K and V are padded to it
 
 size_t padded_len(int S) { return ((size_t)S + kTileKeys - 1) / kTileKeys * kTileKeys; }
+
+// Prepared tiles of the bf16 forward: rotated keys, then transposed values.
+size_t tile_bytes(int B, int S, int Hkv, int d) { return 2 * (size_t)B * Hkv * padded_len(S) * d * 2; }
+
+// After the tiles, the one-launch form's flags (one 8-byte tag per tile half) and a status word.
+size_t flag_bytes(int B, int S, int Hkv) {
+  const size_t n = (size_t)B * Hkv * (padded_len(S) / kTileKeys) * 2;
+  return (n * 8 + 16 + 255) / 256 * 256;
+}
+
+// Tags of one-launch calls: a process-wide counter started at a random 64-bit value, so a tag
+// equals a value left in a workspace by an earlier call (or by anything else) only by chance,
+// with probability 2^-64 per flag; 0 is skipped.
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    unsigned long long s = ((unsigned long long)rd() << 32) ^ rd();
+    s ^= (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    return s;
+  }()};
+  unsigned long long t = counter.fetch_add(1, std::memory_order_relaxed);
+  if (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed);
+  return t;
+}
+
+// Whether a bf16 forward of this grid takes the one-launch form: every workgroup must be
+// resident at once, and each wave group prepares at most kMaxPrepRounds tile halves (beyond
+// that the separate pass, whose workgroups each take one tile, is faster).  The environment
+// variable ATTN_FWD_PATH = "split" or "fused" overrides the choice (a diagnostic; "fused" is
+// still refused when the grid would not be resident).
+constexpr int kMaxPrepRounds = 2;
+
+// Bound of the one-launch form's wait for published tiles: each poll is a device-scope read
+// plus a ~0.1 us sleep, so the bound is a fraction of a second; the wait normally ends within
+// a few microseconds.
+constexpr int kMaxPolls = 1 << 18;
+
+template <int D>
+bool choose_fused(long long blocks, bool dual, int prep_rounds) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return false;
+  static std::atomic<int> per_cu[2] = {{-1}, {-1}};
+  int n = per_cu[dual].load(std::memory_order_relaxed);
+  if (n < 0) {
+    n = attn::fwd_bf16_wgs_per_cu<D>(dual);
+    per_cu[dual].store(n, std::memory_order_relaxed);
+  }
+  if (blocks > (long long)cus * n) return false;
+  const char *env = std::getenv("ATTN_FWD_PATH");
+  if (env && std::strcmp(env, "split") == 0) return false;
+  if (env && std::strcmp(env, "fused") == 0) return true;
+  return prep_rounds <= kMaxPrepRounds;
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -58,26 +118,13 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
                     const attn::RopeTable &tab, int causal, int q_pos0, int k_pos0, void *out,
                     float *lse, void *ws, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const size_t s_pad = padded_len(S);
-  attn::PrepParams pp;
-  pp.k = static_cast<const __bf16 *>(k);
-  pp.v = static_cast<const __bf16 *>(v);
-  pp.kr = static_cast<__bf16 *>(ws);
-  pp.vt = pp.kr + (size_t)B * Hkv * s_pad * D;
-  pp.B = B;
-  pp.S = S;
-  pp.Hkv = Hkv;
-  pp.S_pad = (int)s_pad;
-  pp.S_rows = S;
-  pp.tile0 = 0;
-  pp.n_run = (int)(s_pad / kTileKeys);
-  pp.k_pos0 = k_pos0;
-  hipError_t err = attn::launch_prep_kv<D>(pp, tab, st);
-  if (err != hipSuccess) return err;
+  __bf16 *kr = static_cast<__bf16 *>(ws);
+  __bf16 *vt = kr + (size_t)B * Hkv * s_pad * D;
 
-  attn::FwdParams p;
+  attn::FwdParams p{};
   p.q = static_cast<const __bf16 *>(q);
-  p.kr = pp.kr;
-  p.vt = pp.vt;
+  p.kr = kr;
+  p.vt = vt;
   p.out = static_cast<__bf16 *>(out);
   p.lse = lse;
   p.B = B;
@@ -85,7 +132,7 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
-  p.S_pad = pp.S_pad;
+  p.S_pad = (int)s_pad;
   p.hpw = heads_per_group(p.G);
   p.rows_per_blk = 32 * (4 / p.hpw);
   p.n_units = B * Hkv * (p.G / p.hpw);
@@ -105,6 +152,50 @@ hipError_t run_bf16(const void *q, const void *k, const void *v, int B, int S, i
       p.dual = (long long)p.n_units * p.n_pairs > cus ? 1 : 0;
   }
 
+  if constexpr (D != 256) {
+    // one launch when the whole grid is resident: the attention kernel prepares the tiles
+    p.k = static_cast<const __bf16 *>(k);
+    p.v = static_cast<const __bf16 *>(v);
+    p.k_pos0 = k_pos0;
+    p.prep_workers = (p.G / p.hpw) * p.n_pairs * (p.dual ? 1 : 2);
+    const int n_jobs = 2 * (int)(s_pad / kTileKeys);
+    p.prep_rounds = (n_jobs + p.prep_workers - 1) / p.prep_workers;
+    const long long blocks = (long long)p.n_pairs * (p.dual ? p.n_units / 2 : p.n_units);
+    if (choose_fused<D>(blocks, p.dual != 0, p.prep_rounds)) {
+      char *fl = reinterpret_cast<char *>(ws) + tile_bytes(B, S, Hkv, D);
+      p.flags = reinterpret_cast<unsigned long long *>(fl);
+      p.status = reinterpret_cast<unsigned int *>(fl + (size_t)B * Hkv * (s_pad / kTileKeys) * 2 * 8);
+      p.tag = next_call_tag();
+      p.await_tag = p.tag;
+      p.max_polls = kMaxPolls;
+      const char *force = std::getenv("ATTN_FWD_FORCE_TIMEOUT");
+      if (force && std::strcmp(force, "1") == 0) {
+        // diagnostic: every wait looks for a tag no workgroup writes and gives up after a few
+        // polls, so the timeout path runs with every kernel exiting normally
+        p.await_tag = p.tag ^ 1ull;
+        p.max_polls = 4;
+      }
+      return causal ? attn::launch_attn_bf16<D, true>(p, tab, st, e0, e1)
+                    : attn::launch_attn_bf16<D, false>(p, tab, st, e0, e1);
+    }
+  }
+
+  attn::PrepParams pp;
+  pp.k = static_cast<const __bf16 *>(k);
+  pp.v = static_cast<const __bf16 *>(v);
+  pp.kr = kr;
+  pp.vt = vt;
+  pp.B = B;
+  pp.S = S;
+  pp.Hkv = Hkv;
+  pp.S_pad = (int)s_pad;
+  pp.S_rows = S;
+  pp.tile0 = 0;
+  pp.n_run = (int)(s_pad / kTileKeys);
+  pp.k_pos0 = k_pos0;
+  hipError_t err = attn::launch_prep_kv<D>(pp, tab, st);
+  if (err != hipSuccess) return err;
+  p.flags = nullptr;
   if constexpr (D == 256) {
     return causal ? attn::launch_attn_d256<true>(p, tab, st, e0, e1) : attn::launch_attn_d256<false>(p, tab, st, e0, e1);
   } else {
@@ -185,7 +276,8 @@ ATTN_EXPORT const char *attn_strerror(int code) {
 ATTN_EXPORT size_t attn_fwd_workspace_bytes(int B, int S, int Hkv, int head_dim, int dtype) {
   if (dtype != ATTN_DTYPE_BF16) return 0;
   if (B < 1 || S < 1 || Hkv < 1 || (head_dim != 64 && head_dim != 128 && head_dim != 256) || S > (1 << 28)) return 0;
-  return 2 * (size_t)B * Hkv * padded_len(S) * head_dim * 2;  // rotated K and transposed V
+  // rotated K and transposed V, then the one-launch form's flags
+  return tile_bytes(B, S, Hkv, head_dim) + (head_dim != 256 ? flag_bytes(B, S, Hkv) : 0);
 }
 
 ATTN_EXPORT int attn_fwd(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,

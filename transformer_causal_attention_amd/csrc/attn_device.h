@@ -67,7 +67,25 @@ struct FwdParams {
   int delta;         // q_pos0 - k_pos0: key j is visible to query i iff j <= i + delta (causal)
   float q_scale;     // log2(e) / sqrt(D): scores come out in the base-2 domain
   int dual;          // head_dim 64: each workgroup runs two units (one per wave group)
+  // One-launch form: the attention kernel prepares the tiles itself (each wave group
+  // rotates the keys or transposes the values of some 64-key tiles, publishes a flag per
+  // tile half, then waits for the flags of every tile it reads).
+  const __bf16 *k;   // (B, S, Hkv, D) as given
+  const __bf16 *v;   // (B, S, Hkv, D) as given
+  unsigned long long *flags;  // (B, Hkv, S_pad/64, 2): tag of the call that wrote each half
+  unsigned int *status;       // set to kStatusTimeout by a workgroup whose wait ran out
+  unsigned long long tag;     // this call's tag (never a value an earlier call left behind)
+  unsigned long long await_tag;  // the tag the waits look for: tag (or, to test the bounded
+                                 // wait, a value no workgroup writes)
+  int max_polls;     // bound of each wait, in polls
+  int k_pos0;        // position of key row 0
+  int prep_workers;  // wave groups that prepare tiles of one (b, K/V head)
+  int prep_rounds;   // jobs per wave group, rounded up: ceil(2 * S_pad/64 / prep_workers)
 };
+
+// Value left in FwdParams::status when a workgroup gave up waiting for a tile (its rows are
+// then written as NaN).
+constexpr unsigned int kStatusTimeout = 1u;
 
 struct F32Params {
   const float *q, *k, *v;
@@ -152,6 +170,19 @@ __device__ __forceinline__ void sincos_turns(float t, float *s, float *c) {
   sincospif(2.0f * t, s, c);
 }
 
+// One rotary pair (x, y) turned by the angle with cosine c and sine s: (x c - y s, y c + x s),
+// each with one explicit fused multiply-add so that every kernel that prepares keys rounds
+// alike.
+__device__ __forceinline__ void rotate_pair(float x, float y, float c, float s, float &rx, float &ry) {
+  rx = __builtin_fmaf(x, c, -(y * s));
+  ry = __builtin_fmaf(y, c, x * s);
+}
+
+// Two rotary pairs, (x0, y0) and (x1, y1) unpacked from the bf16 words xw = (x0, x1) and
+// yw = (y0, y1), turned by (c0, s0) and (c1, s1); returns the packed bf16 words (x0', x1') and
+// (y0', y1').
+__device__ __forceinline__ u32x2 rotate_packed(uint32_t xw, uint32_t yw, float c0, float s0, float c1, float s1);
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -160,6 +191,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 r = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x2 rotate_packed(uint32_t xw, uint32_t yw, float c0, float s0, float c1, float s1) {
+  float a0, b0, a1, b1;
+  rotate_pair(bf16_lo(xw), bf16_lo(yw), c0, s0, a0, b0);
+  rotate_pair(bf16_hi(xw), bf16_hi(yw), c1, s1, a1, b1);
+  return u32x2{pack_bf16x2(a0, a1), pack_bf16x2(b0, b1)};
 }
 
 }  // namespace attn

@@ -92,7 +92,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, u
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
+// 16-byte store at byte voff + soff of buffer `rsrc`, written through to device scope (sc1):
+// visible to every CU once the store has completed, without a cache write-back.
+__device__ __forceinline__ void store_through(const u32x4 &v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)voff, (int)soff, 16);
+}
+
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector memory operations of this wave are outstanding (they complete in
+// issue order, so the ones issued before the last N are done).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -100,7 +111,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 
 constexpr int kReadsAhead = 6;  // LDS operand reads kept in flight ahead of the MFMAs
 
-template <int D, bool CAUSAL, bool DUAL>
+template <int D, bool CAUSAL, bool DUAL, bool FUSED>
 __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;              // MFMA steps over head_dim
   constexpr int NCB = D / 32;              // 32-column blocks of the output
@@ -215,9 +226,11 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
   auto seg_rows = [&](int seg) __attribute__((always_inline)) {
     row0 = (seg == 0 ? r_lo : r_hi) * RPB + sub * 32;
   };
+  // every lane issues the same NKK loads (rows past S load row S-1; clear_dead_q zeroes them
+  // once they are in), so a partial wait can count them
   auto load_q = [&](u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
-    const int my_row = row0 + l32;
-    if (my_row < S && tab.interleaved) {
+    const int my_row = min(row0 + l32, S - 1);
+    if (tab.interleaved) {
       // dims 32kk + 16hh .. +15 of the row; split into evens (raw[kk]) and odds
       // (raw[kk + NKK/2]) by unpair_q once loaded
       const __bf16 *src = p.q + (((size_t)b * S + my_row) * p.Hq + head) * D + 16 * hh;
@@ -226,11 +239,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         raw[kk] = *reinterpret_cast<const u32x4 *>(src + 32 * kk);
         raw[kk + NKK / 2] = *reinterpret_cast<const u32x4 *>(src + 32 * kk + 8);
       }
-    } else if (my_row < S) {
+    } else {
       const __bf16 *src = p.q + (((size_t)b * S + my_row) * p.Hq + head) * D + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) raw[kk] = *reinterpret_cast<const u32x4 *>(src + 16 * kk);
-    } else {
+    }
+  };
+  auto clear_dead_q = [&](u32x4 (&raw)[NKK]) __attribute__((always_inline)) {
+    if (row0 + l32 >= S) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) raw[kk] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -565,6 +581,7 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
         m_lo = m_run;
         seg_rows(1);
         if constexpr (DUAL) {
+          clear_dead_q(raw_hi);
           unpair_q(raw_hi);
           rotate_q(raw_hi);
         } else {
@@ -587,6 +604,164 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     wait_vm_all();
     __syncthreads();
   };
+
+  // ---- one-launch form (FUSED): before attending, each wave group prepares some 64-key
+  // tiles of its (batch row, K/V head) -- the work of the separate preparation pass, spread
+  // over the workgroups that read those tiles -- and publishes them, then waits until every
+  // tile its workgroup reads is published.  A job is one half of a tile: the rotated keys
+  // (rotary embedding of k at positions k_pos0 + j, half-split pairs (c, c + D/2) after the
+  // adjacent-pair reordering when that form is chosen: Picotron page section 1, PaLM page
+  // 2.3) or the values transposed into the V^T layout.  Worker w of a (b, g) does jobs
+  // w, w + prep_workers, ...  The tiles are stored with device-scope write-through stores, and
+  // a half's flag gets this call's tag (a device-scope store) once every wave's stores have
+  // completed; the waiting wave reads the flags at device scope.  No cache can hold an older
+  // copy of a tile: caches start each kernel without stale lines of memory other kernels
+  // wrote, and no workgroup reads a tile before its flags carry the tag, so the staging
+  // copies that follow see the tiles.  This avoids a write-back and an invalidation of a
+  // whole L2 per workgroup, which a release/acquire pair at device scope would cost.  Every
+  // workgroup of the grid is resident at once (the host launches this form only then), so
+  // the wait ends; it is bounded all the same, and a workgroup whose wait runs out records
+  // kStatusTimeout and writes NaN to its rows.
+  constexpr int NL = D / 32;  // 16-byte loads per thread and preparation job (either half)
+  const int prep_tid = tid & 255;
+  const int prep_worker = DUAL ? pi * HG + hg : (pi * HG + hg) * 2 + grp;
+  const int prep_jobs = 2 * (int)n_tiles;
+  const size_t rs = (size_t)p.Hkv * D;  // elements between consecutive keys in k, v
+  char *const vstage = ldsk1 + grp * TB;  // a group's staged values: [64 keys][D] bf16
+  // the loads of round rnd's job, the same NL loads for either half and without branches (a
+  // thread without a job loads the keys of tile 0 and ignores them), so that they stay in
+  // flight behind the query loads
+  //   keys:   item (key row = lane, chunk pair cp = gw + 4 * (i / 2)); chunk pair cp holds dims
+  //           8cp.. and D/2 + 8cp.. (adjacent-pair form: 16cp..16cp+15, split into evens and
+  //           odds once loaded)
+  //   values: item (key row, 8-dim chunk) = prep_tid + 256 * i
+  //   rows past S load row S-1 and are zeroed once loaded
+  auto prep_load = [&](int rnd, u32x4 (&ld)[NL]) __attribute__((always_inline)) {
+    const int job_r = prep_worker + rnd * p.prep_workers;
+    const int job = job_r < prep_jobs ? job_r : 0;
+    const bool is_v = (job & 1) != 0;
+    const int j0 = (job >> 1) * BN;
+    const __bf16 *base = (is_v ? p.v : p.k) + (size_t)b * S * rs + (size_t)g * D;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int item = prep_tid + 256 * i;
+      const int cp = gw + 4 * (i / 2);
+      const int kcol = tab.interleaved ? 16 * cp + 8 * (i & 1) : 8 * cp + (i & 1) * (D / 2);
+      const int row = is_v ? item / (D / 8) : lane;
+      const int col = is_v ? 8 * (item % (D / 8)) : kcol;
+      ld[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)min(j0 + row, S - 1) * rs + col);
+    }
+  };
+  // once the loads are in: keys rotated and stored; values staged in LDS
+  auto prep_work_a = [&](int rnd, const u32x4 (&ld)[NL]) __attribute__((always_inline)) {
+    const int job = prep_worker + rnd * p.prep_workers;
+    if (job >= prep_jobs) return;
+    const int j0 = (job >> 1) * BN;
+    const uint32_t tile_off = (uint32_t)(job >> 1) * TB;  // in this (b, g)'s run of tiles
+    if ((job & 1) == 0) {
+#pragma unroll
+      for (int it = 0; it < NL / 2; ++it) {
+        const int cp = gw + 4 * it;
+        const int j = j0 + lane;
+        u32x4 xk = ld[2 * it], yk = ld[2 * it + 1];
+        if (tab.interleaved) deinterleave16(ld[2 * it], ld[2 * it + 1], xk, yk);
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (j < S) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float t0 = turn_fraction(p.k_pos0 + j, tab.rev[8 * cp + 2 * w]);
+            const float t1 = turn_fraction(p.k_pos0 + j, tab.rev[8 * cp + 2 * w + 1]);
+            // (hardware sin/cos take turns)
+            const u32x2 r = rotate_packed(xk[w], yk[w], __builtin_amdgcn_cosf(t0), __builtin_amdgcn_sinf(t0),
+                                          __builtin_amdgcn_cosf(t1), __builtin_amdgcn_sinf(t1));
+            lo[w] = r[0];
+            hi[w] = r[1];
+          }
+        }
+        store_through(lo, kr_buf, dma_lane, tile_off + cp * 1024);
+        store_through(hi, kr_buf, dma_lane, tile_off + (cp + D / 16) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < NL; ++it) {
+        const int item = prep_tid + 256 * it;
+        const int row = item / (D / 8), ch = item % (D / 8);
+        *reinterpret_cast<u32x4 *>(vstage + row * (D * 2) + ch * 16) = j0 + row < S ? ld[it] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // after a barrier: the staged values leave as the V^T tile, [8 key chunks qq][D columns c][8
+  // keys]; inside each group of 16 keys the key at position p0 is swap23(p0) (bits 2 and 3
+  // exchanged), the order in which the score accumulators list their keys
+  auto prep_work_b = [&](int rnd) __attribute__((always_inline)) {
+    const int job = prep_worker + rnd * p.prep_workers;
+    if (job >= prep_jobs || (job & 1) == 0) return;
+    const uint32_t tile_off = (uint32_t)(job >> 1) * TB;
+    const uint16_t *vs = reinterpret_cast<const uint16_t *>(vstage);
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const int item = prep_tid + 256 * it;
+      const int c = item % D, qq = item / D;
+      u32x4 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p0 = 8 * qq + 2 * e;
+        const int r0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
+        w4[e] = (uint32_t)vs[r0 * D + c] | ((uint32_t)vs[(r0 + 1) * D + c] << 16);
+      }
+      store_through(w4, vt_buf, 16u * (uint32_t)c, tile_off + qq * (D * 16));
+    }
+  };
+  // publish: the tiles were written through to device scope, and every wave's stores have
+  // completed before the barrier; one thread per group then tags the halves its group wrote
+  auto publish = [&]() __attribute__((always_inline)) {
+    wait_vm_all();
+    __syncthreads();
+    if (prep_tid == 0) {
+      const size_t bg_id = (size_t)b * p.Hkv + g;
+      for (int rnd = 0; rnd < p.prep_rounds; ++rnd) {
+        const int job = prep_worker + rnd * p.prep_workers;
+        if (job < prep_jobs)
+          __hip_atomic_store(p.flags + bg_id * n_tiles * 2 + job, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  // wait: one wave per (b, g) the workgroup reads (both groups share it unless DUAL) checks
+  // both halves of tiles 0 .. t_hi-1, the tiles any of its rows can see
+  auto await_tiles = [&]() __attribute__((always_inline)) -> bool {
+    const size_t bg_id = (size_t)b * p.Hkv + g;
+    int *const verdict = reinterpret_cast<int *>(ldsk1);  // [group]
+    if (gw == 0 && (DUAL || grp == 0)) {
+      const unsigned long long *fl = p.flags + bg_id * n_tiles * 2;
+      const int n_fl = 2 * t_hi;
+      bool ok = false;
+      for (int poll = 0; poll < p.max_polls; ++poll) {
+        bool mine = true;
+        for (int f = lane; f < n_fl; f += 64)
+          mine = mine && __hip_atomic_load(fl + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.await_tag;
+        if (__builtin_amdgcn_ballot_w64(!mine) == 0) {
+          ok = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      if (!ok && lane == 0) __hip_atomic_store(p.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) verdict[grp] = ok ? 1 : 0;
+    }
+    __syncthreads();
+    const bool ok = DUAL ? (verdict[0] & verdict[1]) != 0 : verdict[0] != 0;
+    __syncthreads();  // the verdict is read before anything is copied into ldsk1
+    return ok;
+  };
+  // a workgroup that gave up waiting writes NaN to every row it owns
+  auto fail_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x16{} + __builtin_nanf("");
+    // (a positive sum with a NaN reference makes both out and lse NaN)
+    if (runs_lo && two) store_seg(r_lo * RPB + sub * 32, 1.f, __builtin_nanf(""));
+    if (DUAL || grp == 1) store_seg(r_hi * RPB + sub * 32, 1.f, __builtin_nanf(""));
+  };
+
   // ---- prologue: the first row block's queries are loaded while the first K tile is copied,
   // then rotated; group B leaves its rotated queries in its hand-off slot for group A (read at
   // A's switch to block r_hi, at step len0 >= 1, so after at least one barrier).  The P.V
@@ -604,7 +779,14 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 #pragma unroll
         for (int z = 0; z < 2; ++z) fq[j][z] = tab.rev[tab_freq_index(j, z)];
     }
+    // this thread's rotation frequency for the LDS copy (DUAL, or fewer than four heads per
+    // group), loaded unconditionally so that no branch waits for it here
+    const double fr_own = tab.rev[min(tid, D / 2 - 1)];
     u32x4 raw[NKK];
+    u32x4 ld[NL];
+    // one-launch form: the preparation job's loads go first, so its tiles are published as
+    // early as possible (every workgroup of the (b, g) waits for the last of them)
+    if constexpr (FUSED) prep_load(0, ld);
     if constexpr (DUAL) {
       if (len0 > 0) {  // block r_hi's queries come in now and wait in registers for the switch
         seg_rows(1);
@@ -613,7 +795,9 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
       }
     }
     load_q(raw);
-    if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
+    if constexpr (!FUSED) {
+      if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
+    }
     {
       u32x4 *z1 = reinterpret_cast<u32x4 *>(ldsv1);
 #pragma unroll
@@ -621,20 +805,47 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
     }
     // (DUAL keeps the frequencies in LDS for the rotation at the switch: no hand-off slot)
     if (DUAL || !shared_tab) {
-      if (tid < D / 2) freq[tid] = tab.rev[tid];
+      if (tid < D / 2) freq[tid] = fr_own;
     }
-    if (shared_tab) {
-      build_rot_tab(fq);
-      wait_vm_all();
+    if (shared_tab) build_rot_tab(fq);
+    if constexpr (FUSED) {
+      // the job's loads are in once at most the query loads issued after them are outstanding
+      if (DUAL && len0 > 0)
+        wait_vm_le<2 * NKK>();
+      else
+        wait_vm_le<NKK>();
+      prep_work_a(0, ld);
       __syncthreads();
-      unpair_q(raw);
-      rotate_q_tab(raw, len0 > 0 ? 0 : 1);
+      prep_work_b(0);
+      __syncthreads();
+      for (int rnd = 1; rnd < p.prep_rounds; ++rnd) {  // the same count in every group
+        prep_load(rnd, ld);
+        wait_vm_all();
+        prep_work_a(rnd, ld);
+        __syncthreads();
+        prep_work_b(rnd);
+        __syncthreads();
+      }
+      publish();  // waits for every load and store of the wave, then a barrier
     } else {
       wait_vm_all();
       __syncthreads();
-      unpair_q(raw);
+    }
+    clear_dead_q(raw);
+    unpair_q(raw);
+    if (shared_tab)
+      rotate_q_tab(raw, len0 > 0 ? 0 : 1);
+    else
       rotate_q(raw);
-      if (!DUAL) __syncthreads();  // the frequencies (in the hand-off slot) are no longer read
+    // the frequencies (in the hand-off slot unless DUAL) are no longer read
+    __syncthreads();
+    if constexpr (FUSED) {
+      if (!await_tiles()) {
+        fail_rows();
+        return;  // uniform over the workgroup: no barrier follows for anyone
+      }
+      if (n_mine > 0) stage(kr_buf, tile_of(0), ldsk0 + grp * TB);  // first K tile of each group
+      wait_vm_all();  // (made visible to every wave by the barrier closing the prologue)
     }
     reset_seg();
     // block r_lo sees no key at all (a shard of later keys): its rows are empty
@@ -749,19 +960,43 @@ __global__ void __launch_bounds__(512) attn_fwd_bf16_kernel(FwdParams p, RopeTab
 template <int D, bool CAUSAL>
 hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const bool fused = p.flags != nullptr;
   if constexpr (D == 64) {
     if (p.dual) {  // two units per workgroup (the host checks that n_units is even)
       const long long blocks = (long long)(p.n_units / 2) * p.n_pairs;
-      hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                            ev_start, ev_stop, 0, p, tab);
+      if (fused)
+        hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, true>), dim3((unsigned)blocks), dim3(512), 0,
+                              stream, ev_start, ev_stop, 0, p, tab);
+      else
+        hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true, false>), dim3((unsigned)blocks), dim3(512), 0,
+                              stream, ev_start, ev_stop, 0, p, tab);
       return hipGetLastError();
     }
   }
   const long long blocks = (long long)p.n_units * p.n_pairs;
-  hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)blocks), dim3(512), 0, stream,
-                        ev_start, ev_stop, 0, p, tab);
+  if (fused)
+    hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, true>), dim3((unsigned)blocks), dim3(512), 0, stream,
+                          ev_start, ev_stop, 0, p, tab);
+  else
+    hipExtLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false, false>), dim3((unsigned)blocks), dim3(512), 0,
+                          stream, ev_start, ev_stop, 0, p, tab);
   return hipGetLastError();
 }
+
+// Workgroups of the forward kernel that one CU holds at once (the one-launch form needs the
+// whole grid resident).
+template <int D>
+int fwd_bf16_wgs_per_cu(bool dual) {
+  int n = 0;
+  hipError_t e;
+  if (D == 64 && dual)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<D, true, D == 64, true>, 512, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<D, true, false, true>, 512, 0);
+  return e == hipSuccess ? n : 0;
+}
+template int fwd_bf16_wgs_per_cu<64>(bool);
+template int fwd_bf16_wgs_per_cu<128>(bool);
 
 template hipError_t launch_attn_bf16<64, true>(const FwdParams &, const RopeTable &, hipStream_t,
                                                     hipEvent_t, hipEvent_t);

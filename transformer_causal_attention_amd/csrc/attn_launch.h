@@ -14,6 +14,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_attn_bf16(const FwdParams &p, const RopeTable &tab, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Workgroups of the bf16 forward kernel (one-launch form) one CU holds at once; 0 on error.
+template <int D>
+int fwd_bf16_wgs_per_cu(bool dual);
+
 // head_dim 256: one wave per 32 query rows, prepared K/V streamed into registers
 template <bool CAUSAL>
 hipError_t launch_attn_d256(const FwdParams &p, const RopeTable &tab, hipStream_t stream, hipEvent_t ev_start,

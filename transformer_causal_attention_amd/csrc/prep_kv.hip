@@ -101,12 +101,11 @@ __global__ void __launch_bounds__(256) prep_kv_kernel(PrepParams p, RopeTable ta
       for (int w = 0; w < 4; ++w) {
         const float t0 = turn_fraction(p.k_pos0 + j, freq[c0 + 2 * w]);
         const float t1 = turn_fraction(p.k_pos0 + j, freq[c0 + 2 * w + 1]);
-        const float s0 = __builtin_amdgcn_sinf(t0), cs0 = __builtin_amdgcn_cosf(t0);
-        const float s1 = __builtin_amdgcn_sinf(t1), cs1 = __builtin_amdgcn_cosf(t1);
-        const float x0 = bf16_lo(xk[w]), x1 = bf16_hi(xk[w]);
-        const float y0 = bf16_lo(yk[w]), y1 = bf16_hi(yk[w]);
-        lo[w] = pack_bf16x2(x0 * cs0 - y0 * s0, x1 * cs1 - y1 * s1);
-        hi[w] = pack_bf16x2(y0 * cs0 + x0 * s0, y1 * cs1 + x1 * s1);
+        // (hardware sin/cos take turns)
+        const u32x2 r = rotate_packed(xk[w], yk[w], __builtin_amdgcn_cosf(t0), __builtin_amdgcn_sinf(t0),
+                                      __builtin_amdgcn_cosf(t1), __builtin_amdgcn_sinf(t1));
+        lo[w] = r[0];
+        hi[w] = r[1];
       }
     }
     *reinterpret_cast<u32x4 *>(kdst + (size_t)cp * 1024 + row * 16) = lo;
