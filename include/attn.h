@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* Element types of q, k, v and out. */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 inputs/outputs; bf16 MFMA with float32 accumulation */
@@ -64,6 +64,8 @@ extern "C" {
                                   dtype, sizes too large */
 #define ATTN_EHIP (-3)         /* the HIP runtime rejected an event record or kernel launch */
 #define ATTN_EWORKSPACE (-4)   /* workspace pointer null while needed, or workspace too small */
+#define ATTN_ESCRATCH (-5)     /* attn_fwd_noalloc: the call needs more than the library's
+                                  fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES) */
 
 /* Version of this interface (ATTN_ABI_VERSION). */
 int attn_abi_version(void);
@@ -131,6 +133,24 @@ int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, in
                    int head_dim, double rope_theta, int rope_style, int causal, int dtype,
                    void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
                    void *ev_start, void *ev_stop);
+
+/*
+ * attn_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it): the same computation,
+ * arguments and results, but without a workspace argument.  The workspace is a fixed array of
+ * ATTN_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per GPU, held until the
+ * process ends; the call allocates nothing (its address is looked up once per device, on the
+ * first call there).  A call whose attn_fwd_workspace_bytes(...) exceeds that size returns
+ * ATTN_ESCRATCH before any HIP call.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (different streams, or different host threads without
+ * ordering) race on it and give undefined results; calls ordered on one stream are safe.  The
+ * array keeps the last call's contents, and nothing in it needs clearing between calls.
+ * The stream must belong to the current device (else ATTN_EINVAL).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_fwd_noalloc(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                     int head_dim, double rope_theta, int rope_style, int causal, int dtype,
+                     void *out, float *lse, void *stream);
 
 /*
  * One shard of a longer sequence: attn_fwd for queries at positions q_pos0 .. q_pos0+S-1

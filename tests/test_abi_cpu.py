@@ -52,8 +52,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert _lib.abi_version() == 5
-    for code in (0, -1, -2, -3, -4):
+    assert _lib.abi_version() == 6
+    for code in (0, -1, -2, -3, -4, -5):
         assert len(_lib.strerror(code)) > 5
     assert "unknown" in _lib.strerror(12345)
 
@@ -269,3 +269,13 @@ def bwd_call(**over):
 ])
 def test_bwd_rejections(over, code):
     assert bwd_call(**over) == code
+
+
+def test_noalloc_rejections_before_any_hip_call():
+    lib = _lib.load()
+    # 2 * 8 * 2^20 * 128 * 2 bytes of tiles > the fixed scratch
+    rc = lib.attn_fwd_noalloc(P, P, P, 1, 1 << 20, 32, 8, 128, 5e5, 0, 1, 0, P, P, None)
+    assert rc == _lib.ATTN_ESCRATCH
+    assert lib.attn_fwd_noalloc(None, P, P, 1, 64, 4, 1, 64, 1e4, 0, 1, 0, P, P, None) == _lib.ATTN_EINVAL
+    assert lib.attn_fwd_noalloc(P, P, P, 1, 64, 4, 1, 96, 1e4, 0, 1, 0, P, P, None) == _lib.ATTN_EUNSUPPORTED
+    assert "scratch" in _lib.strerror(_lib.ATTN_ESCRATCH)

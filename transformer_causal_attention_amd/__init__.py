@@ -44,6 +44,7 @@ from .api import (  # noqa: F401
     attn_decode,
     attn_fwd,
     attn_fwd_into,
+    attn_fwd_noalloc,
     attn_merge,
     kv_cache_bytes,
     kv_prepare,

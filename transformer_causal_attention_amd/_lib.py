@@ -20,6 +20,7 @@ ATTN_EINVAL = -1
 ATTN_EUNSUPPORTED = -2
 ATTN_EHIP = -3
 ATTN_EWORKSPACE = -4
+ATTN_ESCRATCH = -5
 
 # Every symbol include/attn.h declares, with its ctypes signature.
 _VP = ctypes.c_void_p
@@ -38,6 +39,7 @@ SIGNATURES = {
     "attn_fwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "attn_fwd": (_I, _FWD_ARGS),
     "attn_fwd_timed": (_I, _FWD_ARGS + [_VP, _VP]),
+    "attn_fwd_noalloc": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _VP, _VP, _VP]),
     "attn_fwd_shard": (_I, _SHARD_ARGS),
     "attn_merge": (_I, _MERGE_ARGS),
     "attn_kv_prepare": (_I, _PREP_ARGS),
@@ -97,6 +99,13 @@ def fwd_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, ls
     if ev_start is None and ev_stop is None:
         return lib.attn_fwd(*args)
     return lib.attn_fwd_timed(*args, ev_start, ev_stop)
+
+
+def fwd_noalloc_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype, out, lse, stream,
+                    rope_style=ATTN_ROPE_HALF):
+    """Call attn_fwd_noalloc (the library's own scratch as workspace) with raw pointers; returns the code."""
+    return load().attn_fwd_noalloc(q, k, v, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style), int(causal),
+                                   dtype, out, lse, stream)
 
 
 def shard_raw(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dtype, out, lse,

@@ -89,6 +89,26 @@ def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, even
                          interleaved)
 
 
+def attn_fwd_noalloc(q, k, v, rope_theta, causal, out, lse, stream=None, interleaved=False):
+    """attn_fwd through attn_fwd_noalloc: no workspace, and nothing allocated by this call.
+
+    out (like q) and lse ((B, Hq, S) float32) are caller-provided; the library's own fixed
+    scratch serves as workspace (calls that overlap in time on one GPU race on it).
+    """
+    B, S, Hq, Hkv, D = _shapes(q, k, v)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, S)")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = _lib.fwd_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, S, Hq, Hkv, D, rope_theta,
+                              1 if causal else 0, _DTYPE_CODE[q.dtype], out.data_ptr(), lse.data_ptr(),
+                              st.cuda_stream, rope_style=_rope_style(interleaved))
+    if rc != _lib.ATTN_OK:
+        raise _lib.AttnError(rc, "attn_fwd_noalloc")
+    return out, lse
+
+
 def attn_merge(o1, lse1, o2, lse2, out=None, lse=None, stream=None):
     """Join two partial results over disjoint keys (attn_merge).  Returns (out, lse).
 

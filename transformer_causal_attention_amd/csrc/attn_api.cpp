@@ -269,6 +269,7 @@ ATTN_EXPORT const char *attn_strerror(int code) {
     case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, dtype bf16 or fp32, sizes within limits)";
     case ATTN_EHIP: return "HIP runtime error while recording an event or launching a kernel";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()";
+    case ATTN_ESCRATCH: return "attn_fwd_noalloc: the call needs more workspace than the library's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }
@@ -327,6 +328,51 @@ ATTN_EXPORT int attn_merge(const void *o1, const float *lse1, const void *o2, co
           : head_dim == 128 ? attn::launch_merge<float, 128>(p, st)
                             : attn::launch_merge<float, 256>(p, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+namespace {
+
+// Workspace of attn_fwd_noalloc: one array per GPU in the library's device memory.  Host code
+// uses only the device address that hipGetSymbolAddress returns for the current device (the
+// array's own name is a host-side stand-in, not a device address).
+__device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch, looked up once per device (concurrent first
+// calls may both look it up; they store the same address).  nullptr on failure.
+void *scratch_for(int dev) {
+  static std::atomic<void *> addr[kMaxDevices];
+  void *ptr = addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_fwd_noalloc(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
+                                 int head_dim, double rope_theta, int rope_style, int causal, int dtype, void *out,
+                                 float *lse, void *stream) {
+  // the arguments attn_fwd checks first, so that a rejected call touches no device state
+  if (!q || !k || !v || !out || !lse) return ATTN_EINVAL;
+  const int rc = check_shape(B, S, Hq, Hkv, head_dim, rope_theta, causal, dtype);
+  if (rc != ATTN_OK) return rc;
+  const size_t need = attn_fwd_workspace_bytes(B, S, Hkv, head_dim, dtype);
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ESCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    int dev = -1, sdev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_EHIP;
+    if (stream != nullptr && (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != dev))
+      return ATTN_EINVAL;
+    ws = scratch_for(dev);
+    if (ws == nullptr) return ATTN_EHIP;
+  }
+  return fwd_impl(q, k, v, B, S, Hq, Hkv, head_dim, rope_theta, rope_style, causal, 0, 0, dtype, out, lse, ws,
+                  need, stream, nullptr, nullptr);
 }
 
 ATTN_EXPORT int attn_fwd_timed(const void *q, const void *k, const void *v, int B, int S, int Hq, int Hkv,
