@@ -102,47 +102,89 @@ def copy_calibration(n_bytes=256 << 20, reps=3):
     print(json.dumps({"copy_bytes_each_way": n_bytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, budget_s=20.0, interleaved=False):
-    """Time the oracle as it stands on a bounded sample of the workload (whole heads)."""
-    import numpy as np
+_ORACLE_STATE = {}
 
+
+def _oracle_worker_init(wd, interleaved):
+    """Worker process of the CPU baseline: regenerate the seeded inputs once (one BLAS thread)."""
+    from transformer_causal_attention_amd.workloads import Workload, make_inputs
+
+    w = Workload(**wd)
+    _ORACLE_STATE.update(w=w, qkv=make_inputs(w), interleaved=interleaved)
+
+
+def _oracle_task(task):
+    """One (query head, row block) of batch row 0 through the oracle; returns its FLOPs."""
     from oracle import attention
-    from transformer_causal_attention_amd.workloads import make_inputs
 
+    h, r0, r1 = task
+    w, (q, k, v), il = _ORACLE_STATE["w"], _ORACLE_STATE["qkv"], _ORACLE_STATE["interleaved"]
+    g = h // (w.Hq // w.Hkv)
+    n = r1 if w.causal else w.S  # causal rows below r1 see keys below r1 only
+    attention(q[:1, :n, h:h + 1].double().numpy(), k[:1, :n, g:g + 1].double().numpy(),
+              v[:1, :n, g:g + 1].double().numpy(), w.rope_theta, w.causal, rows=list(range(r0, r1)),
+              interleaved=il)
+    vis = sum(i + 1 for i in range(r0, r1)) if w.causal else (r1 - r0) * w.S
+    return 4.0 * w.d * vis
+
+
+def cpu_baseline(w, budget_s=10.0, interleaved=False, rows_per_task=256):
+    """Time the oracle as it stands on the host's cores: one worker process per core of the
+    affinity mask, one BLAS thread each, tasks of (query head, block of query rows) of batch row
+    0 (heads and rows are independent, so each task is the definition restricted to its rows).
+    Tasks are handed out (two per worker in flight) until budget_s of wall time has passed,
+    cycling over batch row 0; the row blocks are visited in a spread order so that a partial pass
+    samples every part of the sequence.  value = FLOPs of the finished tasks / wall time."""
+    import dataclasses
+    import multiprocessing as mp
+    from collections import deque
+
+    cores = len(os.sched_getaffinity(0))
+    n_blk = (w.S + rows_per_task - 1) // rows_per_task
+    step = max(1, int(round(n_blk * 0.6180339887)))
+    while n_blk > 1 and np_gcd(step, n_blk) != 1:
+        step += 1
+    blocks = [(i * step) % n_blk for i in range(n_blk)]
+    tasks = [(h, b * rows_per_task, min(w.S, (b + 1) * rows_per_task)) for b in blocks for h in range(w.Hq)]
+    workers = max(1, min(cores, len(tasks)))
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k_: os.environ.get(k_) for k_ in env_keys}
+    for k_ in env_keys:
+        os.environ[k_] = "1"  # inherited by the spawned workers only (this process's BLAS is set up)
     try:
-        from threadpoolctl import threadpool_info
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_oracle_worker_init,
+                      initargs=(dataclasses.asdict(w), interleaved)) as pool:
+            pool.map(_oracle_task, [(0, 0, 1)] * (2 * workers), chunksize=1)  # imports, first touch
+            pending, fl, done, ti = deque(), 0.0, 0, 0
+            t0 = time.perf_counter()
+            while True:
+                while len(pending) < 2 * workers and time.perf_counter() - t0 < budget_s:
+                    pending.append(pool.apply_async(_oracle_task, (tasks[ti % len(tasks)],)))
+                    ti += 1
+                if not pending:
+                    break
+                fl += pending.popleft().get()
+                done += 1
+            elapsed = time.perf_counter() - t0
+    finally:
+        for k_, v_ in saved.items():
+            if v_ is None:
+                os.environ.pop(k_, None)
+            else:
+                os.environ[k_] = v_
+    passes, rest = divmod(done, len(tasks))
+    sample = f"batch row 0 of {w.name} ({w.Hq} query heads x {w.S} rows in tasks of {rows_per_task} rows): "
+    sample += f"{passes} whole passes" + (f" and {rest} of {len(tasks)} tasks of one more" if rest else "")
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle", "sample": sample,
+            "seconds": round(elapsed, 3), "host_cores": cores, "blas_threads_per_worker": 1,
+            "workers": workers}
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    q, k, v = make_inputs(w)
-    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
-    # one batch row, K/V head 0 and its query heads first; grow while within the budget, and
-    # when every head of the row is done, go over the row again until half the budget is spent
-    G = w.Hq // w.Hkv
-    heads_done, passes, elapsed, fl = 0, 0, 0.0, 0.0
-    while elapsed < budget_s / 2:
-        if heads_done == w.Hq:
-            heads_done, passes = 0, passes + 1
-        n = G if heads_done == 0 else min(w.Hq - heads_done, max(G, heads_done))
-        n = n - n % G if n >= G else n
-        hs = slice(heads_done, heads_done + n)
-        g0, g1 = heads_done // G, (heads_done + n) // G
-        t0 = time.perf_counter()
-        attention(qd[:1, :, hs], kd[:1, :, g0:g1], vd[:1, :, g0:g1], w.rope_theta, w.causal, interleaved=interleaved)
-        elapsed += time.perf_counter() - t0
-        fl += flops(w.with_(B=1, Hq=n, Hkv=g1 - g0))
-        heads_done += n
-    if heads_done == w.Hq:
-        heads_done, passes = 0, passes + 1
-    if passes == 0:
-        sample = f"batch row 0, query heads 0..{heads_done - 1} of {w.name} (all {w.S} rows)"
-    else:
-        sample = f"batch row 0 of {w.name}, all {w.Hq} query heads and all {w.S} rows, {passes} whole passes"
-        if heads_done:
-            sample += f" and query heads 0..{heads_done - 1} of one more"
-    return {"value": fl / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 3)}
+
+def np_gcd(a, b):
+    while b:
+        a, b = b, a % b
+    return a
 
 
 def ring_bench(args):

@@ -223,16 +223,19 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_dim);
  * lse.  Keys 0 .. q_pos of `cache` must have been prepared by attn_kv_prepare with the same
  * rope_theta and rope_style.  The key range is split over workgroups and joined by a second kernel.
  *   q        device, (B, Hq, head_dim) bfloat16 contiguous, 16-byte aligned
- *   cache    as filled by attn_kv_prepare for (B, S_cap, Hkv, head_dim)
+ *   cache    as filled by attn_kv_prepare for (B, S_cap, Hkv, head_dim): S_cap, B, Hkv and
+ *            head_dim must be the values used there (they fix the cache's layout)
+ *   cache_bytes  bytes of the cache allocation; below attn_fwd_workspace_bytes(B, S_cap, Hkv,
+ *            head_dim, ATTN_DTYPE_BF16) the call returns ATTN_EWORKSPACE before any HIP call
  *   out      device, (B, Hq, head_dim) bfloat16, 16-byte aligned (written)
  *   lse      device, (B, Hq) float32, natural log (written)
  *   workspace  device, >= attn_decode_workspace_bytes(...) bytes, 16-byte aligned, caller owned
  *   0 <= q_pos < S_cap; Hq a multiple of Hkv
  * Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE or ATTN_EHIP as above.
  */
-int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
-                double rope_theta, int rope_style, int q_pos, void *out, float *lse,
-                void *workspace, size_t workspace_bytes, void *stream);
+int attn_decode(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq,
+                int Hkv, int head_dim, double rope_theta, int rope_style, int q_pos, void *out,
+                float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass: the gradients dq, dk, dv of attn_fwd's out for a given output gradient dout

@@ -217,11 +217,27 @@ def test_kv_prepare_rejections(over, code):
 
 
 def decode_call(**over):
-    a = dict(q=P, cache=P, B=1, S=256, Hq=8, Hkv=2, d=128, theta=1e4, pos=100, out=P, lse=P, ws=P, wsb=1 << 30,
-             stream=None, rope=0)
+    a = dict(q=P, cache=P, cb=1 << 30, B=1, S=256, Hq=8, Hkv=2, d=128, theta=1e4, pos=100, out=P, lse=P, ws=P,
+             wsb=1 << 30, stream=None, rope=0)
     a.update(over)
-    return _lib.decode_raw(a["q"], a["cache"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"], a["pos"],
-                           a["out"], a["lse"], a["ws"], a["wsb"], a["stream"], rope_style=a["rope"])
+    return _lib.decode_raw(a["q"], a["cache"], a["cb"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["theta"],
+                           a["pos"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"], rope_style=a["rope"])
+
+
+def test_decode_rejects_a_cache_smaller_than_its_layout():
+    # the cache must hold the whole layout of (B, S_cap, Hkv, d): a larger S_cap, B or Hkv than
+    # the allocation was made for is refused before any HIP call
+    need = _lib.workspace_bytes(1, 256, 2, 128, 0)
+    assert decode_call(cb=need - 1) == _lib.ATTN_EWORKSPACE
+    assert decode_call(cb=need, S=512, pos=100) == _lib.ATTN_EWORKSPACE
+    assert decode_call(cb=need, B=2) == _lib.ATTN_EWORKSPACE
+    assert decode_call(cb=need, Hq=16, Hkv=4) == _lib.ATTN_EWORKSPACE
+    assert decode_call(cb=0) == _lib.ATTN_EWORKSPACE
+
+
+def test_unsupported_message_names_every_head_dim_rule():
+    msg = _lib.strerror(_lib.ATTN_EUNSUPPORTED)
+    assert "64 or 128" in msg and "256" in msg and "backward" in msg and "float32" in msg
 
 
 @pytest.mark.parametrize("over,code", [

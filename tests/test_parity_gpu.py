@@ -85,9 +85,13 @@ def test_workload_full(name):
 
 
 def long_shard_rows(S, seed=5):
+    # 32-row blocks: both blocks of three of the pairs (r, n-1-r) that one workgroup runs (the
+    # first, the second and the middle pair), and six seeded random blocks
+    n = S // 32
+    fixed = [0, n - 1, 1, n - 2, n // 2 - 1, n // 2]
     rng = np.random.default_rng(seed)
-    blocks = [0, S // 32 - 1] + sorted(rng.choice(np.arange(1, S // 32 - 1), size=6, replace=False).tolist())
-    return np.concatenate([np.arange(32 * b, 32 * b + 32) for b in blocks])
+    rest = sorted(rng.choice(np.setdiff1d(np.arange(n), fixed), size=6, replace=False).tolist())
+    return np.concatenate([np.arange(32 * b, 32 * b + 32) for b in sorted(fixed + rest)])
 
 
 def test_long_shard_sampled_rows():

@@ -51,8 +51,12 @@ def test_cpu_baseline_record():
     from transformer_causal_attention_amd.workloads import Workload
 
     w = Workload("tiny", 1, 96, 4, 2, 64, "bf16", 1.0, 10000.0, True, 1)
-    r = bench.cpu_baseline(w, budget_s=0.4)
-    assert set(r) == {"value", "unit", "cores", "kind", "sample", "seconds"}
+    r = bench.cpu_baseline(w, budget_s=0.4, rows_per_task=32)
+    assert set(r) == {"value", "unit", "cores", "kind", "sample", "seconds", "host_cores", "blas_threads_per_worker",
+                      "workers"}
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
-    assert r["value"] > 0 and r["seconds"] >= 0.2
+    # one worker process per core of the affinity mask (at most one per task), one BLAS thread each
+    assert r["cores"] == r["workers"] == min(len(os.sched_getaffinity(0)), 4 * 3) and r["blas_threads_per_worker"] == 1
+    assert r["host_cores"] == len(os.sched_getaffinity(0))
+    assert r["value"] > 0 and r["seconds"] >= 0.4
     assert "whole passes" in r["sample"] and "tiny" in r["sample"]

@@ -32,7 +32,8 @@ _MERGE_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]
 _PREP_ARGS = [_VP, _VP, _I, _I, _I, _I, ctypes.c_double, _I, _I, _I, _VP, ctypes.c_size_t, _VP]
 _BWD_ARGS = [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, _VP,
              ctypes.c_size_t, _VP]
-_DECODE_ARGS = [_VP, _VP, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+_DECODE_ARGS = [_VP, _VP, ctypes.c_size_t, _I, _I, _I, _I, _I, ctypes.c_double, _I, _I, _VP, _VP, _VP, ctypes.c_size_t,
+                _VP]
 SIGNATURES = {
     "attn_abi_version": (_I, []),
     "attn_strerror": (ctypes.c_char_p, [_I]),
@@ -131,11 +132,11 @@ def decode_workspace_bytes(B, Hq, Hkv, head_dim):
     return load().attn_decode_workspace_bytes(B, Hq, Hkv, head_dim)
 
 
-def decode_raw(q, cache, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, out, lse, workspace, workspace_bytes_,
-               stream, rope_style=ATTN_ROPE_HALF):
+def decode_raw(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, out, lse, workspace,
+               workspace_bytes_, stream, rope_style=ATTN_ROPE_HALF):
     """Call attn_decode with raw pointers; returns the code."""
-    return load().attn_decode(q, cache, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(rope_style), int(q_pos),
-                              out, lse, workspace, workspace_bytes_, stream)
+    return load().attn_decode(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(rope_style),
+                              int(q_pos), out, lse, workspace, workspace_bytes_, stream)
 
 
 def bwd_workspace_bytes(B, S, Hq, Hkv, head_dim):

@@ -26,6 +26,16 @@ def _shapes(q, k, v):
     return B, S, Hq, Hkv, D
 
 
+def _keep_for(stream, *allocated):
+    """Tensors this wrapper allocated on the current stream but hands to kernels on `stream`: record
+    that stream on them, so the caching allocator does not reuse their memory (after the caller
+    frees them) before those kernels are done."""
+    if stream is not None:
+        for t in allocated:
+            if t is not None:
+                t.record_stream(stream)
+
+
 def _rope_style(interleaved):
     return _lib.ATTN_ROPE_INTERLEAVED if interleaved else _lib.ATTN_ROPE_HALF
 
@@ -85,6 +95,7 @@ def attn_fwd(q, k, v, rope_theta, causal=True, workspace=None, stream=None, even
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _keep_for(stream, out, lse)
     return attn_fwd_into(q, k, v, rope_theta, causal, out, lse, workspace, stream, events, q_pos0, k_pos0,
                          interleaved)
 
@@ -124,8 +135,10 @@ def attn_merge(o1, lse1, o2, lse2, out=None, lse=None, stream=None):
     for name, t in (("lse1", lse1), ("lse2", lse2)):
         if tuple(t.shape) != (B, H, S) or t.dtype != torch.float32 or not t.is_contiguous() or t.device != o1.device:
             raise ValueError(f"{name} must be a contiguous float32 tensor of shape (B, H, S)")
-    out = torch.empty_like(o1) if out is None else out
-    lse = torch.empty_like(lse1) if lse is None else lse
+    made = (torch.empty_like(o1) if out is None else None, torch.empty_like(lse1) if lse is None else None)
+    out = made[0] if out is None else out
+    lse = made[1] if lse is None else lse
+    _keep_for(stream, *made)
     if out.shape != o1.shape or out.dtype != o1.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor shaped and typed like o1")
     if lse.shape != lse1.shape or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -188,8 +201,11 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
     B, Hq, D = q.shape
     if cache.dtype != torch.uint8 or cache.device != q.device or not cache.is_contiguous():
         raise ValueError("cache must be a contiguous uint8 tensor on q's device")
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    made = (torch.empty_like(q) if out is None else None,
+            torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else None)
+    out = made[0] if out is None else out
+    lse = made[1] if lse is None else lse
+    _keep_for(stream, *made)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor shaped and typed like q")
     if tuple(lse.shape) != (B, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
@@ -200,8 +216,8 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         if stream is not None:
             workspace.record_stream(st)
-    rc = _lib.decode_raw(q.data_ptr(), cache.data_ptr(), B, S_cap, Hq, Hkv, D, rope_theta, q_pos, out.data_ptr(),
-                         lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream,
+    rc = _lib.decode_raw(q.data_ptr(), cache.data_ptr(), cache.numel(), B, S_cap, Hq, Hkv, D, rope_theta, q_pos,
+                         out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream,
                          rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
         raise _lib.AttnError(rc, "attn_decode")
@@ -222,9 +238,12 @@ def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None,
             raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
     if tuple(lse.shape) != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 tensor of shape (B, Hq, S)")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    made = (torch.empty_like(q) if dq is None else None, torch.empty_like(k) if dk is None else None,
+            torch.empty_like(v) if dv is None else None)
+    dq = made[0] if dq is None else dq
+    dk = made[1] if dk is None else dk
+    dv = made[2] if dv is None else dv
+    _keep_for(stream, *made)
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor shaped and typed like {name[1:]}")

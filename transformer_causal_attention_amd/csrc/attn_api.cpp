@@ -266,7 +266,7 @@ ATTN_EXPORT const char *attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size, Hq not a multiple of Hkv, bad rope_theta, rope_style or causal flag)";
-    case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, dtype bf16 or fp32, sizes within limits)";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, or 256 for the bf16 forward, shard, merge and decode calls but not the backward or float32; dtype bf16 or fp32; sizes within limits)";
     case ATTN_EHIP: return "HIP runtime error while recording an event or launching a kernel";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()";
     case ATTN_ESCRATCH: return "attn_fwd_noalloc: the call needs more workspace than the library's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
@@ -459,15 +459,18 @@ ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_
   return rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-ATTN_EXPORT int attn_decode(const void *q, const void *cache, int B, int S_cap, int Hq, int Hkv, int head_dim,
-                            double rope_theta, int rope_style, int q_pos, void *out, float *lse,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+ATTN_EXPORT int attn_decode(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq,
+                            int Hkv, int head_dim, double rope_theta, int rope_style, int q_pos, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !cache || !out || !lse) return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
   const int rc = check_decode_shape(B, S_cap, Hq, Hkv, head_dim);
   if (rc != ATTN_OK) return rc;
   if (!std::isfinite(rope_theta) || rope_theta <= 0.0 || !rope_style_ok(rope_style)) return ATTN_EINVAL;
   if (q_pos < 0 || q_pos >= S_cap) return ATTN_EINVAL;
+  // the kernels address the V^T half at B * Hkv * S_cap (padded) * head_dim past the start: the
+  // cache must hold the whole layout for these sizes
+  if (cache_bytes < attn_fwd_workspace_bytes(B, S_cap, Hkv, head_dim, ATTN_DTYPE_BF16)) return ATTN_EWORKSPACE;
   const size_t need = attn_decode_workspace_bytes(B, Hq, Hkv, head_dim);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_EWORKSPACE;
   const size_t s_pad = padded_len(S_cap);
