@@ -5,6 +5,7 @@ from .attn_oracle import (  # noqa: F401
     apply_rope_interleaved,
     attention,
     attention_backward,
+    attention_backward_shard,
     merge,
     attention_weights,
     causal_mask,

@@ -283,3 +283,64 @@ def attention_backward(q, k, v, dout, rope_theta, causal=True, interleaved=False
     dq = rope(dq_rot, -pos, rope_theta)
     dk = rope(dk_rot, -pos, rope_theta)
     return dq, dk, dv
+
+
+def attention_backward_shard(q, k, v, dout, out, lse, rope_theta, causal=True, q_pos0=0, k_pos0=0,
+                             interleaved=False):
+    """The part of the gradients that one block of keys contributes, for one block of queries,
+    given the finished forward of those queries over every key block: one step of the backward
+    of ring attention, which the Picotron page runs as an autograd function ("context
+    parallelism and ring attention"; the pages print no backward, so this is the derivative of
+    the definition restricted to one key block).
+
+    q, dout: (B, S, Hq, d) at query positions q_pos0 + i; k, v: (B, S, Hkv, d) at key positions
+    k_pos0 + j; out (B, S, Hq, d) and lse (B, Hq, S): the forward's results for these queries
+    over all keys (for one block alone, attention()'s own).  With the weights of this block's
+    keys taken from the whole softmax, P = exp(s - lse) (0 where masked, and for a row whose lse
+    is -inf), the chain rule of out = sum over blocks of P v gives
+      dv_g += P^T dout,   dP = dout v^T,   ds = P * (dP - rowsum(dout * out)),
+      dq' = ds k' / sqrt(d),   dk'_g += ds^T q' / sqrt(d),   dx = R(-position) dx'.
+    Summed over key blocks, dq is the full dq; summed over query blocks, dk and dv are.
+    Returns dq (B, S, Hq, d), dk and dv (B, S, Hkv, d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, d) or v.shape != k.shape or dout.shape != q.shape or out.shape != q.shape:
+        raise ValueError("k, v must be (B, S, Hkv, d); dout and out like q")
+    if lse.shape != (B, Hq, S):
+        raise ValueError("lse must be (B, Hq, S)")
+    q_positions = q_pos0 + np.arange(S)
+    k_positions = k_pos0 + np.arange(S)
+    rope = apply_rope_interleaved if interleaved else apply_rope
+    q_rot = rope(q, q_positions, rope_theta)
+    k_rot = rope(k, k_positions, rope_theta)
+    scale = 1.0 / np.sqrt(np.float64(d))
+
+    dq_rot = np.zeros_like(q_rot)
+    dk_rot = np.zeros_like(k_rot)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            scores = (q_rot[b, :, h, :] @ k_rot[b, :, g, :].T) * scale
+            if causal:
+                scores = scores + causal_mask(q_positions, S, k_pos0)
+            L = lse[b, h, :][:, None]
+            with np.errstate(invalid="ignore"):
+                P = np.where(np.isfinite(L) & np.isfinite(scores), np.exp(scores - np.where(np.isfinite(L), L, 0.0)),
+                             0.0)
+            do = dout[b, :, h, :]
+            dv[b, :, g, :] += P.T @ do
+            dP = do @ v[b, :, g, :].T
+            ds = P * (dP - (do * out[b, :, h, :]).sum(axis=-1, keepdims=True))
+            dq_rot[b, :, h, :] = (ds @ k_rot[b, :, g, :]) * scale
+            dk_rot[b, :, g, :] += (ds.T @ q_rot[b, :, h, :]) * scale
+    dq = rope(dq_rot, -q_positions, rope_theta)
+    dk = rope(dk_rot, -k_positions, rope_theta)
+    return dq, dk, dv

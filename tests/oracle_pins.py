@@ -465,6 +465,68 @@ def pin_backward_row0_dq_zero():
     assert np.abs(dq[:, 1:]).max() > 1e-3, "later dq rows must not vanish"
 
 
+def pin_backward_shard_single_block():
+    """One block holding the whole sequence, with the forward's own out and lse, is the plain
+    backward."""
+    rng = np.random.default_rng(41)
+    q, k, v = _rand(rng, 2, 24, 4, 8), _rand(rng, 2, 24, 2, 8), _rand(rng, 2, 24, 2, 8)
+    do = _rand(rng, 2, 24, 4, 8)
+    for causal, il in ((True, False), (False, False), (True, True)):
+        out, lse = O.attention(q, k, v, 300.0, causal, interleaved=il)
+        got = O.attention_backward_shard(q, k, v, do, out, lse, 300.0, causal, interleaved=il)
+        want = O.attention_backward(q, k, v, do, 300.0, causal, interleaved=il)
+        for n, a, b in zip("qkv", got, want):
+            _close(a, b, 1e-12, f"single-block shard d{n}, causal {causal}, interleaved {il}")
+
+
+def pin_backward_ring_split():
+    """The backward of ring attention: split the sequence into 3 blocks; each (query block, key
+    block) step at its offsets, with the full forward's out and lse for its queries, gives a part
+    of the gradients; dq summed over key blocks and dk, dv summed over query blocks equal the
+    plain backward of the whole sequence (finite-difference pinned)."""
+    rng = np.random.default_rng(42)
+    S, n = 48, 16
+    for causal, il in ((True, False), (False, False), (True, True)):
+        q, k, v = _rand(rng, 1, S, 4, 8), _rand(rng, 1, S, 2, 8), _rand(rng, 1, S, 2, 8)
+        do = _rand(rng, 1, S, 4, 8)
+        out, lse = O.attention(q, k, v, 1000.0, causal, interleaved=il)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for a in range(3):
+            qa = slice(a * n, (a + 1) * n)
+            for c in range(3):
+                kc = slice(c * n, (c + 1) * n)
+                gq, gk, gv = O.attention_backward_shard(q[:, qa], k[:, kc], v[:, kc], do[:, qa], out[:, qa],
+                                                        lse[:, :, qa], 1000.0, causal, q_pos0=a * n, k_pos0=c * n,
+                                                        interleaved=il)
+                if causal and c > a:
+                    assert not gq.any() and not gk.any() and not gv.any(), "a later key block has no gradient"
+                dq[:, qa] += gq
+                dk[:, kc] += gk
+                dv[:, kc] += gv
+        want = O.attention_backward(q, k, v, do, 1000.0, causal, interleaved=il)
+        for nm, a_, b_ in zip("qkv", (dq, dk, dv), want):
+            _close(a_, b_, 1e-12, f"ring backward d{nm}, causal {causal}, interleaved {il}")
+
+
+def pin_backward_shard_shift_invariance():
+    """Moving both blocks by the same number of positions changes no gradient: the scores and
+    the mask depend on position differences, and each rotation back undoes its own angle."""
+    rng = np.random.default_rng(43)
+    q, k, v = _rand(rng, 1, 20, 2, 8), _rand(rng, 1, 20, 1, 8), _rand(rng, 1, 20, 1, 8)
+    do = _rand(rng, 1, 20, 2, 8)
+    out, lse = O.attention(q, k, v, 700.0, True, q_pos0=21, k_pos0=30)
+    g0 = O.attention_backward_shard(q, k, v, do, out, lse, 700.0, True, q_pos0=21, k_pos0=30)
+    out1, lse1 = O.attention(q, k, v, 700.0, True, q_pos0=21 + 55, k_pos0=30 + 55)
+    g1 = O.attention_backward_shard(q, k, v, do, out1, lse1, 700.0, True, q_pos0=21 + 55, k_pos0=30 + 55)
+    for n, a, b in zip("qkv", g0, g1):
+        _close(a, b, 1e-12, f"shifted shard d{n}")
+    # rows 0..8 see no key of this block (their lse is -inf): no gradient flows through them,
+    # and keys 11.. are seen by no row
+    assert np.all(lse[:, :, :9] == -np.inf) and np.isfinite(lse[:, :, 9:]).all()
+    assert not g0[0][:, :9].any() and np.abs(g0[0][:, 9:]).max() > 1e-3
+    assert not g0[1][:, 11:].any() and not g0[2][:, 11:].any()
+
+
 ALL_PINS = [
     pin_bruteforce,
     pin_rows_sum_to_one,
@@ -489,5 +551,8 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_dv_sums_to_dout,
     pin_backward_row0_dq_zero,
+    pin_backward_shard_single_block,
+    pin_backward_ring_split,
+    pin_backward_shard_shift_invariance,
     pin_golden,
 ]

@@ -195,6 +195,43 @@ def _backward_variant(*, drop_rowsum=False, rope_forward_sign=False, no_scale=Fa
     return attention_backward
 
 
+def _shard_backward_variant(*, mask_no_key_offset=False, dq_back_no_offset=False, dk_back_no_offset=False,
+                            block_softmax=False):
+    def attention_backward_shard(q, k, v, dout, out, lse, rope_theta, causal=True, q_pos0=0, k_pos0=0,
+                                 interleaved=False):
+        q, k, v, dout, out, lse = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout, out, lse))
+        B, S, Hq, d = q.shape
+        Hkv = k.shape[2]
+        qp, kp = q_pos0 + np.arange(S), k_pos0 + np.arange(S)
+        rope = O.apply_rope_interleaved if interleaved else O.apply_rope
+        q_rot, k_rot = rope(q, qp, rope_theta), rope(k, kp, rope_theta)
+        scale = 1.0 / np.sqrt(np.float64(d))
+        dq_rot, dk_rot, dv = np.zeros_like(q_rot), np.zeros_like(k_rot), np.zeros_like(v)
+        for b in range(B):
+            for h in range(Hq):
+                g = O.kv_head_of(h, Hq, Hkv)
+                sc = (q_rot[b, :, h] @ k_rot[b, :, g].T) * scale
+                if causal:
+                    sc = sc + O.causal_mask(qp, S, 0 if mask_no_key_offset else k_pos0)
+                if block_softmax:
+                    P, _, _ = O.softmax_rows(sc)
+                else:
+                    L = lse[b, h][:, None]
+                    with np.errstate(invalid="ignore"):
+                        P = np.where(np.isfinite(L) & np.isfinite(sc), np.exp(sc - np.where(np.isfinite(L), L, 0.0)),
+                                     0.0)
+                do = dout[b, :, h]
+                dv[b, :, g] += P.T @ do
+                ds = P * (do @ v[b, :, g].T - (do * out[b, :, h]).sum(axis=-1, keepdims=True))
+                dq_rot[b, :, h] = (ds @ k_rot[b, :, g]) * scale
+                dk_rot[b, :, g] += (ds.T @ q_rot[b, :, h]) * scale
+        dq = rope(dq_rot, -(np.arange(S) if dq_back_no_offset else qp), rope_theta)
+        dk = rope(dk_rot, -(np.arange(S) if dk_back_no_offset else kp), rope_theta)
+        return dq, dk, dv
+
+    return attention_backward_shard
+
+
 def _rope_interleaved_half_split(x, positions, rope_theta):
     return O.apply_rope(x, positions, rope_theta)
 
@@ -242,6 +279,13 @@ MUTATIONS = {
     "backward_scale_dropped": ("attention_backward", _backward_variant(no_scale=True)),
     "backward_dk_untransposed": ("attention_backward", _backward_variant(ds_untransposed=True)),
     "backward_dv_untransposed": ("attention_backward", _backward_variant(dv_untransposed=True)),
+    "shard_backward_mask_ignores_key_offset": ("attention_backward_shard",
+                                               _shard_backward_variant(mask_no_key_offset=True)),
+    "shard_backward_dq_rotated_back_at_row": ("attention_backward_shard",
+                                              _shard_backward_variant(dq_back_no_offset=True)),
+    "shard_backward_dk_rotated_back_at_row": ("attention_backward_shard",
+                                              _shard_backward_variant(dk_back_no_offset=True)),
+    "shard_backward_block_softmax": ("attention_backward_shard", _shard_backward_variant(block_softmax=True)),
     "interleaved_is_half_split": ("apply_rope_interleaved", _rope_interleaved_half_split),
     "interleaved_wrong_sign": ("apply_rope_interleaved", _rope_interleaved_sign),
 }
