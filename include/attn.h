@@ -262,6 +262,25 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *out, const
              int rope_style, int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
              void *stream);
 
+/*
+ * One step of the backward of ring attention (Picotron page, "context parallelism and ring
+ * attention", where the ring is an autograd function): attn_bwd for queries at positions
+ * q_pos0 .. q_pos0+S-1 against keys and values at k_pos0 .. k_pos0+S-1, with the visibility and
+ * rotations of attn_fwd_shard.  out and lse must be the forward's results for these queries
+ * over ALL key blocks (the merged ones, as attn_merge leaves them), so that the weights of this
+ * block's keys are the full softmax's: P = exp(s - lse), 0 where masked.  The results are this
+ * pair of blocks' parts of the gradients: dq summed over the key blocks a query block sees, and
+ * dk, dv summed over the query blocks that see a key block, equal the gradients of the whole
+ * sequence.  A row whose lse is -inf (it sees no key at all) contributes nothing.  attn_bwd is
+ * this call with q_pos0 = k_pos0 = 0.
+ *   q_pos0, k_pos0  >= 0, with q_pos0 + S and k_pos0 + S at most 2^30 (else ATTN_EINVAL)
+ *   other arguments, workspace size and return codes as for attn_bwd
+ */
+int attn_bwd_shard(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                   const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
+                   int rope_style, int causal, int q_pos0, int k_pos0, void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Timing events (hipEvent_t behind an opaque pointer).  create returns NULL on failure. */
 void *attn_event_create(void);
 int attn_event_destroy(void *ev);

@@ -48,6 +48,7 @@ SIGNATURES = {
     "attn_decode": (_I, _DECODE_ARGS),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "attn_bwd": (_I, _BWD_ARGS),
+    "attn_bwd_shard": (_I, _BWD_ARGS[:14] + [_I, _I] + _BWD_ARGS[14:]),
     "attn_event_create": (_VP, []),
     "attn_event_destroy": (_I, [_VP]),
     "attn_event_elapsed_ms": (_I, [_VP, _VP, ctypes.POINTER(ctypes.c_float)]),
@@ -148,6 +149,13 @@ def bwd_raw(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, rope_theta, causal
     """Call attn_bwd with raw pointers; returns the code."""
     return load().attn_bwd(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style),
                            int(causal), dq, dk, dv, workspace, workspace_bytes_, stream)
+
+
+def bwd_shard_raw(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, rope_theta, causal, q_pos0, k_pos0, dq, dk, dv,
+                  workspace, workspace_bytes_, stream, rope_style=ATTN_ROPE_HALF):
+    """Call attn_bwd_shard with raw pointers; returns the code."""
+    return load().attn_bwd_shard(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, float(rope_theta), int(rope_style),
+                                 int(causal), int(q_pos0), int(k_pos0), dq, dk, dv, workspace, workspace_bytes_, stream)
 
 
 class Event:

@@ -225,10 +225,14 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
 
 
 def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None, dv=None, workspace=None,
-             stream=None, interleaved=False):
+             stream=None, interleaved=False, q_pos0=0, k_pos0=0):
     """Gradients (dq, dk, dv) of attn_fwd's out for the output gradient dout (bf16).
 
     out, lse: attn_fwd's results for the same q, k, v, rope_theta, causal and interleaved.
+    With q_pos0 / k_pos0 the call is one step of ring attention's backward (attn_bwd_shard):
+    out and lse must then be the merged forward results of these queries over every key block,
+    and the returned gradients are this pair of blocks' parts (dq summed over key blocks, dk and
+    dv over query blocks give the whole sequence's).
     """
     B, S, Hq, Hkv, D = _shapes(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -252,9 +256,10 @@ def attn_bwd(q, k, v, out, lse, dout, rope_theta, causal=True, dq=None, dk=None,
         workspace = torch.empty(_lib.bwd_workspace_bytes(B, S, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
         if stream is not None:
             workspace.record_stream(st)
-    rc = _lib.bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                      B, S, Hq, Hkv, D, rope_theta, 1 if causal else 0, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      workspace.data_ptr(), workspace.numel(), st.cuda_stream, rope_style=_rope_style(interleaved))
+    rc = _lib.bwd_shard_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), B, S, Hq, Hkv, D, rope_theta, 1 if causal else 0, q_pos0, k_pos0,
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                            st.cuda_stream, rope_style=_rope_style(interleaved))
     if rc != _lib.ATTN_OK:
-        raise _lib.AttnError(rc, "attn_bwd")
+        raise _lib.AttnError(rc, "attn_bwd_shard" if (q_pos0 or k_pos0) else "attn_bwd")
     return dq, dk, dv

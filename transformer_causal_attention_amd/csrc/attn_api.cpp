@@ -520,11 +520,13 @@ ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int h
   return 3 * (size_t)B * Hkv * nb * tile + 4 * (size_t)B * Hq * nb * tile + 2 * (size_t)B * Hq * nb * kBwdRows * 4;
 }
 
-ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
-                         const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
-                         int rope_style, int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+ATTN_EXPORT int attn_bwd_shard(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                               const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
+                               int rope_style, int causal, int q_pos0, int k_pos0, void *dq, void *dk, void *dv,
+                               void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (q_pos0 < 0 || k_pos0 < 0 || (long long)q_pos0 + S > (1LL << 30) || (long long)k_pos0 + S > (1LL << 30))
+    return ATTN_EINVAL;
   for (const void *ptr : {q, k, v, out, dout, (const void *)dq, (const void *)dk, (const void *)dv})
     if (!aligned(ptr, 16)) return ATTN_EINVAL;
   if (!aligned(lse, 4) || !rope_style_ok(rope_style)) return ATTN_EINVAL;
@@ -566,12 +568,22 @@ ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void
   p.n_pairs = (int)((nb + 1) / 2);
   p.W = std::min(G, 4);
   p.causal = causal;
+  p.q_pos0 = q_pos0;
+  p.k_pos0 = k_pos0;
   p.scale_log2 = q_scale(head_dim);
   p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)head_dim));
   const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t err = head_dim == 64 ? attn::launch_bwd<64>(p, tab, st) : attn::launch_bwd<128>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+ATTN_EXPORT int attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                         const void *dout, int B, int S, int Hq, int Hkv, int head_dim, double rope_theta,
+                         int rope_style, int causal, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  return attn_bwd_shard(q, k, v, out, lse, dout, B, S, Hq, Hkv, head_dim, rope_theta, rope_style, causal, 0, 0, dq, dk,
+                        dv, workspace, workspace_bytes, stream);
 }
 
 ATTN_EXPORT int attn_event_destroy(void *ev) {

@@ -21,6 +21,12 @@
 //               each row is written once (no atomics);
 //   bwd_dq      one wave per (b, query head, pair of query blocks): S^T = K Q^T and
 //               dP^T = V dO^T with one query per lane, dq += dS K; rotated back and written.
+// A call may be one block of a longer sequence (one step of ring attention's backward): queries
+// at positions q_pos0 + i, keys at k_pos0 + j, key j visible to query i iff j <= i + delta with
+// delta = q_pos0 - k_pos0; out and lse are then the forward's results over every key block, and
+// dq (dk, dv) is this key block's (query block's) part of the gradient.  Block kb of keys is seen
+// by query blocks from qb_lo(kb) on, query block qb sees key blocks below kb_end(qb), and a
+// block pair needs the element mask only where some key is later than some row.
 // Causal work is balanced by pairing block kb with NB-1-kb.  Operands are read straight from
 // the pre-laid-out tiles into registers (16-byte loads, each a whole MFMA operand per lane), so
 // no LDS is needed outside the dk/dv reduction and the layout passes.
@@ -52,6 +58,9 @@ __device__ __forceinline__ int xcd_order(int i, int n) {
 }
 
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// floor(a / b) for b > 0 and any sign of a
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
@@ -132,7 +141,7 @@ __global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable 
       vy = *reinterpret_cast<const u32x4 *>(p.v + src + D / 2);
     }
     float x[8], y[8];
-    rotate8<D>(tab, c, r, kx, ky, x, y);
+    rotate8<D>(tab, c, p.k_pos0 + r, kx, ky, x, y);
     const u32x4 wx = r < p.S ? pack8(x, 1.f) : u32x4{0u, 0u, 0u, 0u};
     const u32x4 wy = r < p.S ? pack8(y, 1.f) : u32x4{0u, 0u, 0u, 0u};
     // c layout: chunk c at [c][row][8]
@@ -179,7 +188,7 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
       oy = *reinterpret_cast<const u32x4 *>(p.out + src + D / 2);
     }
     float x[8], y[8];
-    rotate8<D>(tab, c, r, qx, qy, x, y);
+    rotate8<D>(tab, c, p.q_pos0 + r, qx, qy, x, y);
     const u32x4 zero = {0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4 *>(p.qc + tile + ((size_t)c * BR + row) * 8) = ok ? pack8(x, p.scale_log2) : zero;
     *reinterpret_cast<u32x4 *>(p.qc + tile + ((size_t)(c + NCH) * BR + row) * 8) = ok ? pack8(y, p.scale_log2) : zero;
@@ -202,7 +211,10 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
     if (c == 0) {
       const size_t ri = (size_t)unit * p.NB * BR + (size_t)qb * BR + row;
       p.dd[ri] = ok ? acc : 0.f;
-      p.l2[ri] = ok ? p.lse[((size_t)b * p.Hq + h) * p.S + r] * 1.4426950408889634f : INFINITY;
+      // a row with no visible key (lse -inf) has no gradient: +inf makes its weights 0 as for
+      // rows past S
+      const float lr = ok ? p.lse[((size_t)b * p.Hq + h) * p.S + r] : INFINITY;
+      p.l2[ri] = lr == -INFINITY ? INFINITY : lr * 1.4426950408889634f;
     }
   }
   __syncthreads();
@@ -250,7 +262,9 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
     // query-block operands, two sets (see the dq kernel)
     bf16x8 qa[2][NKK], da[2][NKK], tb[2][2][NCB];
     f32x4 L[2][4], Dd[2][4];
-    const int qb_lo = p.causal ? kb : 0;
+    const int delta = p.q_pos0 - p.k_pos0;
+    // the first query block with a row that sees a key of this block: 32 qb + 31 + delta >= 32 kb
+    const int qb_lo = p.causal ? max(0, floor_div(BR * kb - delta, BR)) : 0;
     for (int hc = wave; hc < p.G; hc += p.W) {
       const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
       auto load_q = [&](int qb, int buf) __attribute__((always_inline)) {
@@ -281,7 +295,9 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
           s = bwd_mfma(qa[buf][kk], kf[kk], s);
           if (!DV) dp = bwd_mfma(da[buf][kk], vf[kk], dp);
         }
-        const bool diag = p.causal && qb == kb;
+        // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel
+        const int rel = BR * (qb - kb) + delta;
+        const bool partial = p.causal && rel < BR - 1;
         bf16x8 op[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -293,7 +309,7 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
             for (int z = 0; z < 2; ++z) {
               const int v = 8 * tt + e + z;
               float pr = __builtin_amdgcn_exp2f(s[v] - L[buf][v >> 2][v & 3]);
-              if (!key_ok || (diag && l32 > res_row(v, hh))) pr = 0.f;
+              if (!key_ok || (partial && l32 - res_row(v, hh) > rel)) pr = 0.f;
               x[z] = DV ? pr : pr * (dp[v] - Dd[buf][v >> 2][v & 3]);
             }
             wv[e / 2] = pack_bf16x2(x[0], x[1]);
@@ -342,7 +358,7 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = kb * BR + res_row(v, hh);
-            const float t = turn_fraction(key, rev);
+            const float t = turn_fraction(p.k_pos0 + key, rev);
             const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
             const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
             acc[cb][v] = x * cs + y * sn;
@@ -401,7 +417,9 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
     f32x16 dq[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
-    const int kb_end = p.causal ? qb + 1 : p.NB;
+    const int delta = p.q_pos0 - p.k_pos0;
+    // key blocks with a key some row of this block sees: 32 kb <= 32 qb + 31 + delta
+    const int kb_end = p.causal ? min(p.NB, max(0, floor_div(BR * qb + BR - 1 + delta, BR) + 1)) : p.NB;
     // key-block operands, two sets: the next block's are loaded while the current one is used
     // (the index is clamped, so the last step re-reads its own block instead of branching)
     bf16x8 ka[2][NKK], va[2][NKK], kt[2][2][NCB];
@@ -425,7 +443,9 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
         st = bwd_mfma(ka[buf][kk], qf[kk], st);
         dpt = bwd_mfma(va[buf][kk], df[kk], dpt);
       }
-      const bool diag = p.causal && kb == qb;
+      // key kb*32 + k is later than row qb*32 + l32 iff k - l32 > rel
+      const int rel = BR * (qb - kb) + delta;
+      const bool partial = p.causal && rel < BR - 1;
       bf16x8 sa[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -438,7 +458,7 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
             const int v = 8 * tt + e + z;
             const int key = res_row(v, hh);  // within the block
             float pr = __builtin_amdgcn_exp2f(st[v] - Lq);
-            if (kb * BR + key >= p.S || (diag && key > l32)) pr = 0.f;
+            if (kb * BR + key >= p.S || (partial && key - l32 > rel)) pr = 0.f;
             sv[z] = pr * (dpt[v] - Dq);
           }
           ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
@@ -466,7 +486,7 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = qb * BR + res_row(v, hh);
-        const float t = turn_fraction(row, rev);
+        const float t = turn_fraction(p.q_pos0 + row, rev);
         const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
         const float x = dq[cb][v] * p.inv_sqrt_d, y = dq[cb + NCB / 2][v] * p.inv_sqrt_d;
         dq[cb][v] = x * cs + y * sn;

@@ -152,6 +152,7 @@ struct BwdParams {
                               // q / sqrt(D) (t), dout (c, t)
   float *l2, *dd;           // (B, Hq, NB*32): lse * log2(e) (+inf past S); rowsum(dout * out)
   int B, S, Hq, Hkv, G, NB, n_pairs, W, causal;
+  int q_pos0, k_pos0;       // positions of query row 0 and key row 0 (a sequence shard's offsets)
   float scale_log2;         // log2(e) / sqrt(D)
   float inv_sqrt_d;         // 1 / sqrt(D)
 };
