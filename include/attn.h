@@ -238,6 +238,23 @@ int attn_decode(const void *q, const void *cache, size_t cache_bytes, int B, int
                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode for a ragged batch, where each batch row has generated a different number of
+ * tokens (the PaLM page's generation loop, section 2.7, run over a batch of sequences of
+ * different lengths): batch row b's query sits at position q_pos[b] and attends to its own
+ * cached keys 0 .. q_pos[b].  Arguments as for attn_decode, except
+ *   q_pos    device, B int32 positions, 4-byte aligned, read by the kernel (so a serving loop
+ *            can advance them on the GPU without a host round trip)
+ *   max_pos  0 <= max_pos < S_cap, at least every q_pos[b]: it sizes the key ranges the work is
+ *            split into; ranges past a row's position are empty.  A row whose q_pos[b] lies
+ *            outside [0, max_pos] gets NaN in out and lse (checked on the GPU).
+ * Returns the codes of attn_decode (ATTN_EINVAL also for a null or misaligned q_pos).
+ */
+int attn_decode_ragged(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap,
+                       int Hq, int Hkv, int head_dim, double rope_theta, int rope_style,
+                       const int *q_pos, int max_pos, void *out, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
  * Backward pass: the gradients dq, dk, dv of attn_fwd's out for a given output gradient dout
  * (the pages train these models -- PaLM-in-ColossalAI page, section 2.7, a cross-entropy
  * training loss -- and a training step needs them).  With P = softmax of the scaled, masked

@@ -295,3 +295,19 @@ def test_noalloc_rejections_before_any_hip_call():
     assert lib.attn_fwd_noalloc(None, P, P, 1, 64, 4, 1, 64, 1e4, 0, 1, 0, P, P, None) == _lib.ATTN_EINVAL
     assert lib.attn_fwd_noalloc(P, P, P, 1, 64, 4, 1, 96, 1e4, 0, 1, 0, P, P, None) == _lib.ATTN_EUNSUPPORTED
     assert "scratch" in _lib.strerror(_lib.ATTN_ESCRATCH)
+
+
+def test_decode_ragged_rejections_before_any_hip_call():
+    lib = _lib.load()
+    args = lambda **o: dict(dict(q=P, cache=P, cb=1 << 30, B=2, S=256, Hq=8, Hkv=2, d=128, th=1e4, rope=0, qp=P,  # noqa: E731
+                                 mp=100, out=P, lse=P, ws=P, wsb=1 << 30, st=None), **o)
+    call_r = lambda a: _lib.decode_ragged_raw(a["q"], a["cache"], a["cb"], a["B"], a["S"], a["Hq"], a["Hkv"],  # noqa: E731
+                                              a["d"], a["th"], a["qp"], a["mp"], a["out"], a["lse"], a["ws"],
+                                              a["wsb"], a["st"], rope_style=a["rope"])
+    assert call_r(args(qp=None)) == _lib.ATTN_EINVAL
+    assert call_r(args(qp=P + 2)) == _lib.ATTN_EINVAL
+    assert call_r(args(mp=256)) == _lib.ATTN_EINVAL  # max_pos must be below S_cap
+    assert call_r(args(mp=-1)) == _lib.ATTN_EINVAL
+    assert call_r(args(cb=16)) == _lib.ATTN_EWORKSPACE
+    assert call_r(args(d=96)) == _lib.ATTN_EUNSUPPORTED
+    assert lib is not None

@@ -46,6 +46,7 @@ SIGNATURES = {
     "attn_kv_prepare": (_I, _PREP_ARGS),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_decode": (_I, _DECODE_ARGS),
+    "attn_decode_ragged": (_I, _DECODE_ARGS[:10] + [_VP, _I] + _DECODE_ARGS[11:]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "attn_bwd": (_I, _BWD_ARGS),
     "attn_bwd_shard": (_I, _BWD_ARGS[:14] + [_I, _I] + _BWD_ARGS[14:]),
@@ -138,6 +139,14 @@ def decode_raw(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, rope_theta, q
     """Call attn_decode with raw pointers; returns the code."""
     return load().attn_decode(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, float(rope_theta), int(rope_style),
                               int(q_pos), out, lse, workspace, workspace_bytes_, stream)
+
+
+def decode_ragged_raw(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, rope_theta, q_pos, max_pos, out, lse,
+                      workspace, workspace_bytes_, stream, rope_style=ATTN_ROPE_HALF):
+    """Call attn_decode_ragged (q_pos: device pointer to B int32 positions); returns the code."""
+    return load().attn_decode_ragged(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, float(rope_theta),
+                                     int(rope_style), q_pos, int(max_pos), out, lse, workspace, workspace_bytes_,
+                                     stream)
 
 
 def bwd_workspace_bytes(B, S, Hq, Hkv, head_dim):

@@ -192,10 +192,13 @@ def kv_prepare(k, v, rope_theta, key0, key1, cache, stream=None, interleaved=Fal
 
 
 def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, workspace=None, stream=None,
-                interleaved=False):
+                interleaved=False, max_pos=None):
     """One decode step: q (B, Hq, D) bfloat16 at position q_pos against cached keys 0 .. q_pos.
 
     Returns (out (B, Hq, D) bfloat16, lse (B, Hq) float32), equal to row q_pos of attn_fwd.
+    q_pos may also be an int32 GPU tensor of B positions, one per batch row (a ragged batch,
+    attn_decode_ragged); max_pos bounds them (default S_cap - 1, which needs no host read of
+    the positions but splits the keys for the longest possible row).
     """
     _gpu_bf16("q", q, 3)
     B, Hq, D = q.shape
@@ -216,6 +219,17 @@ def attn_decode(q, cache, S_cap, Hkv, rope_theta, q_pos, out=None, lse=None, wor
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         if stream is not None:
             workspace.record_stream(st)
+    if isinstance(q_pos, torch.Tensor):
+        if (q_pos.dtype != torch.int32 or q_pos.device != q.device or tuple(q_pos.shape) != (B,)
+                or not q_pos.is_contiguous()):
+            raise ValueError("q_pos must be an int32 GPU tensor of shape (B,) on q's device")
+        bound = S_cap - 1 if max_pos is None else int(max_pos)
+        rc = _lib.decode_ragged_raw(q.data_ptr(), cache.data_ptr(), cache.numel(), B, S_cap, Hq, Hkv, D, rope_theta,
+                                    q_pos.data_ptr(), bound, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), st.cuda_stream, rope_style=_rope_style(interleaved))
+        if rc != _lib.ATTN_OK:
+            raise _lib.AttnError(rc, "attn_decode_ragged")
+        return out, lse
     rc = _lib.decode_raw(q.data_ptr(), cache.data_ptr(), cache.numel(), B, S_cap, Hq, Hkv, D, rope_theta, q_pos,
                          out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), st.cuda_stream,
                          rope_style=_rope_style(interleaved))

@@ -459,9 +459,13 @@ ATTN_EXPORT size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int head_
   return rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
-ATTN_EXPORT int attn_decode(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq,
-                            int Hkv, int head_dim, double rope_theta, int rope_style, int q_pos, void *out,
-                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// attn_decode and attn_decode_ragged: q_pos is the batch's position, or with q_pos_rows the
+// largest position a row may have.
+int decode_impl(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq, int Hkv,
+                int head_dim, double rope_theta, int rope_style, int q_pos, const int *q_pos_rows, void *out,
+                float *lse, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !cache || !out || !lse) return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_EINVAL;
   const int rc = check_decode_shape(B, S_cap, Hq, Hkv, head_dim);
@@ -487,6 +491,7 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, size_t cache_bytes
   p.G = G;
   p.S_pad = (int)s_pad;
   p.q_pos = q_pos;
+  p.q_pos_rows = q_pos_rows;
   p.n_hblk = decode_hblk(G);
   const int halves = (q_pos + 1 + 31) / 32;
   const int max_split = std::max(1, std::min(decode_max_splits(B, Hkv, G, head_dim), halves / kDecodeMinHalves));
@@ -503,6 +508,24 @@ ATTN_EXPORT int attn_decode(const void *q, const void *cache, size_t cache_bytes
                          : head_dim == 128 ? attn::launch_decode<128>(p, tab, st)
                                            : attn::launch_decode<256>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_decode(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq,
+                            int Hkv, int head_dim, double rope_theta, int rope_style, int q_pos, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, rope_theta, rope_style, q_pos, nullptr, out,
+                     lse, workspace, workspace_bytes, stream);
+}
+
+ATTN_EXPORT int attn_decode_ragged(const void *q, const void *cache, size_t cache_bytes, int B, int S_cap, int Hq,
+                                   int Hkv, int head_dim, double rope_theta, int rope_style, const int *q_pos,
+                                   int max_pos, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  if (!q_pos || !aligned(q_pos, 4)) return ATTN_EINVAL;
+  return decode_impl(q, cache, cache_bytes, B, S_cap, Hq, Hkv, head_dim, rope_theta, rope_style, max_pos, q_pos, out,
+                     lse, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -94,7 +94,17 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
   const int g = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  const int key_end0 = p.q_pos + 1;  // keys 0 .. q_pos are visible
+  // the row's position: the batch's, or (ragged batch) the row's own, which must lie in
+  // [0, q_pos]; a position outside makes the row's partials NaN, so its out and lse are NaN.
+  // Key ranges past a row's position are empty (m = -inf, l = 0, o = 0).
+  int qp = p.q_pos;
+  bool bad_pos = false;
+  if (p.q_pos_rows != nullptr) {
+    qp = p.q_pos_rows[b];
+    bad_pos = qp < 0 || qp > p.q_pos;
+    if (bad_pos) qp = 0;
+  }
+  const int key_end0 = qp + 1;  // keys 0 .. qp are visible
   const int h_begin = split * p.halves_per_split;
   const int h_end = min((key_end0 + 31) / 32, h_begin + p.halves_per_split);
   const int key_end = min(key_end0, 32 * h_end);  // first key past this split's range
@@ -193,7 +203,7 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
         // both lane halves' frequencies at wave-uniform indices (scalar loads, which the
         // cache loads in flight do not hold up), then this lane's
         const double f0 = tab.rev[16 * kk + e], f1 = tab.rev[16 * kk + 8 + e];
-        const float t = turn_fraction(p.q_pos, hh ? f1 : f0);
+        const float t = turn_fraction(qp, hh ? f1 : f0);
         const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);  // turns
         const uint32_t lo = raw[j][ww], hi = raw[j + NKW / 2][ww];
         const float xv = z ? bf16_hi(lo) : bf16_lo(lo);
@@ -217,7 +227,7 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
   // Steps past h_end (padding to a multiple of PD) load zeros and have every key masked, so the
   // loop body needs no branch around its loads.  Both waves of a workgroup see the same key
   // range, so they meet at the same barriers.
-  const int n_steps = (h_end - h_begin + PD - 1) / PD * PD;
+  const int n_steps = (max(0, h_end - h_begin) + PD - 1) / PD * PD;
   for (int s0 = 0; s0 < n_steps; s0 += PD) {
 #pragma unroll
     for (int r = 0; r < PD; ++r) {
@@ -247,12 +257,31 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) >= key_end) sc[v] = -INFINITY;
+        // The values of those keys are zeroed too: their weight is 0, but 0 times a NaN left in
+        // the cache past a row's position (a ragged batch) would still be NaN.  Element e of the
+        // V^T operand (tt, cb) is key swap23(8 qc + e) of the 64-key tile, qc = 4 jb + 2 tt + hh
+        // its key chunk (swap23 exchanging bits 2 and 3, the accumulators' key order).
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int p0 = 8 * (4 * (h & 1) + 2 * tt + hh);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            u32x4 w = __builtin_bit_cast(u32x4, vq[r][tt][cb]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int pe = p0 + e;
+              const int key = 64 * (h >> 1) + ((pe & ~12) | ((pe & 4) << 1) | ((pe & 8) >> 1));
+              if (key >= key_end) w[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+            vq[r][tt][cb] = __builtin_bit_cast(bf16x8, w);
+          }
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
       mx = dec_max_xor32(mx);
-      // finite from the first step on: key 32 h_begin <= q_pos is in it
+      // finite from the first step on: key 32 h_begin <= qp is in it (the loop runs only then)
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -296,7 +325,7 @@ __global__ void __launch_bounds__(D == 256 ? 128 : 64) attn_decode_kernel(Decode
   const float l_tot = l_run + dec_xor32(l_run);
   if (wv == 0 && hh == 0 && head_ok) {  // both waves hold the same m and l
     const size_t prow = (unit * p.n_split + split) * p.G + hc;
-    p.pm[prow] = m_run;
+    p.pm[prow] = bad_pos ? __builtin_nanf("") : m_run;
     p.pl[prow] = l_tot;
   }
 }
@@ -325,8 +354,10 @@ __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
 
   const int sg = tid / TPR;  // row group
   const int c4 = tid % TPR;  // dimensions 4 c4 .. 4 c4 + 3
-  // every split has a visible key (its first), so each m_i is finite; a group without rows
-  // keeps m = -inf and contributes 2^(-inf) = 0 below
+  // A split past a ragged row's position is empty (m_i = -inf, l_i = 0, o_i = 0); split 0 never
+  // is, so each row's final maximum is finite.  A group without rows, or with empty ones only,
+  // keeps m = -inf and contributes 2^(-inf) = 0 below.  A factor whose maximum did not change is
+  // 1 (also when both are -inf, where 2^(m - mn) would be NaN).
   float m = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = sg; s < p.n_split; s += R) {
@@ -334,7 +365,8 @@ __global__ void __launch_bounds__(256) attn_decode_join_kernel(DecodeParams p) {
     const float ms = p.pm[r], ls = p.pl[r];
     const f32x4 os = *reinterpret_cast<const f32x4 *>(p.po + r * D + 4 * c4);
     const float mn = fmaxf(m, ms);
-    const float a = __builtin_amdgcn_exp2f(m - mn), c = __builtin_amdgcn_exp2f(ms - mn);
+    const float a = m == mn ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+    const float c = ms == mn ? 1.f : __builtin_amdgcn_exp2f(ms - mn);
     acc = acc * a + os * c;
     l = l * a + ls * c;
     m = mn;

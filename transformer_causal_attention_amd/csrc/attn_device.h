@@ -130,7 +130,9 @@ struct DecodeParams {
   float *po;         // partial outputs: (B, Hkv, n_split, G, D)
   float *pm, *pl;    // partial maxima and sums: (B, Hkv, n_split, G)
   int B, Hq, Hkv, G, S_pad;
-  int q_pos;             // the query's position; keys 0 .. q_pos are visible
+  int q_pos;             // the query's position (keys 0 .. q_pos are visible); with q_pos_rows,
+                         // the largest position any batch row may have (it sizes the key splits)
+  const int *q_pos_rows; // nullptr, or each batch row's own position (B entries, device)
   int n_hblk;            // blocks of 32 heads per K/V head: ceil(G / 32)
   int n_split;           // key ranges per (b, K/V head)
   int halves_per_split;  // 32-key half tiles per key range
