@@ -270,7 +270,8 @@ int attn_decode_ragged(const void *q, const void *cache, size_t cache_bytes, int
  *   dq; dk, dv     device, shaped like q; like k (written), 16-byte aligned
  *   workspace      device, >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned (the
  *                  re-laid-out operands), caller owned
- * bf16 only; head_dim 64 or 128.  Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED,
+ * bf16 only; head_dim 64, 128 or 256 (at 256 the kernels keep the block that stays fixed over
+ * their loop in LDS instead of registers).  Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED,
  * ATTN_EWORKSPACE or ATTN_EHIP with the meanings given for attn_fwd.
  */
 size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim);

@@ -237,7 +237,7 @@ def test_decode_rejects_a_cache_smaller_than_its_layout():
 
 def test_unsupported_message_names_every_head_dim_rule():
     msg = _lib.strerror(_lib.ATTN_EUNSUPPORTED)
-    assert "64 or 128" in msg and "256" in msg and "backward" in msg and "float32" in msg
+    assert "64 or 128" in msg and "256" in msg and "float32" in msg
 
 
 @pytest.mark.parametrize("over,code", [
@@ -259,7 +259,7 @@ def test_bwd_workspace_bytes():
     assert _lib.bwd_workspace_bytes(2, 100, 8, 2, 128) == (3 * 2 * 2 + 4 * 2 * 8) * nb * 32 * 128 * 2 + 2 * 2 * 8 * nb * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 64) == (3 + 4 * 4) * 2 * 32 * 64 * 2 + 2 * 4 * 2 * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 96) == 0
-    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 256) == 0  # the backward covers head_dim 64 and 128
+    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 256) == (3 + 4 * 4) * 2 * 32 * 256 * 2 + 2 * 4 * 2 * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 6, 4, 64) == 0
 
 
@@ -280,7 +280,7 @@ def bwd_call(**over):
     (dict(Hq=3, Hkv=2), _lib.ATTN_EINVAL), (dict(causal=2), _lib.ATTN_EINVAL), (dict(theta=float("inf")), _lib.ATTN_EINVAL),
     (dict(rope=2), _lib.ATTN_EINVAL),
     (dict(d=96), _lib.ATTN_EUNSUPPORTED), (dict(S=(1 << 28) + 1), _lib.ATTN_EUNSUPPORTED),
-    (dict(d=256), _lib.ATTN_EUNSUPPORTED),
+    (dict(d=512), _lib.ATTN_EUNSUPPORTED), (dict(d=256, wsb=100), _lib.ATTN_EWORKSPACE),
     (dict(ws=None), _lib.ATTN_EWORKSPACE), (dict(wsb=100), _lib.ATTN_EWORKSPACE), (dict(ws=P + 8), _lib.ATTN_EWORKSPACE),
 ])
 def test_bwd_rejections(over, code):

@@ -59,6 +59,9 @@ SHAPES = [
     (1, 200, 6, 2, 128, False),  # 3 heads per K/V head: 3 waves
     (1, 33, 2, 1, 128, True),    # two blocks, second holds one row
     (3, 1, 4, 2, 64, True),      # single row
+    (1, 100, 8, 1, 256, True),   # head_dim 256 (PaLM-540B's), multi-query, ragged
+    (2, 70, 4, 2, 256, False),   # head_dim 256, full attention
+    (1, 33, 2, 2, 256, True),    # head_dim 256, two blocks, second holds one row
 ]
 
 

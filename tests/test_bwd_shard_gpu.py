@@ -49,6 +49,8 @@ STEPS = [
     (1, 90, 8, 1, 128, True, 13, 77, False),
     (1, 160, 8, 2, 128, True, 500, 0, False),   # every key visible to every row
     (1, 100, 8, 2, 64, False, 300, 7, True),    # full attention: offsets rotate only
+    (1, 96, 4, 1, 256, True, 40, 0, False),     # head_dim 256, offset not a multiple of 32
+    (1, 70, 4, 1, 256, True, 13, 77, True),     # head_dim 256, rows that see nothing
 ]
 
 

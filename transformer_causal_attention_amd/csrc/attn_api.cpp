@@ -48,11 +48,13 @@ unsigned long long next_call_tag() {
 }
 
 // Whether a bf16 forward of this grid takes the one-launch form: every workgroup must be
-// resident at once, and each wave group prepares at most kMaxPrepRounds tile halves (beyond
-// that the separate pass, whose workgroups each take one tile, is faster).  The environment
+// resident at once, and each wave group prepares at most kMaxPrepRounds tile halves (measured:
+// the one-launch form is as fast or faster up to 8 on the SmolLM MHA shape, B 4, S 1024, 32
+// heads of 64, and 1 on the Llama-3-8B and PaLM MQA shapes; a larger count would move more of
+// the preparation into the prologue than the separate pass costs).  The environment
 // variable ATTN_FWD_PATH = "split" or "fused" overrides the choice (a diagnostic; "fused" is
 // still refused when the grid would not be resident).
-constexpr int kMaxPrepRounds = 2;
+constexpr int kMaxPrepRounds = 8;
 
 // Bound of the one-launch form's wait for published tiles: each poll is a device-scope read
 // plus a ~0.1 us sleep, so the bound is a fraction of a second; the wait normally ends within
@@ -266,7 +268,7 @@ ATTN_EXPORT const char *attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size, Hq not a multiple of Hkv, bad rope_theta, rope_style or causal flag)";
-    case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, or 256 for the bf16 forward, shard, merge and decode calls but not the backward or float32; dtype bf16 or fp32; sizes within limits)";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration (head_dim must be 64 or 128, or 256 for the bf16 calls but not float32; dtype bf16 or fp32; sizes within limits)";
     case ATTN_EHIP: return "HIP runtime error while recording an event or launching a kernel";
     case ATTN_EWORKSPACE: return "workspace missing, misaligned or smaller than attn_fwd_workspace_bytes()";
     case ATTN_ESCRATCH: return "attn_fwd_noalloc: the call needs more workspace than the library's fixed scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
@@ -537,7 +539,7 @@ size_t bwd_blocks(int S) { return ((size_t)S + kBwdRows - 1) / kBwdRows; }
 }  // namespace
 
 ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int head_dim) {
-  if (head_dim == 256 || check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
+  if (check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
   const size_t nb = bwd_blocks(S);
   const size_t tile = (size_t)kBwdRows * head_dim * 2;
   return 3 * (size_t)B * Hkv * nb * tile + 4 * (size_t)B * Hq * nb * tile + 2 * (size_t)B * Hq * nb * kBwdRows * 4;
@@ -553,7 +555,6 @@ ATTN_EXPORT int attn_bwd_shard(const void *q, const void *k, const void *v, cons
   for (const void *ptr : {q, k, v, out, dout, (const void *)dq, (const void *)dk, (const void *)dv})
     if (!aligned(ptr, 16)) return ATTN_EINVAL;
   if (!aligned(lse, 4) || !rope_style_ok(rope_style)) return ATTN_EINVAL;
-  if (head_dim == 256) return ATTN_EUNSUPPORTED;  // the backward kernels cover head_dim 64 and 128
   const int rc = check_shape(B, S, Hq, Hkv, head_dim, rope_theta, causal, ATTN_DTYPE_BF16);
   if (rc != ATTN_OK) return rc;
   const size_t nb = bwd_blocks(S);
@@ -597,7 +598,9 @@ ATTN_EXPORT int attn_bwd_shard(const void *q, const void *k, const void *v, cons
   p.inv_sqrt_d = (float)(1.0 / std::sqrt((double)head_dim));
   const attn::RopeTable tab = rope_table(head_dim, rope_theta, rope_style);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t err = head_dim == 64 ? attn::launch_bwd<64>(p, tab, st) : attn::launch_bwd<128>(p, tab, st);
+  const hipError_t err = head_dim == 64    ? attn::launch_bwd<64>(p, tab, st)
+                         : head_dim == 128 ? attn::launch_bwd<128>(p, tab, st)
+                                           : attn::launch_bwd<256>(p, tab, st);
   return err == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

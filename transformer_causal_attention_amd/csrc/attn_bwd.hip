@@ -64,6 +64,13 @@ __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b :
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// 16 bytes at byte voff (per lane) + soff (uniform) of a buffer: the base stays in scalar
+// registers and each lane keeps one 32-bit offset, not a 64-bit address per operand stream.
+// Constant parts of an offset go into soff, so that no lane holds a register per operand.
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
 // Row of result register v in lane half hh.
 __device__ __forceinline__ int res_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
 
@@ -124,8 +131,8 @@ __global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable 
   const int unit = blockIdx.x / p.NB;  // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const size_t tile = (size_t)blockIdx.x * T;
-  if (tid < BR * NCH) {
-    const int row = tid / NCH, c = tid % NCH;
+  for (int item = tid; item < BR * NCH; item += 256) {  // one pass, two at head_dim 256
+    const int row = item / NCH, c = item % NCH;
     const int r = kb * BR + row;
     u32x4 kx = {0u, 0u, 0u, 0u}, ky = kx, vx = kx, vy = kx;
     if (r < p.S) {
@@ -168,8 +175,10 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
   const int unit = blockIdx.x / p.NB;  // b * Hq + h
   const int h = unit % p.Hq, b = unit / p.Hq;
   const size_t tile = (size_t)blockIdx.x * T;
-  if (tid < BR * NCH) {
-    const int row = tid / NCH, c = tid % NCH;
+  // one pass, two at head_dim 256 (the NCH items of a row are consecutive lanes of one wave in
+  // either pass, for the row sums below)
+  for (int item = tid; item < BR * NCH; item += 256) {
+    const int row = item / NCH, c = item % NCH;
     const int r = qb * BR + row;
     const bool ok = r < p.S;
     u32x4 qx = {0u, 0u, 0u, 0u}, qy = qx, gx = qx, gy = qx, ox = qx, oy = qx;
@@ -235,8 +244,12 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
   constexpr int T = BR * D;
   constexpr int RED = NCB * 16 * 64;  // floats of one accumulator set of a wave
   __shared__ float red[3][RED];
+  // dv: the key block's operand, the same for every wave, is read from LDS at each step rather
+  // than held in registers (two waves per SIMD leave no room for it beside two query blocks'
+  // operands); dk keeps it in registers
+  __shared__ bf16x8 kl[DV ? NKK * 64 : 1];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int blk = xcd_order(blockIdx.x, gridDim.x);
   const int pair = blk % p.n_pairs;
@@ -244,15 +257,24 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
 
+#pragma unroll 1
   for (int side = 0; side < 2; ++side) {
     const int kb = side == 0 ? pair : p.NB - 1 - pair;
     if (side == 1 && kb == pair) break;
     const size_t ktile = ((size_t)unit * p.NB + kb) * T;
     bf16x8 kf[NKK], vf[NKK];
+    if constexpr (DV) {
+      // operand kk of lane l at kl[64 kk + l]; the previous side's readers have passed the
+      // barrier at the end of its reduction
+      for (int i = threadIdx.x; i < NKK * 64; i += blockDim.x)
+        kl[i] = ld16(p.kc + ktile + (i & 32) * BR / 4 + (i & 31) * 8 + (i >> 6) * 2 * BR * 8);
+      __syncthreads();
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
-      if (!DV) vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+      for (int kk = 0; kk < NKK; ++kk) {
+        kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
+        vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+      }
     }
     const bool key_ok = kb * BR + l32 < p.S;
     f32x16 acc[NCB];
@@ -265,39 +287,53 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
     const int delta = p.q_pos0 - p.k_pos0;
     // the first query block with a row that sees a key of this block: 32 qb + 31 + delta >= 32 kb
     const int qb_lo = p.causal ? max(0, floor_div(BR * kb - delta, BR)) : 0;
+    // per-lane byte offsets within a query block's tiles and row vectors
+    const uint32_t v_c = 2u * c_off, v_t = 16u * (hh * D + l32), v_r = 16u * hh;
     for (int hc = wave; hc < p.G; hc += p.W) {
       const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
+      // this head's run of query blocks as buffers (NB * T * 2 < 2^31 bytes)
+      const uint32_t run_t = (uint32_t)p.NB * T * 2, run_r = (uint32_t)p.NB * BR * 4;
+      const __amdgpu_buffer_rsrc_t qbuf = raw_buffer(p.qc + qunit * p.NB * T, run_t);
+      const __amdgpu_buffer_rsrc_t dbuf = raw_buffer(p.dc + qunit * p.NB * T, run_t);
+      const __amdgpu_buffer_rsrc_t tbuf = raw_buffer((DV ? p.dt : p.qt) + qunit * p.NB * T, run_t);
+      const __amdgpu_buffer_rsrc_t lbuf = raw_buffer(p.l2 + qunit * p.NB * BR, run_r);
+      const __amdgpu_buffer_rsrc_t ddbuf = raw_buffer(p.dd + qunit * p.NB * BR, run_r);
       auto load_q = [&](int qb, int buf) __attribute__((always_inline)) {
-        const size_t qtile = (qunit * p.NB + qb) * T;
+        const uint32_t st = (uint32_t)qb * T * 2, sr = (uint32_t)qb * BR * 4;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          qa[buf][kk] = ld16(p.qc + qtile + c_off + kk * 2 * BR * 8);
-          if (!DV) da[buf][kk] = ld16(p.dc + qtile + c_off + kk * 2 * BR * 8);
+          qa[buf][kk] = __builtin_bit_cast(bf16x8, bld16(qbuf, v_c, st + kk * 2 * BR * 16));
+          if (!DV) da[buf][kk] = __builtin_bit_cast(bf16x8, bld16(dbuf, v_c, st + kk * 2 * BR * 16));
         }
         // per-row lse and rowsum for this lane's rows 8c + 4hh + 0..3
-        const size_t r0 = (qunit * p.NB + qb) * BR + 4 * hh;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          L[buf][c] = *reinterpret_cast<const f32x4 *>(p.l2 + r0 + 8 * c);
-          if (!DV) Dd[buf][c] = *reinterpret_cast<const f32x4 *>(p.dd + r0 + 8 * c);
+          L[buf][c] = __builtin_bit_cast(f32x4, bld16(lbuf, v_r, sr + 32 * c));
+          if (!DV) Dd[buf][c] = __builtin_bit_cast(f32x4, bld16(ddbuf, v_r, sr + 32 * c));
         }
-        const __bf16 *tsrc = DV ? p.dt : p.qt;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            tb[buf][tt][cb] = ld16(tsrc + qtile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8);
+            tb[buf][tt][cb] = __builtin_bit_cast(bf16x8, bld16(tbuf, v_t, st + (tt * 2 * D + 32 * cb) * 16));
       };
       auto step = [&](int qb, int buf) __attribute__((always_inline)) {
         f32x16 s = f32x16{}, dp = f32x16{};
+        // (the LDS index goes through an empty asm so that the reads stay in the step)
+        int ki = lane;
+        if (DV) asm volatile("" : "+v"(ki));
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          s = bwd_mfma(qa[buf][kk], kf[kk], s);
+          s = bwd_mfma(qa[buf][kk], DV ? kl[64 * kk + ki] : kf[kk], s);
           if (!DV) dp = bwd_mfma(da[buf][kk], vf[kk], dp);
         }
-        // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel
+        // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel, i.e. (r = res_row(v, hh))
+        // iff 8(v/4) + v%4 < thr.  One threshold per lane and step, compared with constants and
+        // applied by selects: a key past S masks every row (thr 32), a block pair with no later
+        // key none (thr 0).  (A short-circuit test here becomes a branch around each exp, and
+        // per-lane constants per v would stay live across the loop.)
         const int rel = BR * (qb - kb) + delta;
-        const bool partial = p.causal && rel < BR - 1;
+        const int thr = !key_ok ? 32 : (p.causal && rel < BR - 1) ? l32 - 4 * hh - rel : 0;
         bf16x8 op[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -309,7 +345,7 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
             for (int z = 0; z < 2; ++z) {
               const int v = 8 * tt + e + z;
               float pr = __builtin_amdgcn_exp2f(s[v] - L[buf][v >> 2][v & 3]);
-              if (!key_ok || (partial && l32 - res_row(v, hh) > rel)) pr = 0.f;
+              pr = 8 * (v >> 2) + (v & 3) < thr ? 0.f : pr;
               x[z] = DV ? pr : pr * (dp[v] - Dd[buf][v >> 2][v & 3]);
             }
             wv[e / 2] = pack_bf16x2(x[0], x[1]);
@@ -423,18 +459,24 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
     // key-block operands, two sets: the next block's are loaded while the current one is used
     // (the index is clamped, so the last step re-reads its own block instead of branching)
     bf16x8 ka[2][NKK], va[2][NKK], kt[2][2][NCB];
+    // this K/V head's run of key blocks as buffers (NB * T * 2 < 2^31 bytes), per-lane byte offsets
+    const uint32_t run_t = (uint32_t)p.NB * T * 2;
+    const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(p.kc + kunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t vbuf = raw_buffer(p.vc + kunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t tbuf = raw_buffer(p.kt + kunit * p.NB * T, run_t);
+    const uint32_t v_c = 2u * c_off, v_t = 16u * (hh * D + l32);
     auto load_kv = [&](int kb, int buf) __attribute__((always_inline)) {
-      const size_t ktile = (kunit * p.NB + kb) * T;
+      const uint32_t st = (uint32_t)kb * T * 2;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        ka[buf][kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
-        va[buf][kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+        ka[buf][kk] = __builtin_bit_cast(bf16x8, bld16(kbuf, v_c, st + kk * 2 * BR * 16));
+        va[buf][kk] = __builtin_bit_cast(bf16x8, bld16(vbuf, v_c, st + kk * 2 * BR * 16));
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          kt[buf][tt][cb] = ld16(p.kt + ktile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8);
+          kt[buf][tt][cb] = __builtin_bit_cast(bf16x8, bld16(tbuf, v_t, st + (tt * 2 * D + 32 * cb) * 16));
     };
     auto step = [&](int kb, int buf) __attribute__((always_inline)) {
       f32x16 st = f32x16{}, dpt = f32x16{};
@@ -443,9 +485,12 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
         st = bwd_mfma(ka[buf][kk], qf[kk], st);
         dpt = bwd_mfma(va[buf][kk], df[kk], dpt);
       }
-      // key kb*32 + k is later than row qb*32 + l32 iff k - l32 > rel
+      // key kb*32 + k is later than row qb*32 + l32 iff k - l32 > rel, i.e. (k = res_row(v, hh))
+      // iff 8(v/4) + v%4 > thr: one threshold per lane and step against constants, applied by
+      // selects (thr 27 masks nothing).  Keys past S: those of the last block from S - 32 kb on.
       const int rel = BR * (qb - kb) + delta;
-      const bool partial = p.causal && rel < BR - 1;
+      const int thr = (p.causal && rel < BR - 1) ? rel + l32 - 4 * hh : 27;
+      const int kend = p.S - kb * BR - 4 * hh;  // key 8(v/4) + v%4 + 4hh < S iff 8(v/4) + v%4 < kend
       bf16x8 sa[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -456,9 +501,8 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
 #pragma unroll
           for (int z = 0; z < 2; ++z) {
             const int v = 8 * tt + e + z;
-            const int key = res_row(v, hh);  // within the block
             float pr = __builtin_amdgcn_exp2f(st[v] - Lq);
-            if (kb * BR + key >= p.S || (partial && key - l32 > rel)) pr = 0.f;
+            pr = ((8 * (v >> 2) + (v & 3) > thr) | (8 * (v >> 2) + (v & 3) >= kend)) ? 0.f : pr;
             sv[z] = pr * (dpt[v] - Dq);
           }
           ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
@@ -505,6 +549,250 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// head_dim 256 (the PaLM page's 540B head size, section 3).  The kernels above keep a block's
+// operands in registers: at 256 dims the dk kernel would need ~650 VGPRs.  Here the block that
+// stays fixed over a kernel's loop lives in LDS (the key block's rotated keys and values for
+// dk/dv, the query block's rotated queries and dout for dq), every MFMA operand of it is one
+// 16-byte LDS read, and the moving block's operands are read from the prepared tiles per step.
+// Same arithmetic, operand layouts, visibility and masks as the kernels above.
+
+__device__ __forceinline__ bf16x8 lds16(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+template <bool DV>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, RopeTable tab) {
+  constexpr int D = 256;
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  constexpr int RED = NCB * 16 * 64;
+  __shared__ float red[3][RED];
+  __shared__ __attribute__((aligned(16))) __bf16 kv[DV ? 1 : 2][T];  // key block: rotated keys, values
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int nthreads = 64 * p.W;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int blk = xcd_order(blockIdx.x, gridDim.x);
+  const int pair = blk % p.n_pairs;
+  const int unit = blk / p.n_pairs;  // b * Hkv + g
+  const int g = unit % p.Hkv, b = unit / p.Hkv;
+  const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
+  const int delta = p.q_pos0 - p.k_pos0;
+
+  for (int side = 0; side < 2; ++side) {
+    const int kb = side == 0 ? pair : p.NB - 1 - pair;
+    if (side == 1 && kb == pair) break;
+    const size_t ktile = ((size_t)unit * p.NB + kb) * T;
+    __syncthreads();  // the previous block's operands are no longer read
+    for (int i = threadIdx.x; i < T / 8; i += nthreads) {
+      *reinterpret_cast<u32x4 *>(&kv[0][8 * i]) = *reinterpret_cast<const u32x4 *>(p.kc + ktile + 8 * i);
+      if (!DV) *reinterpret_cast<u32x4 *>(&kv[DV ? 0 : 1][8 * i]) = *reinterpret_cast<const u32x4 *>(p.vc + ktile + 8 * i);
+    }
+    __syncthreads();
+    const bool key_ok = kb * BR + l32 < p.S;
+    f32x16 acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+    const int qb_lo = p.causal ? max(0, floor_div(BR * kb - delta, BR)) : 0;
+    for (int hc = wave; hc < p.G; hc += p.W) {
+      const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
+      for (int qb = p.NB - 1; qb >= qb_lo; --qb) {
+        const size_t qtile = (qunit * p.NB + qb) * T;
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sc = bwd_mfma(ld16(p.qc + qtile + c_off + kk * 2 * BR * 8), lds16(&kv[0][c_off + kk * 2 * BR * 8]), sc);
+          if (!DV)
+            dp = bwd_mfma(ld16(p.dc + qtile + c_off + kk * 2 * BR * 8), lds16(&kv[DV ? 0 : 1][c_off + kk * 2 * BR * 8]),
+                          dp);
+        }
+        // per-row lse and rowsum for this lane's rows 8c + 4hh + 0..3
+        const size_t r0 = (qunit * p.NB + qb) * BR + 4 * hh;
+        f32x4 L[4], Dd[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          L[c] = *reinterpret_cast<const f32x4 *>(p.l2 + r0 + 8 * c);
+          Dd[c] = DV ? f32x4{} : *reinterpret_cast<const f32x4 *>(p.dd + r0 + 8 * c);
+        }
+        // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel, i.e. (r = res_row(v, hh))
+        // iff 8(v/4) + v%4 < thr.  One threshold per lane and step, compared with constants and
+        // applied by selects: a key past S masks every row (thr 32), a block pair with no later
+        // key none (thr 0).  (A short-circuit test here becomes a branch around each exp, and
+        // per-lane constants per v would stay live across the loop.)
+        const int rel = BR * (qb - kb) + delta;
+        const int thr = !key_ok ? 32 : (p.causal && rel < BR - 1) ? l32 - 4 * hh - rel : 0;
+        bf16x8 op[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 wv;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float x[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int v = 8 * tt + e + z;
+              float pr = __builtin_amdgcn_exp2f(sc[v] - L[v >> 2][v & 3]);
+              pr = 8 * (v >> 2) + (v & 3) < thr ? 0.f : pr;
+              x[z] = DV ? pr : pr * (dp[v] - Dd[v >> 2][v & 3]);
+            }
+            wv[e / 2] = pack_bf16x2(x[0], x[1]);
+          }
+          op[tt] = __builtin_bit_cast(bf16x8, wv);
+        }
+        // dv += P^T dO, dk += dS^T (q'/sqrt(D))
+        const __bf16 *tsrc = DV ? p.dt : p.qt;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            acc[cb] = bwd_mfma(op[tt], ld16(tsrc + qtile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8), acc[cb]);
+      }
+    }
+
+    // add the waves' sums into wave 0
+    if (wave > 0) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[wave - 1][(cb * 16 + v) * 64 + lane] = acc[cb][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < p.W; ++w)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[cb][v] += red[w - 1][(cb * 16 + v) * 64 + lane];
+      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block;
+      // dk' -> dk: rotate the pair (column i, i + D/2) back by the key's angle
+      if (!DV) {
+#pragma unroll
+        for (int cb = 0; cb < NCB / 2; ++cb) {
+          const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb * BR + res_row(v, hh);
+            const float t = turn_fraction(p.k_pos0 + key, rev);
+            const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+            const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
+            acc[cb][v] = x * cs + y * sn;
+            acc[cb + NCB / 2][v] = y * cs - x * sn;
+          }
+        }
+      }
+      __bf16 *dst0 = DV ? p.dv : p.dk;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * BR + res_row(v, hh);
+        if (key < p.S) {
+          const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
+          const int il = DV ? 0 : tab.interleaved;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
+        }
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64, 1) bwd_dq_d256_kernel(BwdParams p, RopeTable tab) {
+  constexpr int D = 256;
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  __shared__ __attribute__((aligned(16))) __bf16 qd[2][T];  // query block: scaled rotated queries, dout
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int blk = xcd_order(blockIdx.x, gridDim.x);
+  const int pair = blk % p.n_pairs;
+  const int qunit = blk / p.n_pairs;  // b * Hq + h
+  const int h = qunit % p.Hq, b = qunit / p.Hq;
+  const int g = h / p.G;
+  const size_t kunit = (size_t)b * p.Hkv + g;
+  const int c_off = hh * BR * 8 + l32 * 8;
+  const int delta = p.q_pos0 - p.k_pos0;
+
+  for (int side = 0; side < 2; ++side) {
+    const int qb = side == 0 ? pair : p.NB - 1 - pair;
+    if (side == 1 && qb == pair) break;
+    const size_t qtile = ((size_t)qunit * p.NB + qb) * T;
+    __syncthreads();  // the previous block's operands are no longer read
+    for (int i = lane; i < T / 8; i += 64) {
+      *reinterpret_cast<u32x4 *>(&qd[0][8 * i]) = *reinterpret_cast<const u32x4 *>(p.qc + qtile + 8 * i);
+      *reinterpret_cast<u32x4 *>(&qd[1][8 * i]) = *reinterpret_cast<const u32x4 *>(p.dc + qtile + 8 * i);
+    }
+    __syncthreads();
+    // this lane's query: row l32 of the block
+    const float Lq = p.l2[((size_t)qunit * p.NB + qb) * BR + l32];
+    const float Dq = p.dd[((size_t)qunit * p.NB + qb) * BR + l32];
+    f32x16 dq[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
+    const int kb_end = p.causal ? min(p.NB, max(0, floor_div(BR * qb + BR - 1 + delta, BR) + 1)) : p.NB;
+    for (int kb = 0; kb < kb_end; ++kb) {
+      const size_t ktile = (kunit * p.NB + kb) * T;
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        st = bwd_mfma(ld16(p.kc + ktile + c_off + kk * 2 * BR * 8), lds16(&qd[0][c_off + kk * 2 * BR * 8]), st);
+        dpt = bwd_mfma(ld16(p.vc + ktile + c_off + kk * 2 * BR * 8), lds16(&qd[1][c_off + kk * 2 * BR * 8]), dpt);
+      }
+      // key kb*32 + k is later than row qb*32 + l32 iff k - l32 > rel, i.e. (k = res_row(v, hh))
+      // iff 8(v/4) + v%4 > thr: one threshold per lane and step against constants, applied by
+      // selects (thr 27 masks nothing).  Keys past S: those of the last block from S - 32 kb on.
+      const int rel = BR * (qb - kb) + delta;
+      const int thr = (p.causal && rel < BR - 1) ? rel + l32 - 4 * hh : 27;
+      const int kend = p.S - kb * BR - 4 * hh;  // key 8(v/4) + v%4 + 4hh < S iff 8(v/4) + v%4 < kend
+      bf16x8 sa[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 ws;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float sv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int v = 8 * tt + e + z;
+            float pr = __builtin_amdgcn_exp2f(st[v] - Lq);
+            pr = ((8 * (v >> 2) + (v & 3) > thr) | (8 * (v >> 2) + (v & 3) >= kend)) ? 0.f : pr;
+            sv[z] = pr * (dpt[v] - Dq);
+          }
+          ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
+        }
+        sa[tt] = __builtin_bit_cast(bf16x8, ws);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          dq[cb] = bwd_mfma(sa[tt], ld16(p.kt + ktile + ((size_t)(tt * 2 + hh) * D + 32 * cb + l32) * 8), dq[cb]);
+    }
+    // result lane = column 32 cb + l32, register v = query 8(v/4) + 4 hh + v%4 of the block
+#pragma unroll
+    for (int cb = 0; cb < NCB / 2; ++cb) {
+      const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = qb * BR + res_row(v, hh);
+        const float t = turn_fraction(p.q_pos0 + row, rev);
+        const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+        const float x = dq[cb][v] * p.inv_sqrt_d, y = dq[cb + NCB / 2][v] * p.inv_sqrt_d;
+        dq[cb][v] = x * cs + y * sn;
+        dq[cb + NCB / 2][v] = y * cs - x * sn;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = qb * BR + res_row(v, hh);
+      if (row < p.S) {
+        const size_t dst = (((size_t)b * p.S + row) * p.Hq + h) * D;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) p.dq[dst + rope_src_dim(32 * cb + l32, D / 2, tab.interleaved)] = (__bf16)dq[cb][v];
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
   const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
@@ -515,16 +803,26 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
   hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(qblocks), dim3(256), 0, stream, p, tab);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.n_pairs));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((long long)p.B * p.Hq * p.n_pairs)), dim3(64), 0, stream, p,
-                     tab);
-  return hipGetLastError();
+  const dim3 q_grid((unsigned)((long long)p.B * p.Hq * p.n_pairs));
+  if constexpr (D == 256) {
+    hipLaunchKernelGGL((bwd_dkdv_d256_kernel<true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_dkdv_d256_kernel<false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_dq_d256_kernel, q_grid, dim3(64), 0, stream, p, tab);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, q_grid, dim3(64), 0, stream, p, tab);
+    return hipGetLastError();
+  }
 }
 
 template hipError_t launch_bwd<64>(const BwdParams &, const RopeTable &, hipStream_t);
 template hipError_t launch_bwd<128>(const BwdParams &, const RopeTable &, hipStream_t);
+template hipError_t launch_bwd<256>(const BwdParams &, const RopeTable &, hipStream_t);
 
 }  // namespace attn

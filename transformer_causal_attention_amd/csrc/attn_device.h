@@ -186,6 +186,12 @@ __device__ __forceinline__ void rotate_pair(float x, float y, float c, float s, 
 // (y0', y1').
 __device__ __forceinline__ u32x2 rotate_packed(uint32_t xw, uint32_t yw, float c0, float s0, float c1, float s1);
 
+// Raw (unformatted, byte-addressed) buffer resource over `bytes` bytes at `base`.  A buffer load
+// takes its base from scalar registers and a 32-bit offset per lane from one VGPR.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -87,11 +87,6 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)lds_base, 16, voff, soff, 0, 0);
 }
 
-// Raw (unformatted, byte-addressed) buffer resource over `bytes` bytes at `base`.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-
 // 16-byte store at byte voff + soff of buffer `rsrc`, written through to device scope (sc1):
 // visible to every CU once the store has completed, without a cache write-back.
 __device__ __forceinline__ void store_through(const u32x4 &v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
