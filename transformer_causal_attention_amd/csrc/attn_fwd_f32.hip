@@ -20,8 +20,10 @@ constexpr int F32_SUB = 8;  // keys per softmax update
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable tab) {
-  __shared__ float ks[F32_TK][D + 1];
-  __shared__ float vs[F32_TK][D + 1];
+  // rows padded by 4 floats: 16-byte aligned for 4-wide broadcast reads, and the staging
+  // writes (one key row per lane) spread over the banks
+  __shared__ __attribute__((aligned(16))) float ks[F32_TK][D + 4];
+  __shared__ __attribute__((aligned(16))) float vs[F32_TK][D + 4];
 
   const int lane = threadIdx.x;
   const int rb = blockIdx.x % p.n_row_blocks;
@@ -88,7 +90,11 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
         const int jl = j0 + u;
         float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[jl][c], acc);
+        for (int c = 0; c < D; c += 4) {
+          const f32x4 k4 = *reinterpret_cast<const f32x4 *>(&ks[jl][c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = fmaf(q[c + e], k4[e], acc);
+        }
         const int j = kbase + jl;
         const bool masked = jl >= tile_end || j >= S || (CAUSAL && j > row + delta);
         s[u] = masked ? -INFINITY : acc;
@@ -106,11 +112,16 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(F32Params p, RopeTable
       l_run = l_run * alpha + rsum;
       m_run = m_new;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        float acc = o[c] * alpha;
+      for (int c = 0; c < D; c += 4) {
+        f32x4 acc = {o[c] * alpha, o[c + 1] * alpha, o[c + 2] * alpha, o[c + 3] * alpha};
 #pragma unroll
-        for (int u = 0; u < F32_SUB; ++u) acc = fmaf(s[u], vs[j0 + u][c], acc);
-        o[c] = acc;
+        for (int u = 0; u < F32_SUB; ++u) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&vs[j0 + u][c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(s[u], v4[e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[c + e] = acc[e];
       }
     }
   }
