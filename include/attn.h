@@ -269,7 +269,9 @@ int attn_decode_ragged(const void *q, const void *cache, size_t cache_bytes, int
  *   out, lse       attn_fwd's outputs for the same q, k, v, rope_theta, rope_style, causal
  *   dq; dk, dv     device, shaped like q; like k (written), 16-byte aligned
  *   workspace      device, >= attn_bwd_workspace_bytes(...) bytes, 16-byte aligned (the
- *                  re-laid-out operands), caller owned
+ *                  re-laid-out operands; for few (b, K/V head) pairs with many query heads
+ *                  each, e.g. PaLM-540B's 48 heads on one K/V head, also fp32 partial dk and
+ *                  dv of head splits, summed by a last kernel), caller owned
  * bf16 only; head_dim 64, 128 or 256 (at 256 the kernels keep the block that stays fixed over
  * their loop in LDS instead of registers).  Returns ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED,
  * ATTN_EWORKSPACE or ATTN_EHIP with the meanings given for attn_fwd.

@@ -62,6 +62,8 @@ SHAPES = [
     (1, 100, 8, 1, 256, True),   # head_dim 256 (PaLM-540B's), multi-query, ragged
     (2, 70, 4, 2, 256, False),   # head_dim 256, full attention
     (1, 33, 2, 2, 256, True),    # head_dim 256, two blocks, second holds one row
+    (1, 64, 48, 1, 256, True),   # PaLM-540B heads: 12 passes of 4 heads spread over 12 head splits
+    (1, 80, 12, 1, 128, False),  # 3 passes over 3 head splits, full attention
 ]
 
 

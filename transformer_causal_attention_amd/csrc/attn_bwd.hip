@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
 // accumulators and has the registers to load the next query block's operands while it uses the
 // current ones; the dv kernel needs neither dP nor dout in "c" layout.
 
-template <int D, bool DV>
+template <int D, bool DV, bool SPLIT>
 __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, RopeTable tab) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
@@ -253,7 +253,9 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
   const int l32 = lane & 31, hh = lane >> 5;
   const int blk = xcd_order(blockIdx.x, gridDim.x);
   const int pair = blk % p.n_pairs;
-  const int unit = blk / p.n_pairs;  // b * Hkv + g
+  const int n_hs = SPLIT ? p.HS : 1;          // head splits (SPLIT: more than one)
+  const int hs = SPLIT ? (blk / p.n_pairs) % n_hs : 0;
+  const int unit = blk / p.n_pairs / n_hs;     // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
 
@@ -289,7 +291,7 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
     const int qb_lo = p.causal ? max(0, floor_div(BR * kb - delta, BR)) : 0;
     // per-lane byte offsets within a query block's tiles and row vectors
     const uint32_t v_c = 2u * c_off, v_t = 16u * (hh * D + l32), v_r = 16u * hh;
-    for (int hc = wave; hc < p.G; hc += p.W) {
+    for (int hc = wave + hs * p.W; hc < p.G; hc += p.W * n_hs) {
       const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
       // this head's run of query blocks as buffers (NB * T * 2 < 2^31 bytes)
       const uint32_t run_t = (uint32_t)p.NB * T * 2, run_r = (uint32_t)p.NB * BR * 4;
@@ -385,7 +387,17 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[cb][v] += red[w - 1][(cb * 16 + v) * 64 + lane];
-      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block;
+      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block
+      if constexpr (SPLIT) {
+        // this head split's partial sums (dk' not yet rotated back), for the reduction kernel
+        float *part = p.part + (((size_t)(DV ? n_hs : 0) + hs) * p.B * p.Hkv + unit) * p.NB * BR * D;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BR + res_row(v, hh);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) part[(size_t)key * D + 32 * cb + l32] = acc[cb][v];
+        }
+      } else {
       // dk' -> dk: rotate the pair (column i, i + D/2) back by the key's angle
       if (!DV) {
 #pragma unroll
@@ -413,6 +425,7 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
         }
+      }
       }
     }
     __syncthreads();  // the reduction slots are reused by the second block
@@ -559,7 +572,7 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
 
 __device__ __forceinline__ bf16x8 lds16(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-template <bool DV>
+template <bool DV, bool SPLIT>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, RopeTable tab) {
   constexpr int D = 256;
   constexpr int NKK = D / 16;
@@ -574,7 +587,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, Rope
   const int l32 = lane & 31, hh = lane >> 5;
   const int blk = xcd_order(blockIdx.x, gridDim.x);
   const int pair = blk % p.n_pairs;
-  const int unit = blk / p.n_pairs;  // b * Hkv + g
+  const int n_hs = SPLIT ? p.HS : 1;          // head splits (SPLIT: more than one)
+  const int hs = SPLIT ? (blk / p.n_pairs) % n_hs : 0;
+  const int unit = blk / p.n_pairs / n_hs;     // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
   const int delta = p.q_pos0 - p.k_pos0;
@@ -594,7 +609,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, Rope
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
     const int qb_lo = p.causal ? max(0, floor_div(BR * kb - delta, BR)) : 0;
-    for (int hc = wave; hc < p.G; hc += p.W) {
+    for (int hc = wave + hs * p.W; hc < p.G; hc += p.W * n_hs) {
       const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
       for (int qb = p.NB - 1; qb >= qb_lo; --qb) {
         const size_t qtile = (qunit * p.NB + qb) * T;
@@ -663,7 +678,17 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, Rope
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[cb][v] += red[w - 1][(cb * 16 + v) * 64 + lane];
-      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block;
+      // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block
+      if constexpr (SPLIT) {
+        // this head split's partial sums (dk' not yet rotated back), for the reduction kernel
+        float *part = p.part + (((size_t)(DV ? n_hs : 0) + hs) * p.B * p.Hkv + unit) * p.NB * BR * D;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BR + res_row(v, hh);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) part[(size_t)key * D + 32 * cb + l32] = acc[cb][v];
+        }
+      } else {
       // dk' -> dk: rotate the pair (column i, i + D/2) back by the key's angle
       if (!DV) {
 #pragma unroll
@@ -690,6 +715,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, Rope
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
         }
+      }
       }
     }
   }
@@ -793,6 +819,40 @@ __global__ void __launch_bounds__(64, 1) bwd_dq_d256_kernel(BwdParams p, RopeTab
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Head-split reduction: dk and dv of key j are the sums over the head splits' partials, added
+// in split order (deterministic); dk' is then rotated back by the key's angle, as in the
+// kernels' own epilogue.  One thread per (unit, key, column pair c, c + D/2).
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_part_reduce_kernel(BwdParams p, RopeTable tab) {
+  const size_t rows = (size_t)p.B * p.Hkv * p.NB * BR;  // (unit, key) rows of the partials
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * (D / 2)) return;
+  const int c = (int)(i % (D / 2));
+  const size_t row = i / (D / 2);
+  const int key = (int)(row % ((size_t)p.NB * BR));
+  const size_t unit = row / ((size_t)p.NB * BR);
+  if (key >= p.S) return;
+  const size_t split = rows * D;  // floats of one split's partials
+  const float *pk = p.part + row * D, *pv = p.part + (size_t)p.HS * split + row * D;
+  float kx = 0.f, ky = 0.f, vx = 0.f, vy = 0.f;
+  for (int hs = 0; hs < p.HS; ++hs) {
+    kx += pk[hs * split + c];
+    ky += pk[hs * split + c + D / 2];
+    vx += pv[hs * split + c];
+    vy += pv[hs * split + c + D / 2];
+  }
+  const float t = turn_fraction(p.k_pos0 + key, tab.rev[c]);
+  const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+  const int g = (int)(unit % p.Hkv), b = (int)(unit / p.Hkv);
+  const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
+  p.dk[dst + rope_src_dim(c, D / 2, tab.interleaved)] = (__bf16)(kx * cs + ky * sn);
+  p.dk[dst + rope_src_dim(c + D / 2, D / 2, tab.interleaved)] = (__bf16)(ky * cs - kx * sn);
+  p.dv[dst + c] = (__bf16)vx;
+  p.dv[dst + c + D / 2] = (__bf16)vy;
+}
+
 template <int D>
 hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
   const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
@@ -802,23 +862,41 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(qblocks), dim3(256), 0, stream, p, tab);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.n_pairs));
+  const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.n_pairs * p.HS));
   const dim3 q_grid((unsigned)((long long)p.B * p.Hq * p.n_pairs));
   if constexpr (D == 256) {
-    hipLaunchKernelGGL((bwd_dkdv_d256_kernel<true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_dkdv_d256_kernel<false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    if (p.HS > 1) {
+      hipLaunchKernelGGL((bwd_dkdv_d256_kernel<true, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((bwd_dkdv_d256_kernel<false, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_d256_kernel<true, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((bwd_dkdv_d256_kernel<false, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(bwd_dq_d256_kernel, q_grid, dim3(64), 0, stream, p, tab);
-    return hipGetLastError();
-  } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+  } else {
+    if (p.HS > 1) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, q_grid, dim3(64), 0, stream, p, tab);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (p.HS > 1) {
+    const long long n = (long long)p.B * p.Hkv * p.NB * BR * (D / 2);
+    hipLaunchKernelGGL(bwd_part_reduce_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, tab);
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
 template hipError_t launch_bwd<64>(const BwdParams &, const RopeTable &, hipStream_t);
