@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
 SOURCES = ["attn_api.cpp", "prep_kv.hip", "attn_fwd_bf16.hip", "attn_fwd_d256.hip", "attn_fwd_f32.hip", "attn_merge.hip",
-           "attn_decode.hip", "attn_bwd.hip"]
+           "attn_decode.hip", "attn_bwd.hip", "attn_bwd_d256.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -34,6 +34,15 @@ COMMON_FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
     f"-I{CSRC}",
 ]
+
+# Per-source additions.  The backward kernels keep more than 256 registers live (one wave per
+# SIMD): by default the compiler then places MFMA results in accumulation registers and moves
+# them to the vector registers the softmax arithmetic reads, ~100 moves per step; with the
+# vector-register form of the MFMA instructions it uses the accumulation registers only as
+# storage for MFMA operands, which the MFMA reads directly.
+EXTRA_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc():
@@ -61,7 +70,7 @@ def build(verbose=False, jobs=4):
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([cc, *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([cc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
