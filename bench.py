@@ -38,11 +38,11 @@ CSRC = os.path.join(ROOT, "transformer_causal_attention_amd", "csrc")
 # while the kernel sources hash to the value it was taken with; otherwise traffic is null.
 PMC_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 MEASURED_TRAFFIC = {
-    "llama3_8b": {"sources_sha256": "7117b1e3b4cf7017", "FETCH_SIZE_KiB": 16617.41, "WRITE_SIZE_KiB": 24848.0},
-    "palm_mqa": {"sources_sha256": "7117b1e3b4cf7017", "FETCH_SIZE_KiB": 7365.44, "WRITE_SIZE_KiB": 10504.0},
-    "smollm_mha": {"sources_sha256": "7117b1e3b4cf7017", "FETCH_SIZE_KiB": 41385.89, "WRITE_SIZE_KiB": 49915.89},
-    "long_shard": {"sources_sha256": "7117b1e3b4cf7017", "FETCH_SIZE_KiB": 1107002.29, "WRITE_SIZE_KiB": 266241.88},
-    "palm540b_d256": {"sources_sha256": "cc0e6d08afaca213", "FETCH_SIZE_KiB": 37884.9, "WRITE_SIZE_KiB": 49612.84},
+    "llama3_8b": {"sources_sha256": "861a4383230c4d82", "FETCH_SIZE_KiB": 16617.41, "WRITE_SIZE_KiB": 24848.0},
+    "palm_mqa": {"sources_sha256": "861a4383230c4d82", "FETCH_SIZE_KiB": 7366.23, "WRITE_SIZE_KiB": 10504.0},
+    "smollm_mha": {"sources_sha256": "861a4383230c4d82", "FETCH_SIZE_KiB": 41396.72, "WRITE_SIZE_KiB": 49898.07},
+    "long_shard": {"sources_sha256": "861a4383230c4d82", "FETCH_SIZE_KiB": 1106943.0, "WRITE_SIZE_KiB": 266242.04},
+    "palm540b_d256": {"sources_sha256": "a06e174a962e6ba8", "FETCH_SIZE_KiB": 37831.38, "WRITE_SIZE_KiB": 49615.95},
 }
 
 
