@@ -42,6 +42,7 @@ COMMON_FLAGS = [
 # storage for MFMA operands, which the MFMA reads directly.
 EXTRA_FLAGS = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_bwd_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
