@@ -576,7 +576,7 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
   const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.n_pairs * p.HS));
   const dim3 q_grid((unsigned)((long long)p.B * p.Hq * p.n_pairs));
   if constexpr (D == 256) {
-    if ((err = launch_bwd_d256_main(p, tab, kv_grid, q_grid, stream)) != hipSuccess) return err;
+    if ((err = launch_bwd_d256_main(p, tab, stream)) != hipSuccess) return err;
   } else {
     if (p.HS > 1) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);

@@ -12,8 +12,7 @@
 namespace attn {
 
 // launches the head_dim 256 dk/dv and dq kernels (attn_bwd_d256.hip)
-hipError_t launch_bwd_d256_main(const BwdParams &p, const RopeTable &tab, dim3 kv_grid, dim3 q_grid,
-                                hipStream_t stream);
+hipError_t launch_bwd_d256_main(const BwdParams &p, const RopeTable &tab, hipStream_t stream);
 
 namespace {
 

@@ -31,20 +31,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d256_kernel(BwdParams p, Rope
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int nthreads = 64 * p.W;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int blk = xcd_order(blockIdx.x, gridDim.x);
-  const int pair = blk % p.n_pairs;
+  // One key block per workgroup, the heaviest first: a causal key block kb is seen by the
+  // NB - kb query blocks from kb on, so the grid's rounds run from kb = 0 up and the last,
+  // partial round holds the lightest blocks.
   const int n_hs = SPLIT ? p.HS : 1;          // head splits (SPLIT: more than one)
-  const int hs = SPLIT ? (blk / p.n_pairs) % n_hs : 0;
-  const int unit = blk / p.n_pairs / n_hs;     // b * Hkv + g
+  const int per_kb = p.B * p.Hkv * n_hs;
+  const int kb_rank = blockIdx.x / per_kb, rest = blockIdx.x % per_kb;
+  const int hs = SPLIT ? rest % n_hs : 0;
+  const int unit = rest / n_hs;                // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const int c_off = hh * BR * 8 + l32 * 8;  // this lane's operand in a "c" tile (chunk 2kk + hh)
   const int delta = p.q_pos0 - p.k_pos0;
 
-  for (int side = 0; side < 2; ++side) {
-    const int kb = side == 0 ? pair : p.NB - 1 - pair;
-    if (side == 1 && kb == pair) break;
+  {
+    const int kb = kb_rank;
     const size_t ktile = ((size_t)unit * p.NB + kb) * T;
-    __syncthreads();  // the previous block's operands are no longer read
     for (int i = threadIdx.x; i < T / 8; i += nthreads) {
       *reinterpret_cast<u32x4 *>(&kv[0][8 * i]) = *reinterpret_cast<const u32x4 *>(p.kc + ktile + 8 * i);
       if (!DV) *reinterpret_cast<u32x4 *>(&kv[DV ? 0 : 1][8 * i]) = *reinterpret_cast<const u32x4 *>(p.vc + ktile + 8 * i);
@@ -221,20 +222,19 @@ __global__ void __launch_bounds__(64, 1) bwd_dq_d256_kernel(BwdParams p, RopeTab
   __shared__ __attribute__((aligned(16))) __bf16 qd[2][T];  // query block: scaled rotated queries, dout
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int blk = xcd_order(blockIdx.x, gridDim.x);
-  const int pair = blk % p.n_pairs;
-  const int qunit = blk / p.n_pairs;  // b * Hq + h
+  // One query block per wave, the heaviest first (causal query block qb sees qb + 1 key blocks):
+  // the grid's rounds run from qb = NB - 1 down and the last, partial round holds the lightest.
+  const int qb_rank = blockIdx.x / (p.B * p.Hq);
+  const int qunit = blockIdx.x % (p.B * p.Hq);  // b * Hq + h
   const int h = qunit % p.Hq, b = qunit / p.Hq;
   const int g = h / p.G;
   const size_t kunit = (size_t)b * p.Hkv + g;
   const int c_off = hh * BR * 8 + l32 * 8;
   const int delta = p.q_pos0 - p.k_pos0;
 
-  for (int side = 0; side < 2; ++side) {
-    const int qb = side == 0 ? pair : p.NB - 1 - pair;
-    if (side == 1 && qb == pair) break;
+  {
+    const int qb = p.NB - 1 - qb_rank;
     const size_t qtile = ((size_t)qunit * p.NB + qb) * T;
-    __syncthreads();  // the previous block's operands are no longer read
     for (int i = lane; i < T / 8; i += 64) {
       *reinterpret_cast<u32x4 *>(&qd[0][8 * i]) = *reinterpret_cast<const u32x4 *>(p.qc + qtile + 8 * i);
       *reinterpret_cast<u32x4 *>(&qd[1][8 * i]) = *reinterpret_cast<const u32x4 *>(p.dc + qtile + 8 * i);
@@ -355,8 +355,9 @@ __global__ void __launch_bounds__(64, 1) bwd_dq_d256_kernel(BwdParams p, RopeTab
   }
 }
 
-hipError_t launch_bwd_d256_main(const BwdParams &p, const RopeTable &tab, dim3 kv_grid, dim3 q_grid,
-                                hipStream_t stream) {
+hipError_t launch_bwd_d256_main(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
+  const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.HS * p.NB));
+  const dim3 q_grid((unsigned)((long long)p.B * p.Hq * p.NB));
   if (p.HS > 1) {
     hipLaunchKernelGGL((bwd_dkdv_d256_kernel<true, true>), kv_grid, dim3(64 * p.W), 0, stream, p, tab);
     hipError_t err = hipGetLastError();
