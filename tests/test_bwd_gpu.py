@@ -64,6 +64,7 @@ SHAPES = [
     (1, 33, 2, 2, 256, True),    # head_dim 256, two blocks, second holds one row
     (1, 64, 48, 1, 256, True),   # PaLM-540B heads: 12 passes of 4 heads spread over 12 head splits
     (1, 80, 12, 1, 128, False),  # 3 passes over 3 head splits, full attention
+    (1, 150, 2, 2, 128, True),   # MHA at head_dim 128: single-block work items for every kernel
 ]
 
 
@@ -109,3 +110,23 @@ def test_bwd_deterministic():
         b = run_case(w, q, k, v, do)
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False),
+                                   (1, 96, 48, 1, 256, True)],
+                         ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_work_items_agree(shape, monkeypatch):
+    """Block pairs and single blocks (heaviest first) are two orders of the same work: every
+    block's sums run in the same order, so both give the same bits (ATTN_BWD_ITEMS forces one
+    kind for every kernel; head_dim 256 always runs single blocks)."""
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    res = {}
+    for items in ("pairs", "single"):
+        monkeypatch.setenv("ATTN_BWD_ITEMS", items)
+        res[items] = run_case(w, q, k, v, do)
+    for name, a, b in zip(("dq", "dk", "dv"), res["pairs"], res["single"]):
+        assert torch.equal(a, b), f"{w}: {name} differs between pairs and single blocks"

@@ -39,6 +39,8 @@
 // lists its rows in the order 16t + swap23(8(l/32) + e), which is the row order of the "t"
 // layout.
 
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "attn_bwd_common.h"
@@ -608,9 +610,14 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     // dk/dv in that last case only.  (Measured on the workloads: single dq blocks 17% faster on
     // PaLM MQA, 13% on SmolLM MHA, 31% on the 32K shard, 6% slower on Llama-3-8B; single dk/dv
     // blocks 10-19% faster on SmolLM MHA, 5-24% slower on Llama-3-8B and PaLM MQA.)
-    const bool single_kv = p.G == 1;
-    const bool single_q = p.G == 1 || p.NB > 64 ||
-                          (long long)p.B * p.Hq * p.n_pairs < bwd_dq_capacity<D>();
+    bool single_kv = p.G == 1;
+    bool single_q = p.G == 1 || p.NB > 64 || (long long)p.B * p.Hq * p.n_pairs < bwd_dq_capacity<D>();
+    // diagnostic: ATTN_BWD_ITEMS=pairs or =single forces one kind for every kernel (both give
+    // the same bits: each block's sums run in the same order either way)
+    if (const char *items = std::getenv("ATTN_BWD_ITEMS")) {
+      if (std::strcmp(items, "pairs") == 0) single_kv = single_q = false;
+      if (std::strcmp(items, "single") == 0) single_kv = single_q = true;
+    }
     const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.HS * (single_kv ? p.NB : p.n_pairs)));
     const dim3 q_grid((unsigned)((long long)p.B * p.Hq * (single_q ? p.NB : p.n_pairs)));
     const dim3 kv_block(64 * p.W);
