@@ -130,3 +130,22 @@ def test_bwd_work_items_agree(shape, monkeypatch):
         res[items] = run_case(w, q, k, v, do)
     for name, a, b in zip(("dq", "dk", "dv"), res["pairs"], res["single"]):
         assert torch.equal(a, b), f"{w}: {name} differs between pairs and single blocks"
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 257, 8, 1, 128, True), (2, 96, 16, 2, 64, True),
+                                   (1, 200, 6, 2, 128, False)],
+                         ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_dq_kernels_agree(shape, monkeypatch):
+    """The dq kernel that shares each key block's tiles between a group's heads through LDS and
+    the one that loads them per wave take the same operands in the same order: the same bits
+    (ATTN_BWD_DQ picks the kernel)."""
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq + 5)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    res = {}
+    for kind in ("regs", "shared"):
+        monkeypatch.setenv("ATTN_BWD_DQ", kind)
+        res[kind] = run_case(w, q, k, v, do)
+    assert torch.equal(res["regs"][0], res["shared"][0]), f"{w}: dq differs between the two dq kernels"

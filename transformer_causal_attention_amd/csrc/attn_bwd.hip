@@ -544,6 +544,183 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
 }
 
 // ---------------------------------------------------------------------------------------------
+// dq with the key blocks shared by the query heads of a K/V group.  Workgroup: W waves, wave w
+// one query head of the group (pass * W + w), all on the same query block; one query block per
+// workgroup, the heaviest first, renumbered within each block rank so that one XCD runs one K/V
+// group.  Each key block's three tiles (rotated keys in "c" and "t" layouts, values in "c"
+// layout, 3 * 32 * D bf16) are copied once per workgroup from L2 into LDS (16-byte loads
+// straight into LDS, the W waves taking turns) and every wave reads its MFMA operands there,
+// so the path from L2 into the CU carries each tile once per workgroup instead of once per
+// wave.  Double-buffered: the copy of block kb+1 runs during block kb; one barrier per block.
+// Same arithmetic, operand layouts, visibility and masks as bwd_dq_kernel.
+
+__device__ __forceinline__ void bwd_lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voff, soff, 0, 0);
+}
+
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  constexpr int TB = T * 2;               // bytes of one tile
+  constexpr int NPART = TB / 1024;        // 1 KiB copy instructions per tile
+  // key block operands, two buffers: [kc | vc | kt] each TB bytes
+  __shared__ __attribute__((aligned(1024))) char kbuf0[3 * TB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[3 * TB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int passes = (p.G + W - 1) / W;
+  const int per_qb = p.B * p.Hkv * passes;
+  const int qb = p.NB - 1 - (int)(blockIdx.x / per_qb);
+  const int item = xcd_order(blockIdx.x % per_qb, per_qb);
+  const int pass = item % passes;
+  const int kunit = item / passes;  // b * Hkv + g
+  const int g = kunit % p.Hkv, b = kunit / p.Hkv;
+  const int hc = pass * W + wave;   // head of the group this wave serves (none past G)
+  const bool has_head = hc < p.G;
+  const int h = g * p.G + (has_head ? hc : 0);
+  const size_t qunit = (size_t)b * p.Hq + h;
+  const int c_off = hh * BR * 8 + l32 * 8;
+  const int delta = p.q_pos0 - p.k_pos0;
+
+  const size_t qtile = (qunit * p.NB + qb) * T;
+  bf16x8 qf[NKK], df[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qf[kk] = ld16(p.qc + qtile + c_off + kk * 2 * BR * 8);
+    df[kk] = ld16(p.dc + qtile + c_off + kk * 2 * BR * 8);
+  }
+  // this lane's query: row l32 of the block
+  const float Lq = p.l2[(qunit * p.NB + qb) * BR + l32];
+  const float Dq = p.dd[(qunit * p.NB + qb) * BR + l32];
+  f32x16 dq[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
+  // key blocks with a key some row of this block sees: 32 kb <= 32 qb + 31 + delta
+  const int kb_end = p.causal ? min(p.NB, max(0, floor_div(BR * qb + BR - 1 + delta, BR) + 1)) : p.NB;
+
+  // this K/V head's run of key blocks as buffers (NB * T * 2 < 2^31 bytes)
+  const uint32_t run_t = (uint32_t)p.NB * TB;
+  const __amdgpu_buffer_rsrc_t kcb = raw_buffer(p.kc + (size_t)kunit * p.NB * T, run_t);
+  const __amdgpu_buffer_rsrc_t vcb = raw_buffer(p.vc + (size_t)kunit * p.NB * T, run_t);
+  const __amdgpu_buffer_rsrc_t ktb = raw_buffer(p.kt + (size_t)kunit * p.NB * T, run_t);
+  // this wave's share of the copies of key block kb into dst: KiB wave, wave + W, ... of each
+  // tile (the tile, and so the buffer resource, known at compile time)
+  auto copy_block = [&](int kb, char *dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const __amdgpu_buffer_rsrc_t r = t == 0 ? kcb : t == 1 ? vcb : ktb;
+#pragma unroll
+      for (int i = 0; i < (NPART + W - 1) / W; ++i) {
+        const int part = wave + W * i;
+        if (NPART % W == 0 || part < NPART)
+          bwd_lds_dma16(r, 16u * lane, (uint32_t)kb * TB + part * 1024, dst + t * TB + part * 1024);
+      }
+    }
+  };
+  const int v_c = 2 * c_off, v_t = 16 * (hh * D + l32);
+  auto step = [&](int kb, const char *src) __attribute__((always_inline)) {
+    f32x16 st = f32x16{}, dpt = f32x16{};
+    // the score products' operands are read from LDS first, all of them, then used
+    bf16x8 ka[NKK], va[NKK], kt[2][NCB];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      ka[kk] = *reinterpret_cast<const bf16x8 *>(src + v_c + kk * 2 * BR * 16);
+      va[kk] = *reinterpret_cast<const bf16x8 *>(src + TB + v_c + kk * 2 * BR * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      st = bwd_mfma(ka[kk], qf[kk], st);
+      dpt = bwd_mfma(va[kk], df[kk], dpt);
+    }
+    // the gradient product's operands are read while the softmax arithmetic runs
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        kt[tt][cb] = *reinterpret_cast<const bf16x8 *>(src + 2 * TB + v_t + (tt * 2 * D + 32 * cb) * 16);
+    // key kb*32 + k is later than row qb*32 + l32 iff k - l32 > rel, i.e. (k = res_row(v, hh))
+    // iff 8(v/4) + v%4 > thr.  Keys past S: those of the last block from S - 32 kb on.
+    const int rel = BR * (qb - kb) + delta;
+    const bool masked = (p.causal && rel < BR - 1) || (kb + 1) * BR > p.S;  // wave-uniform
+    const int thr = (p.causal && rel < BR - 1) ? rel + l32 - 4 * hh : 27;
+    const int kend = p.S - kb * BR - 4 * hh;
+    bf16x8 sa[2];
+    auto probs = [&](bool msk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        u32x4 ws;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float sv[2];
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int v = 8 * tt + e + z;
+            float pr = __builtin_amdgcn_exp2f(st[v] - Lq);
+            if (msk) pr = ((8 * (v >> 2) + (v & 3) > thr) | (8 * (v >> 2) + (v & 3) >= kend)) ? 0.f : pr;
+            sv[z] = pr * (dpt[v] - Dq);
+          }
+          ws[e / 2] = pack_bf16x2(sv[0], sv[1]);
+        }
+        sa[tt] = __builtin_bit_cast(bf16x8, ws);
+      }
+    };
+    if (masked)
+      probs(true);
+    else
+      probs(false);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        dq[cb] = bwd_mfma(sa[tt], kt[tt][cb], dq[cb]);
+  };
+  // Block kb sits in buffer kb % 2.  Before block kb: its copy is in (issued a block earlier)
+  // and every wave has finished block kb - 1; then the copy of block kb + 1 goes into the
+  // buffer block kb - 1 used.
+  if (kb_end > 0) copy_block(0, kbuf0);
+  for (int kb = 0; kb < kb_end; kb += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < kb_end) copy_block(kb + 1, kbuf1);
+    step(kb, kbuf0);
+    if (kb + 1 < kb_end) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kb + 2 < kb_end) copy_block(kb + 2, kbuf0);
+      step(kb + 1, kbuf1);
+    }
+  }
+  if (!has_head) return;
+  // result lane = column 32 cb + l32, register v = query 8(v/4) + 4 hh + v%4 of the block
+#pragma unroll
+  for (int cb = 0; cb < NCB / 2; ++cb) {
+    const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = qb * BR + res_row(v, hh);
+      const float t = turn_fraction(p.q_pos0 + row, rev);
+      const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+      const float x = dq[cb][v] * p.inv_sqrt_d, y = dq[cb + NCB / 2][v] * p.inv_sqrt_d;
+      dq[cb][v] = x * cs + y * sn;
+      dq[cb + NCB / 2][v] = y * cs - x * sn;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = qb * BR + res_row(v, hh);
+    if (row < p.S) {
+      const size_t dst = (((size_t)b * p.S + row) * p.Hq + h) * D;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) p.dq[dst + rope_src_dim(32 * cb + l32, D / 2, tab.interleaved)] = (__bf16)dq[cb][v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Head-split reduction: dk and dv of key j are the sums over the head splits' partials, added
 // in split order (deterministic); dk' is then rotated back by the key's angle, as in the
 // kernels' own epilogue.  One thread per (unit, key, column pair c, c + D/2).
@@ -638,10 +815,25 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
       if ((err = launch_kv(yes, no)) != hipSuccess) return err;
       if ((err = launch_kv(no, no)) != hipSuccess) return err;
     }
-    if (single_q)
+    bool shared_q = p.G >= 2;
+    if (const char *dqk = std::getenv("ATTN_BWD_DQ")) {
+      if (std::strcmp(dqk, "shared") == 0) shared_q = true;
+      if (std::strcmp(dqk, "regs") == 0) shared_q = false;
+    }
+    if (shared_q) {
+      const int passes = (p.G + p.W - 1) / p.W;
+      const dim3 sq_grid((unsigned)((long long)p.NB * p.B * p.Hkv * passes));
+      switch (p.W) {
+        case 1: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 1>), sq_grid, dim3(64), 0, stream, p, tab); break;
+        case 2: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 2>), sq_grid, dim3(128), 0, stream, p, tab); break;
+        case 3: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 3>), sq_grid, dim3(192), 0, stream, p, tab); break;
+        default: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 4>), sq_grid, dim3(256), 0, stream, p, tab); break;
+      }
+    } else if (single_q) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, true>), q_grid, dim3(64), 0, stream, p, tab);
-    else
+    } else {
       hipLaunchKernelGGL((bwd_dq_kernel<D, false>), q_grid, dim3(64), 0, stream, p, tab);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (p.HS > 1) {
