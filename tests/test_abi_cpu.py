@@ -253,13 +253,34 @@ def test_decode_rejections(over, code):
     assert decode_call(**over) == code
 
 
+def bwd_ws_expected(B, S, Hq, Hkv, d):
+    # 3 key-side and 4 query-side tiles of 32 rows x d bf16 per block, 2 floats per query row,
+    # and with HS > 1 head splits 2 x HS fp32 partial dk/dv blocks per K/V head.  HS: head_dim
+    # 64/128 aim at 2048 waves of one key block each (key blocks in groups of 4), at most one
+    # split per query head of the group; head_dim 256 at 512 workgroups of a key-block pair,
+    # at most one split per pass of 4 heads.
+    nb = (S + 31) // 32
+    G = Hq // Hkv
+    if d == 256:
+        groups = B * Hkv * ((nb + 1) // 2)
+        hs = max(1, min(-(-G // min(G, 4)), -(-512 // groups)))
+    else:
+        waves = B * Hkv * -(-nb // 4) * 4
+        hs = max(1, min(G, -(-2048 // waves)))
+    part = 2 * hs * B * Hkv * nb * 32 * d * 4 if hs > 1 else 0
+    return (3 * B * Hkv + 4 * B * Hq) * nb * 32 * d * 2 + 2 * B * Hq * nb * 32 * 4 + part
+
+
 def test_bwd_workspace_bytes():
-    # 3 key-side and 4 query-side tiles of 32 rows x d bf16 per block, 2 floats per query row
+    # B2 S100 Hq8 Hkv2 d128: 4 blocks, 16 waves -> 4 head splits (one per query head)
     nb = (100 + 31) // 32
-    assert _lib.bwd_workspace_bytes(2, 100, 8, 2, 128) == (3 * 2 * 2 + 4 * 2 * 8) * nb * 32 * 128 * 2 + 2 * 2 * 8 * nb * 32 * 4
-    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 64) == (3 + 4 * 4) * 2 * 32 * 64 * 2 + 2 * 4 * 2 * 32 * 4
+    assert _lib.bwd_workspace_bytes(2, 100, 8, 2, 128) == ((3 * 2 * 2 + 4 * 2 * 8) * nb * 32 * 128 * 2
+                                                           + 2 * 2 * 8 * nb * 32 * 4 + 2 * 4 * 2 * 2 * nb * 32 * 128 * 4)
+    # Llama-3-8B backward: 64 blocks, 512 waves -> 4 splits; SmolLM MHA: one head per group
+    for shape in [(2, 100, 8, 2, 128), (1, 2048, 32, 8, 128), (4, 1024, 32, 32, 64), (8, 1024, 8, 1, 64),
+                  (1, 32768, 32, 8, 128), (1, 2048, 48, 1, 256), (1, 64, 4, 1, 64), (1, 64, 4, 1, 256)]:
+        assert _lib.bwd_workspace_bytes(*shape) == bwd_ws_expected(*shape), shape
     assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 96) == 0
-    assert _lib.bwd_workspace_bytes(1, 64, 4, 1, 256) == (3 + 4 * 4) * 2 * 32 * 256 * 2 + 2 * 4 * 2 * 32 * 4
     assert _lib.bwd_workspace_bytes(1, 64, 6, 4, 64) == 0
 
 

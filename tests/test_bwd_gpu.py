@@ -118,18 +118,44 @@ def test_bwd_deterministic():
 def test_bwd_work_items_agree(shape, monkeypatch):
     """Block pairs and single blocks (heaviest first) are two orders of the same work: every
     block's sums run in the same order, so both give the same bits (ATTN_BWD_ITEMS forces one
-    kind for every kernel; head_dim 256 always runs single blocks)."""
+    kind for every kernel, ATTN_BWD_KV=waves picks the dk/dv kernels that take such items;
+    head_dim 256 always runs single blocks)."""
     B, S, Hq, Hkv, d, causal = shape
     w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq)
     q, k, v = make_inputs(w)
     do = dout_of(w)
     say(w)
+    monkeypatch.setenv("ATTN_BWD_KV", "waves")
     res = {}
     for items in ("pairs", "single"):
         monkeypatch.setenv("ATTN_BWD_ITEMS", items)
         res[items] = run_case(w, q, k, v, do)
     for name, a, b in zip(("dq", "dk", "dv"), res["pairs"], res["single"]):
         assert torch.equal(a, b), f"{w}: {name} differs between pairs and single blocks"
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False),
+                                   (1, 150, 2, 2, 128, True)],
+                         ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_kv_kernels_agree(shape, monkeypatch):
+    """dk and dv from the kernel that shares query blocks between four key blocks and from the
+    one that gives each query head a wave: the same sums over the group's heads in another
+    order, so they agree to a few bf16 roundings (ATTN_BWD_KV picks the kernel)."""
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq + 3)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    res = {}
+    for kind in ("waves", "shared"):
+        monkeypatch.setenv("ATTN_BWD_KV", kind)
+        res[kind] = run_case(w, q, k, v, do)
+    assert torch.equal(res["waves"][0], res["shared"][0]), f"{w}: dq depends on the dk/dv kernel"
+    for name, a, b in zip(("dk", "dv"), res["waves"][1:], res["shared"][1:]):
+        a, b = a.float(), b.float()
+        err = (a - b).abs().max().item()
+        scale = a.abs().max().item()
+        assert err <= 2 ** -6 * scale, f"{w}: {name} max difference {err} (scale {scale})"
 
 
 @pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 257, 8, 1, 128, True), (2, 96, 16, 2, 64, True),

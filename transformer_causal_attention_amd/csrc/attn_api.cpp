@@ -536,19 +536,32 @@ constexpr int kBwdRows = 32;  // query and key block of the backward kernels
 
 size_t bwd_blocks(int S) { return ((size_t)S + kBwdRows - 1) / kBwdRows; }
 
-// Head splits of the dk/dv kernels: a (b, g, key-block pair) workgroup takes its group's query
-// heads W = min(G, 4) at a time; when there are few such workgroups and several passes of
+// Head splits of the dk/dv kernels at head_dim 256: a (b, g, key-block pair) workgroup takes its
+// group's query heads W = min(G, 4) at a time; when there are few such workgroups and several passes of
 // heads (PaLM-540B: 32 workgroups, 12 passes), the passes are spread over HS workgroups that
 // leave fp32 partial sums for a reduction kernel.  Aimed at kBwdTargetGroups workgroups (two
 // per CU of a 256-CU GPU); a function of the shapes only, so the workspace size is too.
 constexpr long long kBwdTargetGroups = 512;
 
-int bwd_head_splits(int B, int Hkv, int G, size_t nb) {
+int bwd_head_splits_pairs(int B, int Hkv, int G, size_t nb) {
   const int W = std::min(G, 4);
   const long long passes = (G + W - 1) / W;
   const long long groups = (long long)B * Hkv * (long long)((nb + 1) / 2);
   const long long want = (kBwdTargetGroups + groups - 1) / groups;
   return (int)std::max(1LL, std::min(passes, want));
+}
+
+// head_dim 64 and 128: the dk/dv kernels share each query block between four consecutive key
+// blocks (one wave each) and run a head split's query heads one after another; the splits are
+// aimed at kBwdTargetWaves waves (two per SIMD of a 256-CU GPU), at most one per head.  A
+// function of the shapes only, so the workspace size is too.
+constexpr long long kBwdTargetWaves = 2048;
+
+int bwd_head_splits(int B, int Hkv, int G, size_t nb, int head_dim) {
+  if (head_dim == 256) return bwd_head_splits_pairs(B, Hkv, G, nb);
+  const long long waves = (long long)B * Hkv * (long long)((nb + 3) / 4) * 4;
+  const long long want = (kBwdTargetWaves + waves - 1) / waves;
+  return (int)std::max(1LL, std::min((long long)G, want));
 }
 
 }  // namespace
@@ -557,7 +570,7 @@ ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int h
   if (check_shape(B, S, Hq, Hkv, head_dim, 1.0, 1, ATTN_DTYPE_BF16) != ATTN_OK) return 0;
   const size_t nb = bwd_blocks(S);
   const size_t tile = (size_t)kBwdRows * head_dim * 2;
-  const int hs = bwd_head_splits(B, Hkv, Hq / Hkv, nb);
+  const int hs = bwd_head_splits(B, Hkv, Hq / Hkv, nb, head_dim);
   const size_t part = hs > 1 ? 2 * (size_t)hs * B * Hkv * nb * kBwdRows * head_dim * 4 : 0;
   return 3 * (size_t)B * Hkv * nb * tile + 4 * (size_t)B * Hq * nb * tile + 2 * (size_t)B * Hq * nb * kBwdRows * 4 + part;
 }
@@ -601,7 +614,7 @@ ATTN_EXPORT int attn_bwd_shard(const void *q, const void *k, const void *v, cons
   p.l2 = reinterpret_cast<float *>(p.dt + qt_n);
   p.dd = p.l2 + (size_t)B * Hq * nb * kBwdRows;
   p.part = p.dd + (size_t)B * Hq * nb * kBwdRows;
-  p.HS = bwd_head_splits(B, Hkv, G, nb);
+  p.HS = bwd_head_splits(B, Hkv, G, nb, head_dim);
   p.B = B;
   p.S = S;
   p.Hq = Hq;

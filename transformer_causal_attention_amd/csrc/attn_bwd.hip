@@ -721,6 +721,218 @@ __global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, Rope
 }
 
 // ---------------------------------------------------------------------------------------------
+// dv (DV) or dk (!DV) with the query blocks shared by consecutive key blocks.  Workgroup: KW = 4
+// waves, wave w key block kg * KW + w of K/V head (b, g); the group's query heads of this head
+// split (hs, hs + HS, ...) one after another, and for each the query blocks from the last one
+// down.  Each query block's tiles (scaled rotated queries in "c" layout, dout in "c" layout for
+// dk, queries ("t") for dk or dout ("t") for dv) are copied once per workgroup from L2 into LDS
+// (16-byte loads straight into LDS, the waves taking turns, double-buffered, one barrier per
+// block), with the block's 32 lse and rowsum values, and every wave reads its MFMA operands and
+// those values there (read from global memory at the step that needs them, their latency showed
+// in every step).  A wave skips the blocks that see none of its keys.  Its sums over the heads stay in its registers: dk is rotated back and written (or,
+// with head splits, left as fp32 partials for bwd_part_reduce).  Work items: key-block groups,
+// the heaviest (kg = 0) first, renumbered within each so that one XCD runs one K/V head.
+
+constexpr int KW = 4;  // key blocks (waves) per workgroup
+
+template <int D, bool DV, bool SPLIT>
+__global__ void __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 registers
+bwd_dkdv_shared_kernel(BwdParams p, RopeTable tab) {
+  constexpr int NKK = D / 16;
+  constexpr int NCB = D / 32;
+  constexpr int T = BR * D;
+  constexpr int TB = T * 2;             // bytes of one tile
+  constexpr int NPART = TB / 1024;      // 1 KiB copy instructions per tile
+  constexpr int NT = DV ? 2 : 3;        // tiles per query block: [qc | dt] or [qc | dc | qt]
+  constexpr int RB = NT * TB;           // then 1 KiB for the block's lse rows, 1 KiB for its rowsums
+  __shared__ __attribute__((aligned(1024))) char qbuf0[RB + 2048];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[RB + 2048];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int n_hs = SPLIT ? p.HS : 1;
+  const int per_kg = p.B * p.Hkv * n_hs;
+  const int kg = (int)(blockIdx.x / per_kg);
+  const int item = xcd_order(blockIdx.x % per_kg, per_kg);
+  const int hs = SPLIT ? item % n_hs : 0;
+  const int unit = item / n_hs;  // b * Hkv + g
+  const int g = unit % p.Hkv, b = unit / p.Hkv;
+  const int kb = kg * KW + wave;
+  const bool has_kb = kb < p.NB;
+  const int kbc = has_kb ? kb : p.NB - 1;  // (a wave past the last block computes on the last one and writes nothing)
+  const int c_off = hh * BR * 8 + l32 * 8;
+  const int delta = p.q_pos0 - p.k_pos0;
+  const size_t ktile = ((size_t)unit * p.NB + kbc) * T;
+  bf16x8 kf[NKK], vf[DV ? 1 : NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
+    if (!DV) vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+  }
+  const bool key_ok = kbc * BR + l32 < p.S;
+  const bool key_ok_all = (kbc + 1) * BR <= p.S;
+  // the first query block with a row that sees a key of block kb: 32 qb + 31 + delta >= 32 kb
+  auto qb_lo_of = [&](int k) __attribute__((always_inline)) {
+    return p.causal ? max(0, floor_div(BR * k - delta, BR)) : 0;
+  };
+  const int my_qb_lo = qb_lo_of(kbc);
+  const int wg_qb_lo = qb_lo_of(kg * KW);  // the workgroup's first key block sees the most
+  f32x16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+  const int v_c = 2 * c_off, v_t = 16 * (hh * D + l32), v_r = 16 * hh;
+  const uint32_t run_t = (uint32_t)p.NB * TB, run_r = (uint32_t)p.NB * BR * 4;
+
+  for (int hc = hs; hc < p.G; hc += n_hs) {
+    const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
+    const __amdgpu_buffer_rsrc_t qcb = raw_buffer(p.qc + qunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t dcb = raw_buffer(p.dc + qunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t tb_ = raw_buffer((DV ? p.dt : p.qt) + qunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t lbuf = raw_buffer(p.l2 + qunit * p.NB * BR, run_r);
+    const __amdgpu_buffer_rsrc_t ddbuf = raw_buffer(p.dd + qunit * p.NB * BR, run_r);
+    // this wave's share of the copies of query block qb into dst: KiB wave, wave + KW, ... of
+    // each tile (the tile, and so the buffer resource, known at compile time)
+    auto copy_block = [&](int qb, char *dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const __amdgpu_buffer_rsrc_t r = t == 0 ? qcb : (DV || t == 2) ? tb_ : dcb;
+#pragma unroll
+        for (int i = 0; i < (NPART + KW - 1) / KW; ++i) {
+          const int part = wave + KW * i;
+          if (NPART % KW == 0 || part < NPART)
+            bwd_lds_dma16(r, 16u * lane, (uint32_t)qb * TB + part * 1024, dst + t * TB + part * 1024);
+        }
+      }
+      // the block's 32 lse (and rowsum) values: 128 bytes from lanes 0..7; the other lanes'
+      // offsets lie past the buffer's end, so they read nothing
+      const uint32_t roff = lane < 8 ? (uint32_t)qb * BR * 4 + 16u * lane : 0x80000000u;
+      if (wave == KW - 1) bwd_lds_dma16(lbuf, roff, 0, dst + RB);
+      if (!DV && wave == KW - 2) bwd_lds_dma16(ddbuf, roff, 0, dst + RB + 1024);
+    };
+    auto step = [&](int qb, const char *src) __attribute__((always_inline)) {
+      if (qb < my_qb_lo) return;  // no key of this wave's block is seen by this query block
+      bf16x8 qa[NKK], da[DV ? 1 : NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        qa[kk] = *reinterpret_cast<const bf16x8 *>(src + v_c + kk * 2 * BR * 16);
+        if (!DV) da[kk] = *reinterpret_cast<const bf16x8 *>(src + TB + v_c + kk * 2 * BR * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = bwd_mfma(qa[kk], kf[kk], s);
+        if (!DV) dp = bwd_mfma(da[kk], vf[kk], dp);
+      }
+      // lse and rowsum of this lane's rows 8c + 4hh + 0..3
+      f32x4 L[4], Dd[DV ? 1 : 4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        L[c] = *reinterpret_cast<const f32x4 *>(src + RB + v_r + 32 * c);
+        if (!DV) Dd[c] = *reinterpret_cast<const f32x4 *>(src + RB + 1024 + v_r + 32 * c);
+      }
+      const char *tsrc = src + (NT - 1) * TB;
+      bf16x8 tb[2][NCB];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          tb[tt][cb] = *reinterpret_cast<const bf16x8 *>(tsrc + v_t + (tt * 2 * D + 32 * cb) * 16);
+      // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel, i.e. (r = res_row(v, hh))
+      // iff 8(v/4) + v%4 < thr: one threshold per lane, applied by selects in the steps that
+      // need it (a key past S masks every row, thr 32)
+      const int rel = BR * (qb - kbc) + delta;
+      const bool masked = !key_ok_all || (p.causal && rel < BR - 1);  // wave-uniform
+      const int thr = !key_ok ? 32 : (p.causal && rel < BR - 1) ? l32 - 4 * hh - rel : 0;
+      bf16x8 op[2];
+      auto probs = [&](bool msk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          u32x4 wv;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float x[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const int v = 8 * tt + e + z;
+              float pr = __builtin_amdgcn_exp2f(s[v] - L[v >> 2][v & 3]);
+              if (msk) pr = 8 * (v >> 2) + (v & 3) < thr ? 0.f : pr;
+              x[z] = DV ? pr : pr * (dp[v] - Dd[v >> 2][v & 3]);
+            }
+            wv[e / 2] = pack_bf16x2(x[0], x[1]);
+          }
+          op[tt] = __builtin_bit_cast(bf16x8, wv);
+        }
+      };
+      if (masked)
+        probs(true);
+      else
+        probs(false);
+      // dv += P^T dO, dk += dS^T (q'/sqrt(D))
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = bwd_mfma(op[tt], tb[tt][cb], acc[cb]);
+    };
+    // query block qb sits in buffer qb % 2 ... counted from the top: block NB-1-j in buffer j % 2.
+    // Before each block: its copy is in and every wave has finished the previous block; then
+    // the copy of the next block goes into the buffer the previous one used.
+    __syncthreads();  // the previous head's last block is no longer read
+    if (p.NB - 1 >= wg_qb_lo) copy_block(p.NB - 1, qbuf0);
+    for (int qb = p.NB - 1; qb >= wg_qb_lo; qb -= 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (qb - 1 >= wg_qb_lo) copy_block(qb - 1, qbuf1);
+      step(qb, qbuf0);
+      if (qb - 1 >= wg_qb_lo) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (qb - 2 >= wg_qb_lo) copy_block(qb - 2, qbuf0);
+        step(qb - 1, qbuf1);
+      }
+    }
+  }
+  if (!has_kb) return;
+  // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block
+  if constexpr (SPLIT) {
+    float *part = p.part + (((size_t)(DV ? n_hs : 0) + hs) * p.B * p.Hkv + unit) * p.NB * BR * D;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb * BR + res_row(v, hh);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) part[(size_t)key * D + 32 * cb + l32] = acc[cb][v];
+    }
+  } else {
+    if (!DV) {
+#pragma unroll
+      for (int cb = 0; cb < NCB / 2; ++cb) {
+        const double rev = tab.rev[32 * cb + l32];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BR + res_row(v, hh);
+          const float t = turn_fraction(p.k_pos0 + key, rev);
+          const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+          const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
+          acc[cb][v] = x * cs + y * sn;
+          acc[cb + NCB / 2][v] = y * cs - x * sn;
+        }
+      }
+    }
+    __bf16 *dst0 = DV ? p.dv : p.dk;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb * BR + res_row(v, hh);
+      if (key < p.S) {
+        const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
+        const int il = DV ? 0 : tab.interleaved;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Head-split reduction: dk and dv of key j are the sums over the head splits' partials, added
 // in split order (deterministic); dk' is then rotated back by the key's angle, as in the
 // kernels' own epilogue.  One thread per (unit, key, column pair c, c + D/2).
@@ -784,7 +996,7 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     // Work items of single blocks, heaviest first, instead of balanced pairs: for dq when the
     // pairs would leave SIMDs idle, when the key range is long (the waves of one round then sweep
     // nearby key blocks and share them in L2) or when every K/V head serves one query head; for
-    // dk/dv in that last case only.  (Measured on the workloads: single dq blocks 17% faster on
+    // the per-head dk/dv kernel (ATTN_BWD_KV=waves) in that last case only.  (Measured on the workloads: single dq blocks 17% faster on
     // PaLM MQA, 13% on SmolLM MHA, 31% on the 32K shard, 6% slower on Llama-3-8B; single dk/dv
     // blocks 10-19% faster on SmolLM MHA, 5-24% slower on Llama-3-8B and PaLM MQA.)
     bool single_kv = p.G == 1;
@@ -798,9 +1010,20 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     const dim3 kv_grid((unsigned)((long long)p.B * p.Hkv * p.HS * (single_kv ? p.NB : p.n_pairs)));
     const dim3 q_grid((unsigned)((long long)p.B * p.Hq * (single_q ? p.NB : p.n_pairs)));
     const dim3 kv_block(64 * p.W);
+    // dk/dv: query blocks shared by four consecutive key blocks (default), or (diagnostic,
+    // ATTN_BWD_KV=waves) one wave per query head of the group.  (Measured, dk + dv with their
+    // head-split reduction, against the per-head kernel with the splits it used alone: 12% less
+    // time on Llama-3-8B, 4% on PaLM MQA, 29% on SmolLM MHA, 38% on the 32K shard.)
+    // The head splits follow the shared kernel; the per-head one leaves splits past its last
+    // pass of heads idle (their partials are zeros).
+    bool shared_kv = true;
+    if (const char *kvk = std::getenv("ATTN_BWD_KV")) shared_kv = std::strcmp(kvk, "waves") != 0;
+    const dim3 skv_grid((unsigned)((long long)p.B * p.Hkv * p.HS * ((p.NB + KW - 1) / KW)));
     auto launch_kv = [&](auto dv, auto split) -> hipError_t {
       constexpr bool DV_ = decltype(dv)::value, SPLIT_ = decltype(split)::value;
-      if (single_kv)
+      if (shared_kv)
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, DV_, SPLIT_>), skv_grid, dim3(64 * KW), 0, stream, p, tab);
+      else if (single_kv)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV_, SPLIT_, true>), kv_grid, kv_block, 0, stream, p, tab);
       else
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV_, SPLIT_, false>), kv_grid, kv_block, 0, stream, p, tab);

@@ -154,10 +154,11 @@ struct BwdParams {
                               // q / sqrt(D) (t), dout (c, t)
   float *l2, *dd;           // (B, Hq, NB*32): lse * log2(e) (+inf past S); rowsum(dout * out)
   int B, S, Hq, Hkv, G, NB, n_pairs, W, causal;
-  // head splits of the dk/dv kernels: the HS workgroups of a (b, g, key-block pair) take the
-  // group's query heads in passes hs, hs + HS, ... of W heads and, when HS > 1, leave fp32
-  // partial sums in part ([2][HS][B*Hkv][NB*32][D]: dk' before its rotation back, then dv),
-  // which a reduction kernel adds up (in hs order) and writes
+  // head splits of the dk/dv kernels: the HS workgroups of a (b, g, key-block group) take the
+  // group's query heads hs, hs + HS, ... (head_dim 64, 128; head_dim 256 and the per-head
+  // kernel: passes hs, hs + HS, ... of W heads) and, when HS > 1, leave fp32 partial sums in
+  // part ([2][HS][B*Hkv][NB*32][D]: dk' before its rotation back, then dv), which a reduction
+  // kernel adds up (in hs order) and writes
   int HS;
   float *part;
   int q_pos0, k_pos0;       // positions of query row 0 and key row 0 (a sequence shard's offsets)
