@@ -135,6 +135,29 @@ def test_bwd_work_items_agree(shape, monkeypatch):
 
 
 @pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False),
+                                   (1, 150, 2, 2, 128, True), (1, 257, 8, 1, 128, True), (2, 96, 16, 2, 64, True)],
+                         ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_one_launch_agrees(shape, monkeypatch):
+    """dk, dv and (with four or more heads per K/V head) dq work items in one launch
+    (interleaved, heaviest first), dk and dv in one and dq in another, or a launch each
+    (ATTN_BWD_KVLAUNCH, ATTN_BWD_DQLAUNCH): every item computes the same sums, so the bits
+    agree."""
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq + 4)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    res = {}
+    for kind, kv, dq in (("split", "split", "split"), ("kv", "one", "split"), ("one", "one", "one")):
+        monkeypatch.setenv("ATTN_BWD_KVLAUNCH", kv)
+        monkeypatch.setenv("ATTN_BWD_DQLAUNCH", dq)
+        res[kind] = run_case(w, q, k, v, do)
+    for kind in ("kv", "one"):
+        for name, a, b in zip(("dq", "dk", "dv"), res["split"], res[kind]):
+            assert torch.equal(a, b), f"{w}: {name} differs between launches ({kind})"
+
+
+@pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False),
                                    (1, 150, 2, 2, 128, True)],
                          ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
 def test_bwd_kv_kernels_agree(shape, monkeypatch):

@@ -558,23 +558,29 @@ __device__ __forceinline__ void bwd_lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voff, soff, 0, 0);
 }
 
+// LDS of one key-block buffer of the shared dq kernel: [kc | vc | kt]
+template <int D>
+constexpr int bwd_dq_buf_bytes() {
+  return 3 * BR * D * 2;
+}
+
+// work item blk (query block NB - 1 - blk / per_qb: the heaviest first) with the two key-block
+// buffers kbuf0, kbuf1
 template <int D, int W>
-__global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, RopeTable tab) {
+__device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const RopeTable &tab, int blk, char *kbuf0,
+                                                   char *kbuf1) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
   constexpr int TB = T * 2;               // bytes of one tile
   constexpr int NPART = TB / 1024;        // 1 KiB copy instructions per tile
-  // key block operands, two buffers: [kc | vc | kt] each TB bytes
-  __shared__ __attribute__((aligned(1024))) char kbuf0[3 * TB];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[3 * TB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int passes = (p.G + W - 1) / W;
   const int per_qb = p.B * p.Hkv * passes;
-  const int qb = p.NB - 1 - (int)(blockIdx.x / per_qb);
-  const int item = xcd_order(blockIdx.x % per_qb, per_qb);
+  const int qb = p.NB - 1 - blk / per_qb;
+  const int item = xcd_order(blk % per_qb, per_qb);
   const int pass = item % passes;
   const int kunit = item / passes;  // b * Hkv + g
   const int g = kunit % p.Hkv, b = kunit / p.Hkv;
@@ -720,6 +726,12 @@ __global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, Rope
   }
 }
 
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, RopeTable tab) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * bwd_dq_buf_bytes<D>()];
+  bwd_dq_shared_item<D, W>(p, tab, (int)blockIdx.x, lds, lds + bwd_dq_buf_bytes<D>());
+}
+
 // ---------------------------------------------------------------------------------------------
 // dv (DV) or dk (!DV) with the query blocks shared by consecutive key blocks.  Workgroup: KW = 4
 // waves, wave w key block kg * KW + w of K/V head (b, g); the group's query heads of this head
@@ -729,31 +741,38 @@ __global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, Rope
 // (16-byte loads straight into LDS, the waves taking turns, double-buffered, one barrier per
 // block), with the block's 32 lse and rowsum values, and every wave reads its MFMA operands and
 // those values there (read from global memory at the step that needs them, their latency showed
-// in every step).  A wave skips the blocks that see none of its keys.  Its sums over the heads stay in its registers: dk is rotated back and written (or,
-// with head splits, left as fp32 partials for bwd_part_reduce).  Work items: key-block groups,
-// the heaviest (kg = 0) first, renumbered within each so that one XCD runs one K/V head.
+// in every step).  A wave skips the blocks that see none of its keys.  Its sums over the heads
+// stay in its registers: dk is rotated back and written (or, with head splits, left as fp32
+// partials for bwd_part_reduce).  Work items: key-block groups, the heaviest (kg = 0) first,
+// renumbered within each so that one XCD runs one K/V head.
 
 constexpr int KW = 4;  // key blocks (waves) per workgroup
 
+// LDS of one query-block buffer: NT tiles, then 1 KiB for the block's lse rows and 1 KiB for
+// its rowsums
+template <int D, bool DV>
+constexpr int bwd_kv_buf_bytes() {
+  return (DV ? 2 : 3) * BR * D * 2 + 2048;
+}
+
+// work item blk (key group blk / per_kg, the heaviest first) with the two buffers qbuf0, qbuf1
 template <int D, bool DV, bool SPLIT>
-__global__ void __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 registers
-bwd_dkdv_shared_kernel(BwdParams p, RopeTable tab) {
+__device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const RopeTable &tab, int blk, char *qbuf0,
+                                                     char *qbuf1) {
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
   constexpr int TB = T * 2;             // bytes of one tile
   constexpr int NPART = TB / 1024;      // 1 KiB copy instructions per tile
   constexpr int NT = DV ? 2 : 3;        // tiles per query block: [qc | dt] or [qc | dc | qt]
-  constexpr int RB = NT * TB;           // then 1 KiB for the block's lse rows, 1 KiB for its rowsums
-  __shared__ __attribute__((aligned(1024))) char qbuf0[RB + 2048];
-  __shared__ __attribute__((aligned(1024))) char qbuf1[RB + 2048];
+  constexpr int RB = NT * TB;           // then the lse and rowsum rows
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int n_hs = SPLIT ? p.HS : 1;
   const int per_kg = p.B * p.Hkv * n_hs;
-  const int kg = (int)(blockIdx.x / per_kg);
-  const int item = xcd_order(blockIdx.x % per_kg, per_kg);
+  const int kg = blk / per_kg;
+  const int item = xcd_order(blk % per_kg, per_kg);
   const int hs = SPLIT ? item % n_hs : 0;
   const int unit = item / n_hs;  // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
@@ -932,6 +951,35 @@ bwd_dkdv_shared_kernel(BwdParams p, RopeTable tab) {
   }
 }
 
+// KINDS 1: dk only; 2: dv only; 3: dk and dv in one launch; 7: dk, dv and dq (the shared dq
+// kernel with KW heads per workgroup) in one launch.  In one launch the work items go by
+// level, heaviest first: level j holds the dk and dv items of key group j and (KINDS 7) the dq
+// items of query blocks NB-1-4j down to NB-4-4j, which see as many key blocks as key group j
+// sees query blocks; within a level the dk items (three products per step) come first.  The
+// light items of every kind then fill the CUs as the heavy ones end.
+template <int D, bool SPLIT, int KINDS>
+__global__ void __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 registers
+bwd_dkdv_shared_kernel(BwdParams p, RopeTable tab) {
+  constexpr int BUF = KINDS == 2 ? bwd_kv_buf_bytes<D, true>() : bwd_kv_buf_bytes<D, false>();
+  static_assert(KINDS != 7 || bwd_dq_buf_bytes<D>() <= BUF, "the dq buffers fit in the dk ones");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
+  const int blk = (int)blockIdx.x;
+  if constexpr (KINDS == 3 || KINDS == 7) {
+    const int per_kg = p.B * p.Hkv * (SPLIT ? p.HS : 1);
+    const int per_q = KINDS == 7 ? p.B * p.Hkv * ((p.G + KW - 1) / KW) : 0;  // dq items per query block
+    const int L = 2 * per_kg + KW * per_q;                                 // items per level
+    const int lvl = blk / L, r = blk % L;
+    if (r < per_kg)
+      bwd_dkdv_shared_item<D, false, SPLIT>(p, tab, lvl * per_kg + r, lds, lds + bwd_kv_buf_bytes<D, false>());
+    else if (r < 2 * per_kg)
+      bwd_dkdv_shared_item<D, true, SPLIT>(p, tab, lvl * per_kg + r - per_kg, lds, lds + bwd_kv_buf_bytes<D, true>());
+    else if constexpr (KINDS == 7)
+      bwd_dq_shared_item<D, KW>(p, tab, lvl * KW * per_q + r - 2 * per_kg, lds, lds + bwd_dq_buf_bytes<D>());
+  } else {
+    bwd_dkdv_shared_item<D, KINDS == 2, SPLIT>(p, tab, blk, lds, lds + BUF);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Head-split reduction: dk and dv of key j are the sums over the head splits' partials, added
 // in split order (deterministic); dk' is then rotated back by the key's angle, as in the
@@ -981,6 +1029,24 @@ long long bwd_dq_capacity() {
   return cap;
 }
 
+// workgroups of a one-launch kernel the GPU holds at once; cached per head split mode
+template <int D, int KINDS>
+long long bwd_kv_capacity(bool split) {
+  static long long cap[2] = {-1, -1};
+  long long &c = cap[split ? 1 : 0];
+  if (c < 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    const hipError_t e =
+        split ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dkdv_shared_kernel<D, true, KINDS>, 64 * KW, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_dkdv_shared_kernel<D, false, KINDS>, 64 * KW, 0);
+    if (e != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;  // unknown: two launches
+    c = (long long)cus * per_cu;
+  }
+  return c;
+}
+
 template <int D>
 hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
   const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
@@ -996,9 +1062,10 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     // Work items of single blocks, heaviest first, instead of balanced pairs: for dq when the
     // pairs would leave SIMDs idle, when the key range is long (the waves of one round then sweep
     // nearby key blocks and share them in L2) or when every K/V head serves one query head; for
-    // the per-head dk/dv kernel (ATTN_BWD_KV=waves) in that last case only.  (Measured on the workloads: single dq blocks 17% faster on
-    // PaLM MQA, 13% on SmolLM MHA, 31% on the 32K shard, 6% slower on Llama-3-8B; single dk/dv
-    // blocks 10-19% faster on SmolLM MHA, 5-24% slower on Llama-3-8B and PaLM MQA.)
+    // the per-head dk/dv kernel (ATTN_BWD_KV=waves) in that last case only.  (Measured on the
+    // workloads: single dq blocks 17% faster on PaLM MQA, 13% on SmolLM MHA, 31% on the 32K
+    // shard, 6% slower on Llama-3-8B; single dk/dv blocks 10-19% faster on SmolLM MHA, 5-24%
+    // slower on Llama-3-8B and PaLM MQA.)
     bool single_kv = p.G == 1;
     bool single_q = p.G == 1 || p.NB > 64 || (long long)p.B * p.Hq * p.n_pairs < bwd_dq_capacity<D>();
     // diagnostic: ATTN_BWD_ITEMS=pairs or =single forces one kind for every kernel (both give
@@ -1022,7 +1089,7 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     auto launch_kv = [&](auto dv, auto split) -> hipError_t {
       constexpr bool DV_ = decltype(dv)::value, SPLIT_ = decltype(split)::value;
       if (shared_kv)
-        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, DV_, SPLIT_>), skv_grid, dim3(64 * KW), 0, stream, p, tab);
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, SPLIT_, DV_ ? 2 : 1>), skv_grid, dim3(64 * KW), 0, stream, p, tab);
       else if (single_kv)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV_, SPLIT_, true>), kv_grid, kv_block, 0, stream, p, tab);
       else
@@ -1031,21 +1098,54 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     };
     const std::true_type yes;
     const std::false_type no;
-    if (p.HS > 1) {
-      if ((err = launch_kv(yes, yes)) != hipSuccess) return err;  // dv
-      if ((err = launch_kv(no, yes)) != hipSuccess) return err;   // dk
-    } else {
-      if ((err = launch_kv(yes, no)) != hipSuccess) return err;
-      if ((err = launch_kv(no, no)) != hipSuccess) return err;
+    // dk and dv in one launch when either's work items fit on the GPU at once: each alone would
+    // then last as long as its heaviest item, with CUs emptying behind the light ones.  (Measured:
+    // dk + dv 25% less time on Llama-3-8B, 31% on PaLM MQA; the same on SmolLM MHA, whose items
+    // take two rounds; 11% more on the 32K shard's sixteen rounds, where the two kinds' tiles
+    // then share L2.)  ATTN_BWD_KVLAUNCH=split or =one forces the choice (a diagnostic).
+    bool one_kv = shared_kv && (long long)skv_grid.x <= bwd_kv_capacity<D, 3>(p.HS > 1);
+    if (const char *kvl = std::getenv("ATTN_BWD_KVLAUNCH")) {
+      if (std::strcmp(kvl, "split") == 0) one_kv = false;
+      if (std::strcmp(kvl, "one") == 0) one_kv = shared_kv;
     }
     bool shared_q = p.G >= 2;
     if (const char *dqk = std::getenv("ATTN_BWD_DQ")) {
       if (std::strcmp(dqk, "shared") == 0) shared_q = true;
       if (std::strcmp(dqk, "regs") == 0) shared_q = false;
     }
-    if (shared_q) {
-      const int passes = (p.G + p.W - 1) / p.W;
-      const dim3 sq_grid((unsigned)((long long)p.NB * p.B * p.Hkv * passes));
+    // dq joins that launch when it takes KW heads per workgroup and its items fit at once too
+    // (ATTN_BWD_DQLAUNCH=split or =one forces the choice where it can be made, a diagnostic)
+    const int passes = (p.G + p.W - 1) / p.W;
+    const long long sq_n = (long long)p.NB * p.B * p.Hkv * passes;
+    const bool can_q = one_kv && shared_q && p.W == KW;
+    bool one_q = can_q && sq_n <= bwd_kv_capacity<D, 7>(p.HS > 1) &&
+                 (long long)skv_grid.x <= bwd_kv_capacity<D, 7>(p.HS > 1);
+    if (const char *ql = std::getenv("ATTN_BWD_DQLAUNCH")) {
+      if (std::strcmp(ql, "split") == 0) one_q = false;
+      if (std::strcmp(ql, "one") == 0) one_q = can_q;
+    }
+    if (one_kv) {
+      const dim3 grid2((unsigned)(2LL * skv_grid.x + (one_q ? sq_n : 0)));
+      if (one_q && p.HS > 1)
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, true, 7>), grid2, dim3(64 * KW), 0, stream, p, tab);
+      else if (one_q)
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, false, 7>), grid2, dim3(64 * KW), 0, stream, p, tab);
+      else if (p.HS > 1)
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, true, 3>), grid2, dim3(64 * KW), 0, stream, p, tab);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, false, 3>), grid2, dim3(64 * KW), 0, stream, p, tab);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else if (p.HS > 1) {
+      if ((err = launch_kv(yes, yes)) != hipSuccess) return err;  // dv
+      if ((err = launch_kv(no, yes)) != hipSuccess) return err;   // dk
+    } else {
+      if ((err = launch_kv(yes, no)) != hipSuccess) return err;
+      if ((err = launch_kv(no, no)) != hipSuccess) return err;
+    }
+    if (one_q) {
+      // (dq ran in the launch above)
+    } else if (shared_q) {
+      const dim3 sq_grid((unsigned)sq_n);
       switch (p.W) {
         case 1: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 1>), sq_grid, dim3(64), 0, stream, p, tab); break;
         case 2: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 2>), sq_grid, dim3(128), 0, stream, p, tab); break;
