@@ -9,29 +9,37 @@
 //   dq' = ds k' / sqrt(D);   dk'_g = sum over the group's heads of ds^T q' / sqrt(D);
 //   dq = R^T dq', dk = R^T dk' (the rotation by minus the position's angles).
 //
-// Five launches, 32-row blocks of queries and keys throughout:
-//   bwd_prep_k  rotated keys in "c" and "t" layouts, values in "c" layout, per key block;
-//   bwd_prep_q  rotated queries (scaled) in "c" and "t" layouts, dout in both, and per row
-//               lse * log2(e) and rowsum(dout * out), per query block;
-//   bwd_dkdv    twice, for dv and for dk: one workgroup per (b, K/V head, pair of key blocks
-//               kb, NB-1-kb), one wave per query head of the group (up to 4, each looping over
-//               the rest): for every query block that sees the key block, S = Q K^T (and
-//               dP = dO V^T) on MFMA with one key per lane, then dv += P^T dO or
-//               dk += dS^T Q; the waves' sums are added through LDS, dk is rotated back, and
-//               each row is written once (no atomics);
-//   bwd_dq      one wave per (b, query head, pair of query blocks): S^T = K Q^T and
-//               dP^T = V dO^T with one query per lane, dq += dS K; rotated back and written.
+// 32-row blocks of queries and keys throughout.  Kernels (head_dim 64 and 128 here; the
+// head_dim 256 ones, which keep their fixed block in LDS, are in attn_bwd_d256.hip):
+//   bwd_prep            the layout passes, one launch: per query block rotated queries (scaled)
+//                       in "c" and "t" layouts, dout in both, and per row lse * log2(e) and
+//                       rowsum(dout * out); per key block rotated keys in "c" and "t" layouts
+//                       and values in "c" layout;
+//   dk, dv              bwd_dkdv_shared_item: a workgroup of four waves takes four consecutive
+//                       key blocks of one K/V head (one each) and the query heads of its head
+//                       split; each query block's tiles are copied once into LDS, where every
+//                       wave reads its operands: S = Q K^T (and dP = dO V^T) with one key per
+//                       lane, then dv += P^T dO or dk += dS^T Q, summed over the heads in
+//                       registers; dk is rotated back and each row written once (no atomics),
+//                       or, with head splits, left as fp32 partials for bwd_part_reduce;
+//   dq                  bwd_dq_shared_item for GQA/MQA (a workgroup of up to four query heads
+//                       of a K/V group on one query block, each key block's tiles copied once
+//                       into LDS) or bwd_dq for MHA (one wave per query head and query block or
+//                       pair, operands from L2): S^T = K Q^T and dP^T = V dO^T with one query
+//                       per lane, dq += dS K, rotated back and written;
+//   bwd_dkdv_shared_kernel  runs the dk, dv and (four heads per workgroup) dq work items in one
+//                       launch, heaviest first, when they fit on the GPU at once, else dk and dv
+//                       items in launches of their own;
+//   bwd_part_reduce     adds the head splits' partials in split order.
 // A call may be one block of a longer sequence (one step of ring attention's backward): queries
 // at positions q_pos0 + i, keys at k_pos0 + j, key j visible to query i iff j <= i + delta with
 // delta = q_pos0 - k_pos0; out and lse are then the forward's results over every key block, and
 // dq (dk, dv) is this key block's (query block's) part of the gradient.  Block kb of keys is seen
 // by query blocks from qb_lo(kb) on, query block qb sees key blocks below kb_end(qb), and a
-// block pair needs the element mask only where some key is later than some row.
-// Causal work is balanced by pairing block kb with NB-1-kb.  Operands are read straight from
-// the pre-laid-out tiles into registers (16-byte loads, each a whole MFMA operand per lane), so
-// no LDS is needed outside the dk/dv reduction and the layout passes; each register is reloaded
-// with the next block's operand as soon as its instruction has read it.  (The head_dim 256
-// kernels, which keep their fixed block in LDS instead, are in attn_bwd_d256.hip.)
+// block needs the element mask only where some key is later than some row.  Every MFMA operand
+// is one 16-byte read per lane from the pre-laid-out tiles, in LDS or (per-wave kernels) in
+// registers, each register reloaded with the next block's operand as soon as its instruction
+// has read it.
 //
 // MFMA v_mfma_f32_32x32x16_bf16: A lane l holds row l%32, k = 8(l/32) .. +7; B lane l holds
 // column l%32, same k; the result's register v in lane l is row 8(v/4) + 4(l/32) + v%4,
@@ -51,17 +59,17 @@ namespace attn {
 // Layout passes.  256 threads; item = row * NCH + c covers dims 8c .. 8c+7 and D/2 + 8c .. of
 // one row (NCH = D/16 pairs of 8-dim chunks).
 
+// key block blk of (b, K/V head) blk / NB, staged through sk (32 rows of D + 8)
 template <int D>
-__global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable tab) {
+__device__ __forceinline__ void bwd_prep_k_item(const BwdParams &p, const RopeTable &tab, int blk, uint16_t *sk) {
   constexpr int NCH = D / 16;
   constexpr int LS = D + 8;
   constexpr int T = BR * D;  // elements per tile
-  __shared__ __attribute__((aligned(16))) uint16_t sk[BR * LS];
   const int tid = threadIdx.x;
-  const int kb = blockIdx.x % p.NB;
-  const int unit = blockIdx.x / p.NB;  // b * Hkv + g
+  const int kb = blk % p.NB;
+  const int unit = blk / p.NB;  // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
-  const size_t tile = (size_t)blockIdx.x * T;
+  const size_t tile = (size_t)blk * T;
   for (int item = tid; item < BR * NCH; item += 256) {  // one pass, two at head_dim 256
     const int row = item / NCH, c = item % NCH;
     const int r = kb * BR + row;
@@ -94,18 +102,18 @@ __global__ void __launch_bounds__(256) bwd_prep_k_kernel(BwdParams p, RopeTable 
   write_t_layout<D, LS>(sk, p.kt + tile, tid, 256);
 }
 
+// query block blk of (b, query head) blk / NB, staged through sq and sd
 template <int D>
-__global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable tab) {
+__device__ __forceinline__ void bwd_prep_q_item(const BwdParams &p, const RopeTable &tab, int blk, uint16_t *sq,
+                                                uint16_t *sd) {
   constexpr int NCH = D / 16;
   constexpr int LS = D + 8;
   constexpr int T = BR * D;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[BR * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t sd[BR * LS];
   const int tid = threadIdx.x;
-  const int qb = blockIdx.x % p.NB;
-  const int unit = blockIdx.x / p.NB;  // b * Hq + h
+  const int qb = blk % p.NB;
+  const int unit = blk / p.NB;  // b * Hq + h
   const int h = unit % p.Hq, b = unit / p.Hq;
-  const size_t tile = (size_t)blockIdx.x * T;
+  const size_t tile = (size_t)blk * T;
   // one pass, two at head_dim 256 (the NCH items of a row are consecutive lanes of one wave in
   // either pass, for the row sums below)
   for (int item = tid; item < BR * NCH; item += 256) {
@@ -160,6 +168,20 @@ __global__ void __launch_bounds__(256) bwd_prep_q_kernel(BwdParams p, RopeTable 
   __syncthreads();
   write_t_layout<D, LS>(sq, p.qt + tile, tid, 256);
   write_t_layout<D, LS>(sd, p.dt + tile, tid, 256);
+}
+
+// Both layout passes in one launch: the B * Hq * NB query blocks (four tiles each), then the
+// B * Hkv * NB key blocks.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, RopeTable tab) {
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t st[2 * BR * LS];
+  const int qblocks = p.B * p.Hq * p.NB;
+  const int blk = (int)blockIdx.x;
+  if (blk < qblocks)
+    bwd_prep_q_item<D>(p, tab, blk, st, st + BR * LS);
+  else
+    bwd_prep_k_item<D>(p, tab, blk - qblocks, st);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1051,11 +1073,9 @@ template <int D>
 hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
   const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
   const unsigned qblocks = (unsigned)((long long)p.B * p.Hq * p.NB);
-  hipLaunchKernelGGL(bwd_prep_k_kernel<D>, dim3(kblocks), dim3(256), 0, stream, p, tab);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(kblocks + qblocks), dim3(256), 0, stream, p, tab);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_prep_q_kernel<D>, dim3(qblocks), dim3(256), 0, stream, p, tab);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   if constexpr (D == 256) {
     if ((err = launch_bwd_d256_main(p, tab, stream)) != hipSuccess) return err;
   } else {
