@@ -182,12 +182,13 @@ def test_bwd_kv_kernels_agree(shape, monkeypatch):
 
 
 @pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 257, 8, 1, 128, True), (2, 96, 16, 2, 64, True),
-                                   (1, 200, 6, 2, 128, False)],
+                                   (1, 200, 6, 2, 128, False), (1, 200, 4, 4, 64, True), (2, 170, 4, 2, 128, False),
+                                   (1, 150, 2, 2, 128, True), (1, 33, 2, 2, 64, True)],
                          ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
 def test_bwd_dq_kernels_agree(shape, monkeypatch):
-    """The dq kernel that shares each key block's tiles between a group's heads through LDS and
-    the one that loads them per wave take the same operands in the same order: the same bits
-    (ATTN_BWD_DQ picks the kernel)."""
+    """The dq kernel that shares each key block's tiles through LDS (between a group's heads, or
+    between consecutive query blocks of one head) and the one that loads them per wave take the
+    same operands in the same order: the same bits (ATTN_BWD_DQ picks the kernel)."""
     B, S, Hq, Hkv, d, causal = shape
     w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq + 5)
     q, k, v = make_inputs(w)

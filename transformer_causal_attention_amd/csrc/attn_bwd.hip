@@ -56,8 +56,15 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------------------------
-// Layout passes.  256 threads; item = row * NCH + c covers dims 8c .. 8c+7 and D/2 + 8c .. of
-// one row (NCH = D/16 pairs of 8-dim chunks).
+// threads of a layout-pass workgroup: one per item (32 rows x D/16 chunk pairs), at most 256
+template <int D>
+constexpr int bwd_prep_threads() {
+  return BR * (D / 16) < 256 ? BR * (D / 16) : 256;
+}
+
+// Layout passes.  bwd_prep_threads<D>() threads, one per item (two items each at head_dim 256);
+// item = row * NCH + c covers dims 8c .. 8c+7 and D/2 + 8c .. of one row (NCH = D/16 pairs of
+// 8-dim chunks).
 
 // key block blk of (b, K/V head) blk / NB, staged through sk (32 rows of D + 8)
 template <int D>
@@ -70,7 +77,7 @@ __device__ __forceinline__ void bwd_prep_k_item(const BwdParams &p, const RopeTa
   const int unit = blk / p.NB;  // b * Hkv + g
   const int g = unit % p.Hkv, b = unit / p.Hkv;
   const size_t tile = (size_t)blk * T;
-  for (int item = tid; item < BR * NCH; item += 256) {  // one pass, two at head_dim 256
+  for (int item = tid; item < BR * NCH; item += bwd_prep_threads<D>()) {  // one pass, two at head_dim 256
     const int row = item / NCH, c = item % NCH;
     const int r = kb * BR + row;
     u32x4 kx = {0u, 0u, 0u, 0u}, ky = kx, vx = kx, vy = kx;
@@ -99,7 +106,7 @@ __device__ __forceinline__ void bwd_prep_k_item(const BwdParams &p, const RopeTa
     *reinterpret_cast<u32x4 *>(sk + row * LS + D / 2 + 8 * c) = wy;
   }
   __syncthreads();
-  write_t_layout<D, LS>(sk, p.kt + tile, tid, 256);
+  write_t_layout<D, LS>(sk, p.kt + tile, tid, bwd_prep_threads<D>());
 }
 
 // query block blk of (b, query head) blk / NB, staged through sq and sd
@@ -116,7 +123,7 @@ __device__ __forceinline__ void bwd_prep_q_item(const BwdParams &p, const RopeTa
   const size_t tile = (size_t)blk * T;
   // one pass, two at head_dim 256 (the NCH items of a row are consecutive lanes of one wave in
   // either pass, for the row sums below)
-  for (int item = tid; item < BR * NCH; item += 256) {
+  for (int item = tid; item < BR * NCH; item += bwd_prep_threads<D>()) {
     const int row = item / NCH, c = item % NCH;
     const int r = qb * BR + row;
     const bool ok = r < p.S;
@@ -166,14 +173,14 @@ __device__ __forceinline__ void bwd_prep_q_item(const BwdParams &p, const RopeTa
     }
   }
   __syncthreads();
-  write_t_layout<D, LS>(sq, p.qt + tile, tid, 256);
-  write_t_layout<D, LS>(sd, p.dt + tile, tid, 256);
+  write_t_layout<D, LS>(sq, p.qt + tile, tid, bwd_prep_threads<D>());
+  write_t_layout<D, LS>(sd, p.dt + tile, tid, bwd_prep_threads<D>());
 }
 
 // Both layout passes in one launch: the B * Hq * NB query blocks (four tiles each), then the
 // B * Hkv * NB key blocks.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, RopeTable tab) {
+__global__ void __launch_bounds__(bwd_prep_threads<D>()) bwd_prep_kernel(BwdParams p, RopeTable tab) {
   constexpr int LS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t st[2 * BR * LS];
   const int qblocks = p.B * p.Hq * p.NB;
@@ -586,8 +593,16 @@ constexpr int bwd_dq_buf_bytes() {
   return 3 * BR * D * 2;
 }
 
-// work item blk (query block NB - 1 - blk / per_qb: the heaviest first) with the two key-block
-// buffers kbuf0, kbuf1
+// Query blocks per workgroup of the shared dq kernel with W heads: four waves in all where W
+// divides four (one head: four consecutive query blocks), else one block.
+template <int W>
+constexpr int bwd_dq_qw() {
+  return W == 1 ? 4 : W == 2 ? 2 : 1;
+}
+
+// work item blk: W heads times QW consecutive query blocks, the top one NB - 1 - QW (blk /
+// per_qg) (the heaviest first); wave w serves head w % W of its pass and query block
+// top - w / W; the two key-block buffers kbuf0, kbuf1
 template <int D, int W>
 __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const RopeTable &tab, int blk, char *kbuf0,
                                                    char *kbuf1) {
@@ -596,19 +611,24 @@ __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const Rop
   constexpr int T = BR * D;
   constexpr int TB = T * 2;               // bytes of one tile
   constexpr int NPART = TB / 1024;        // 1 KiB copy instructions per tile
+  constexpr int QW = bwd_dq_qw<W>();
+  constexpr int NW = W * QW;              // waves
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const int passes = (p.G + W - 1) / W;
-  const int per_qb = p.B * p.Hkv * passes;
-  const int qb = p.NB - 1 - blk / per_qb;
-  const int item = xcd_order(blk % per_qb, per_qb);
+  const int per_qg = p.B * p.Hkv * passes;
+  const int qb_top = p.NB - 1 - QW * (blk / per_qg);
+  const int qb_raw = qb_top - wave / W;
+  const bool has_qb = qb_raw >= 0;
+  const int qb = has_qb ? qb_raw : 0;  // (a wave past the first block computes on block 0 and writes nothing)
+  const int item = xcd_order(blk % per_qg, per_qg);
   const int pass = item % passes;
   const int kunit = item / passes;  // b * Hkv + g
   const int g = kunit % p.Hkv, b = kunit / p.Hkv;
-  const int hc = pass * W + wave;   // head of the group this wave serves (none past G)
-  const bool has_head = hc < p.G;
-  const int h = g * p.G + (has_head ? hc : 0);
+  const int hc = pass * W + wave % W;  // head of the group this wave serves (none past G)
+  const bool has_head = hc < p.G && has_qb;
+  const int h = g * p.G + (hc < p.G ? hc : 0);
   const size_t qunit = (size_t)b * p.Hq + h;
   const int c_off = hh * BR * 8 + l32 * 8;
   const int delta = p.q_pos0 - p.k_pos0;
@@ -626,8 +646,12 @@ __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const Rop
   f32x16 dq[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
-  // key blocks with a key some row of this block sees: 32 kb <= 32 qb + 31 + delta
-  const int kb_end = p.causal ? min(p.NB, max(0, floor_div(BR * qb + BR - 1 + delta, BR) + 1)) : p.NB;
+  // key blocks with a key some row of block q sees: 32 kb <= 32 q + 31 + delta
+  auto kb_end_of = [&](int q) __attribute__((always_inline)) {
+    return p.causal ? min(p.NB, max(0, floor_div(BR * q + BR - 1 + delta, BR) + 1)) : p.NB;
+  };
+  const int kb_end = has_qb ? kb_end_of(qb) : 0;  // this wave's
+  const int wg_kb_end = kb_end_of(qb_top);        // the workgroup's (its top block sees the most)
 
   // this K/V head's run of key blocks as buffers (NB * T * 2 < 2^31 bytes)
   const uint32_t run_t = (uint32_t)p.NB * TB;
@@ -641,15 +665,16 @@ __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const Rop
     for (int t = 0; t < 3; ++t) {
       const __amdgpu_buffer_rsrc_t r = t == 0 ? kcb : t == 1 ? vcb : ktb;
 #pragma unroll
-      for (int i = 0; i < (NPART + W - 1) / W; ++i) {
-        const int part = wave + W * i;
-        if (NPART % W == 0 || part < NPART)
+      for (int i = 0; i < (NPART + NW - 1) / NW; ++i) {
+        const int part = wave + NW * i;
+        if (NPART % NW == 0 || part < NPART)
           bwd_lds_dma16(r, 16u * lane, (uint32_t)kb * TB + part * 1024, dst + t * TB + part * 1024);
       }
     }
   };
   const int v_c = 2 * c_off, v_t = 16 * (hh * D + l32);
   auto step = [&](int kb, const char *src) __attribute__((always_inline)) {
+    if (kb >= kb_end) return;  // no key of block kb is seen by this wave's block
     f32x16 st = f32x16{}, dpt = f32x16{};
     // the score products' operands are read from LDS first, all of them, then used
     bf16x8 ka[NKK], va[NKK], kt[2][NCB];
@@ -709,16 +734,16 @@ __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const Rop
   // Block kb sits in buffer kb % 2.  Before block kb: its copy is in (issued a block earlier)
   // and every wave has finished block kb - 1; then the copy of block kb + 1 goes into the
   // buffer block kb - 1 used.
-  if (kb_end > 0) copy_block(0, kbuf0);
-  for (int kb = 0; kb < kb_end; kb += 2) {
+  if (wg_kb_end > 0) copy_block(0, kbuf0);
+  for (int kb = 0; kb < wg_kb_end; kb += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kb + 1 < kb_end) copy_block(kb + 1, kbuf1);
+    if (kb + 1 < wg_kb_end) copy_block(kb + 1, kbuf1);
     step(kb, kbuf0);
-    if (kb + 1 < kb_end) {
+    if (kb + 1 < wg_kb_end) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kb + 2 < kb_end) copy_block(kb + 2, kbuf0);
+      if (kb + 2 < wg_kb_end) copy_block(kb + 2, kbuf0);
       step(kb + 1, kbuf1);
     }
   }
@@ -749,7 +774,7 @@ __device__ __forceinline__ void bwd_dq_shared_item(const BwdParams &p, const Rop
 }
 
 template <int D, int W>
-__global__ void __launch_bounds__(64 * W) bwd_dq_shared_kernel(BwdParams p, RopeTable tab) {
+__global__ void __launch_bounds__(64 * W * bwd_dq_qw<W>()) bwd_dq_shared_kernel(BwdParams p, RopeTable tab) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * bwd_dq_buf_bytes<D>()];
   bwd_dq_shared_item<D, W>(p, tab, (int)blockIdx.x, lds, lds + bwd_dq_buf_bytes<D>());
 }
@@ -1073,7 +1098,7 @@ template <int D>
 hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stream) {
   const unsigned kblocks = (unsigned)((long long)p.B * p.Hkv * p.NB);
   const unsigned qblocks = (unsigned)((long long)p.B * p.Hq * p.NB);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(kblocks + qblocks), dim3(256), 0, stream, p, tab);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(kblocks + qblocks), dim3(bwd_prep_threads<D>()), 0, stream, p, tab);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (D == 256) {
@@ -1128,7 +1153,7 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
       if (std::strcmp(kvl, "split") == 0) one_kv = false;
       if (std::strcmp(kvl, "one") == 0) one_kv = shared_kv;
     }
-    bool shared_q = p.G >= 2;
+    bool shared_q = true;
     if (const char *dqk = std::getenv("ATTN_BWD_DQ")) {
       if (std::strcmp(dqk, "shared") == 0) shared_q = true;
       if (std::strcmp(dqk, "regs") == 0) shared_q = false;
@@ -1136,7 +1161,8 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     // dq joins that launch when it takes KW heads per workgroup and its items fit at once too
     // (ATTN_BWD_DQLAUNCH=split or =one forces the choice where it can be made, a diagnostic)
     const int passes = (p.G + p.W - 1) / p.W;
-    const long long sq_n = (long long)p.NB * p.B * p.Hkv * passes;
+    const int qw = p.W == 1 ? bwd_dq_qw<1>() : p.W == 2 ? bwd_dq_qw<2>() : 1;  // query blocks per item
+    const long long sq_n = (long long)((p.NB + qw - 1) / qw) * p.B * p.Hkv * passes;
     const bool can_q = one_kv && shared_q && p.W == KW;
     bool one_q = can_q && sq_n <= bwd_kv_capacity<D, 7>(p.HS > 1) &&
                  (long long)skv_grid.x <= bwd_kv_capacity<D, 7>(p.HS > 1);
@@ -1167,8 +1193,8 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     } else if (shared_q) {
       const dim3 sq_grid((unsigned)sq_n);
       switch (p.W) {
-        case 1: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 1>), sq_grid, dim3(64), 0, stream, p, tab); break;
-        case 2: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 2>), sq_grid, dim3(128), 0, stream, p, tab); break;
+        case 1: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 1>), sq_grid, dim3(256), 0, stream, p, tab); break;
+        case 2: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 2>), sq_grid, dim3(256), 0, stream, p, tab); break;
         case 3: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 3>), sq_grid, dim3(192), 0, stream, p, tab); break;
         default: hipLaunchKernelGGL((bwd_dq_shared_kernel<D, 4>), sq_grid, dim3(256), 0, stream, p, tab); break;
       }
