@@ -22,15 +22,17 @@
 //                       lane, then dv += P^T dO or dk += dS^T Q, summed over the heads in
 //                       registers; dk is rotated back and each row written once (no atomics),
 //                       or, with head splits, left as fp32 partials for bwd_part_reduce;
-//   dq                  bwd_dq_shared_item for GQA/MQA (a workgroup of up to four query heads
-//                       of a K/V group on one query block, each key block's tiles copied once
-//                       into LDS) or bwd_dq for MHA (one wave per query head and query block or
-//                       pair, operands from L2): S^T = K Q^T and dP^T = V dO^T with one query
+//   dq                  bwd_dq_shared_item (a workgroup of four waves: up to four query heads
+//                       of a K/V group times consecutive query blocks, each key block's tiles
+//                       copied once into LDS): S^T = K Q^T and dP^T = V dO^T with one query
 //                       per lane, dq += dS K, rotated back and written;
 //   bwd_dkdv_shared_kernel  runs the dk, dv and (four heads per workgroup) dq work items in one
 //                       launch, heaviest first, when they fit on the GPU at once, else dk and dv
 //                       items in launches of their own;
-//   bwd_part_reduce     adds the head splits' partials in split order.
+//   bwd_part_reduce     adds the head splits' partials in split order;
+//   bwd_dkdv, bwd_dq    per-wave kernels with operands from L2 (one wave per query head and
+//                       block or block pair), kept as diagnostics (ATTN_BWD_KV, ATTN_BWD_DQ) and
+//                       checked against the shared ones.
 // A call may be one block of a longer sequence (one step of ring attention's backward): queries
 // at positions q_pos0 + i, keys at k_pos0 + j, key j visible to query i iff j <= i + delta with
 // delta = q_pos0 - k_pos0; out and lse are then the forward's results over every key block, and
@@ -192,8 +194,9 @@ __global__ void __launch_bounds__(bwd_prep_threads<D>()) bwd_prep_kernel(BwdPara
 }
 
 // ---------------------------------------------------------------------------------------------
-// dv (DV) or dk (!DV).  Workgroup: (b, g, key-block pair), W waves; wave w takes the group's
-// heads w, w+W, ...  The two gradients are separate kernels so that each holds one set of
+// Per-wave dv (DV) or dk (!DV), the diagnostic alternative to bwd_dkdv_shared_item.
+// Workgroup: (b, g, key-block pair), W waves; wave w takes the group's heads w, w+W, ...  The
+// two gradients are separate kernels so that each holds one set of
 // accumulators and has the registers to load the next query block's operands while it uses the
 // current ones; the dv kernel needs neither dP nor dout in "c" layout.
 
@@ -418,7 +421,8 @@ __global__ void __launch_bounds__(256, DV ? 2 : 1) bwd_dkdv_kernel(BwdParams p, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dq.  One wave per (b, h, query-block pair).
+// Per-wave dq, the diagnostic alternative to bwd_dq_shared_item (ATTN_BWD_DQ=regs).  One wave
+// per (b, h, query-block pair), or per query block with SINGLE.
 
 template <int D, bool SINGLE>
 __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p, RopeTable tab) {
@@ -573,14 +577,15 @@ __global__ void __launch_bounds__(64, D == 64 ? 2 : 1) bwd_dq_kernel(BwdParams p
 }
 
 // ---------------------------------------------------------------------------------------------
-// dq with the key blocks shared by the query heads of a K/V group.  Workgroup: W waves, wave w
-// one query head of the group (pass * W + w), all on the same query block; one query block per
-// workgroup, the heaviest first, renumbered within each block rank so that one XCD runs one K/V
-// group.  Each key block's three tiles (rotated keys in "c" and "t" layouts, values in "c"
-// layout, 3 * 32 * D bf16) are copied once per workgroup from L2 into LDS (16-byte loads
-// straight into LDS, the W waves taking turns) and every wave reads its MFMA operands there,
-// so the path from L2 into the CU carries each tile once per workgroup instead of once per
-// wave.  Double-buffered: the copy of block kb+1 runs during block kb; one barrier per block.
+// dq with the key blocks shared by the waves of a workgroup: W = min(G, 4) query heads of a K/V
+// group (pass * W + w % W) times 4 / W consecutive query blocks of them (W = 3: three waves on
+// one block).  Work items: groups of query blocks, the heaviest first, renumbered within each
+// rank so that one XCD runs one K/V group.  Each key block's three tiles (rotated keys in "c"
+// and "t" layouts, values in "c" layout, 3 * 32 * D bf16) are copied once per workgroup from
+// L2 into LDS (16-byte loads straight into LDS, the waves taking turns) and every wave reads
+// its MFMA operands there, so the path from L2 into the CU carries each tile once per
+// workgroup instead of once per wave; a wave skips the key blocks its query block does not
+// see.  Double-buffered: the copy of block kb+1 runs during block kb; one barrier per block.
 // Same arithmetic, operand layouts, visibility and masks as bwd_dq_kernel.
 
 __device__ __forceinline__ void bwd_lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, char *lds_base) {
