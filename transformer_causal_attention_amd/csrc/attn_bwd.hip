@@ -1109,8 +1109,8 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
   if constexpr (D == 256) {
     if ((err = launch_bwd_d256_main(p, tab, stream)) != hipSuccess) return err;
   } else {
-    // Work items of single blocks, heaviest first, instead of balanced pairs: for dq when the
-    // pairs would leave SIMDs idle, when the key range is long (the waves of one round then sweep
+    // The per-wave kernels (diagnostics) take work items of single blocks, heaviest first,
+    // instead of balanced pairs: for dq when the pairs would leave SIMDs idle, when the key range is long (the waves of one round then sweep
     // nearby key blocks and share them in L2) or when every K/V head serves one query head; for
     // the per-head dk/dv kernel (ATTN_BWD_KV=waves) in that last case only.  (Measured on the
     // workloads: single dq blocks 17% faster on PaLM MQA, 13% on SmolLM MHA, 31% on the 32K
