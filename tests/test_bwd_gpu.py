@@ -157,6 +157,25 @@ def test_bwd_one_launch_agrees(shape, monkeypatch):
             assert torch.equal(a, b), f"{w}: {name} differs between launches ({kind})"
 
 
+@pytest.mark.parametrize("shape", [(1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False), (2, 96, 16, 2, 64, True),
+                                   (3, 1, 4, 2, 64, True), (1, 64, 4, 1, 64, True), (1, 520, 8, 1, 64, True)],
+                         ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_kv_fused_agrees(shape, monkeypatch):
+    """At head_dim 64 one pass gives dk and dv together from the same probabilities and dS, summed
+    in the same order as the two separate passes (ATTN_BWD_KVFUSE=off): the same bits."""
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S + Hq + 6)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    res = {}
+    for kind in ("off", "on"):
+        monkeypatch.setenv("ATTN_BWD_KVFUSE", kind)
+        res[kind] = run_case(w, q, k, v, do)
+    for name, a, b in zip(("dq", "dk", "dv"), res["off"], res["on"]):
+        assert torch.equal(a, b), f"{w}: {name} differs between one pass and two"
+
+
 @pytest.mark.parametrize("shape", [(2, 300, 8, 2, 128, True), (1, 200, 4, 4, 64, True), (2, 170, 16, 2, 64, False),
                                    (1, 150, 2, 2, 128, True)],
                          ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))

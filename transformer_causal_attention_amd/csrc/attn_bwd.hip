@@ -19,9 +19,10 @@
 //                       key blocks of one K/V head (one each) and the query heads of its head
 //                       split; each query block's tiles are copied once into LDS, where every
 //                       wave reads its operands: S = Q K^T (and dP = dO V^T) with one key per
-//                       lane, then dv += P^T dO or dk += dS^T Q, summed over the heads in
-//                       registers; dk is rotated back and each row written once (no atomics),
-//                       or, with head splits, left as fp32 partials for bwd_part_reduce;
+//                       lane, then dv += P^T dO or dk += dS^T Q (both in one pass at head_dim
+//                       64), summed over the heads in registers; dk is rotated back and each row
+//                       written once (no atomics), or, with head splits, left as fp32 partials
+//                       for bwd_part_reduce;
 //   dq                  bwd_dq_shared_item (a workgroup of four waves: up to four query heads
 //                       of a K/V group times consecutive query blocks, each key block's tiles
 //                       copied once into LDS): S^T = K Q^T and dP^T = V dO^T with one query
@@ -800,24 +801,36 @@ __global__ void __launch_bounds__(64 * W * bwd_dq_qw<W>()) bwd_dq_shared_kernel(
 
 constexpr int KW = 4;  // key blocks (waves) per workgroup
 
-// LDS of one query-block buffer: NT tiles, then 1 KiB for the block's lse rows and 1 KiB for
+// Gradients one work item computes: dk, dv, or both from one pass (the probabilities and dS of
+// a step computed once for the two products; head_dim 64, where both accumulator sets fit).
+enum BwdKvKind { kKvDk = 0, kKvDv = 1, kKvBoth = 2 };
+
+// tiles per query block, in LDS order: [qc | dc | qt] (dk), [qc | dt] (dv), [qc | dc | qt | dt]
+template <int KIND>
+constexpr int bwd_kv_tiles() {
+  return KIND == kKvDk ? 3 : KIND == kKvDv ? 2 : 4;
+}
+
+// LDS of one query-block buffer: the tiles, then 1 KiB for the block's lse rows and 1 KiB for
 // its rowsums
-template <int D, bool DV>
+template <int D, int KIND>
 constexpr int bwd_kv_buf_bytes() {
-  return (DV ? 2 : 3) * BR * D * 2 + 2048;
+  return bwd_kv_tiles<KIND>() * BR * D * 2 + 2048;
 }
 
 // work item blk (key group blk / per_kg, the heaviest first) with the two buffers qbuf0, qbuf1
-template <int D, bool DV, bool SPLIT>
+template <int D, int KIND, bool SPLIT>
 __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const RopeTable &tab, int blk, char *qbuf0,
                                                      char *qbuf1) {
+  constexpr bool DO_K = KIND != kKvDv, DO_V = KIND != kKvDk;
   constexpr int NKK = D / 16;
   constexpr int NCB = D / 32;
   constexpr int T = BR * D;
   constexpr int TB = T * 2;             // bytes of one tile
   constexpr int NPART = TB / 1024;      // 1 KiB copy instructions per tile
-  constexpr int NT = DV ? 2 : 3;        // tiles per query block: [qc | dt] or [qc | dc | qt]
+  constexpr int NT = bwd_kv_tiles<KIND>();
   constexpr int RB = NT * TB;           // then the lse and rowsum rows
+  constexpr int T_Q = 2, T_D = KIND == kKvDv ? 1 : 3;  // tiles of the "t" operands: qt, dt
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
@@ -834,11 +847,11 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
   const int c_off = hh * BR * 8 + l32 * 8;
   const int delta = p.q_pos0 - p.k_pos0;
   const size_t ktile = ((size_t)unit * p.NB + kbc) * T;
-  bf16x8 kf[NKK], vf[DV ? 1 : NKK];
+  bf16x8 kf[NKK], vf[DO_K ? NKK : 1];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     kf[kk] = ld16(p.kc + ktile + c_off + kk * 2 * BR * 8);
-    if (!DV) vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
+    if constexpr (DO_K) vf[kk] = ld16(p.vc + ktile + c_off + kk * 2 * BR * 8);
   }
   const bool key_ok = kbc * BR + l32 < p.S;
   const bool key_ok_all = (kbc + 1) * BR <= p.S;
@@ -848,9 +861,12 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
   };
   const int my_qb_lo = qb_lo_of(kbc);
   const int wg_qb_lo = qb_lo_of(kg * KW);  // the workgroup's first key block sees the most
-  f32x16 acc[NCB];
+  f32x16 acc_k[DO_K ? NCB : 1], acc_v[DO_V ? NCB : 1];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+  for (int cb = 0; cb < NCB; ++cb) {
+    if constexpr (DO_K) acc_k[cb] = f32x16{};
+    if constexpr (DO_V) acc_v[cb] = f32x16{};
+  }
   const int v_c = 2 * c_off, v_t = 16 * (hh * D + l32), v_r = 16 * hh;
   const uint32_t run_t = (uint32_t)p.NB * TB, run_r = (uint32_t)p.NB * BR * 4;
 
@@ -858,7 +874,8 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
     const size_t qunit = (size_t)b * p.Hq + g * p.G + hc;
     const __amdgpu_buffer_rsrc_t qcb = raw_buffer(p.qc + qunit * p.NB * T, run_t);
     const __amdgpu_buffer_rsrc_t dcb = raw_buffer(p.dc + qunit * p.NB * T, run_t);
-    const __amdgpu_buffer_rsrc_t tb_ = raw_buffer((DV ? p.dt : p.qt) + qunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t qtb = raw_buffer(p.qt + qunit * p.NB * T, run_t);
+    const __amdgpu_buffer_rsrc_t dtb = raw_buffer(p.dt + qunit * p.NB * T, run_t);
     const __amdgpu_buffer_rsrc_t lbuf = raw_buffer(p.l2 + qunit * p.NB * BR, run_r);
     const __amdgpu_buffer_rsrc_t ddbuf = raw_buffer(p.dd + qunit * p.NB * BR, run_r);
     // this wave's share of the copies of query block qb into dst: KiB wave, wave + KW, ... of
@@ -866,7 +883,7 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
     auto copy_block = [&](int qb, char *dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const __amdgpu_buffer_rsrc_t r = t == 0 ? qcb : (DV || t == 2) ? tb_ : dcb;
+        const __amdgpu_buffer_rsrc_t r = t == 0 ? qcb : t == T_D ? dtb : t == T_Q ? qtb : dcb;
 #pragma unroll
         for (int i = 0; i < (NPART + KW - 1) / KW; ++i) {
           const int part = wave + KW * i;
@@ -878,61 +895,66 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
       // offsets lie past the buffer's end, so they read nothing
       const uint32_t roff = lane < 8 ? (uint32_t)qb * BR * 4 + 16u * lane : 0x80000000u;
       if (wave == KW - 1) bwd_lds_dma16(lbuf, roff, 0, dst + RB);
-      if (!DV && wave == KW - 2) bwd_lds_dma16(ddbuf, roff, 0, dst + RB + 1024);
+      if (DO_K && wave == KW - 2) bwd_lds_dma16(ddbuf, roff, 0, dst + RB + 1024);
     };
     auto step = [&](int qb, const char *src) __attribute__((always_inline)) {
       if (qb < my_qb_lo) return;  // no key of this wave's block is seen by this query block
-      bf16x8 qa[NKK], da[DV ? 1 : NKK];
+      bf16x8 qa[NKK], da[DO_K ? NKK : 1];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         qa[kk] = *reinterpret_cast<const bf16x8 *>(src + v_c + kk * 2 * BR * 16);
-        if (!DV) da[kk] = *reinterpret_cast<const bf16x8 *>(src + TB + v_c + kk * 2 * BR * 16);
+        if constexpr (DO_K) da[kk] = *reinterpret_cast<const bf16x8 *>(src + TB + v_c + kk * 2 * BR * 16);
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s = bwd_mfma(qa[kk], kf[kk], s);
-        if (!DV) dp = bwd_mfma(da[kk], vf[kk], dp);
+        if constexpr (DO_K) dp = bwd_mfma(da[kk], vf[kk], dp);
       }
       // lse and rowsum of this lane's rows 8c + 4hh + 0..3
-      f32x4 L[4], Dd[DV ? 1 : 4];
+      f32x4 L[4], Dd[DO_K ? 4 : 1];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         L[c] = *reinterpret_cast<const f32x4 *>(src + RB + v_r + 32 * c);
-        if (!DV) Dd[c] = *reinterpret_cast<const f32x4 *>(src + RB + 1024 + v_r + 32 * c);
+        if constexpr (DO_K) Dd[c] = *reinterpret_cast<const f32x4 *>(src + RB + 1024 + v_r + 32 * c);
       }
-      const char *tsrc = src + (NT - 1) * TB;
-      bf16x8 tb[2][NCB];
+      // the "t" operands of the gradient products: queries (dk), dout (dv)
+      bf16x8 tq[DO_K ? 2 : 1][NCB], td[DO_V ? 2 : 1][NCB];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          tb[tt][cb] = *reinterpret_cast<const bf16x8 *>(tsrc + v_t + (tt * 2 * D + 32 * cb) * 16);
+        for (int cb = 0; cb < NCB; ++cb) {
+          if constexpr (DO_K) tq[tt][cb] = *reinterpret_cast<const bf16x8 *>(src + T_Q * TB + v_t + (tt * 2 * D + 32 * cb) * 16);
+          if constexpr (DO_V) td[tt][cb] = *reinterpret_cast<const bf16x8 *>(src + T_D * TB + v_t + (tt * 2 * D + 32 * cb) * 16);
+        }
       // key kb*32 + l32 is later than row qb*32 + r iff l32 - r > rel, i.e. (r = res_row(v, hh))
       // iff 8(v/4) + v%4 < thr: one threshold per lane, applied by selects in the steps that
       // need it (a key past S masks every row, thr 32)
       const int rel = BR * (qb - kbc) + delta;
       const bool masked = !key_ok_all || (p.causal && rel < BR - 1);  // wave-uniform
       const int thr = !key_ok ? 32 : (p.causal && rel < BR - 1) ? l32 - 4 * hh - rel : 0;
-      bf16x8 op[2];
+      bf16x8 op_p[DO_V ? 2 : 1], op_s[DO_K ? 2 : 1];  // P and dS, packed as A operands
       auto probs = [&](bool msk) __attribute__((always_inline)) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          u32x4 wv;
+          u32x4 wp, ws;
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            float x[2];
+            float xp[2], xs[2];
 #pragma unroll
             for (int z = 0; z < 2; ++z) {
               const int v = 8 * tt + e + z;
               float pr = __builtin_amdgcn_exp2f(s[v] - L[v >> 2][v & 3]);
               if (msk) pr = 8 * (v >> 2) + (v & 3) < thr ? 0.f : pr;
-              x[z] = DV ? pr : pr * (dp[v] - Dd[v >> 2][v & 3]);
+              xp[z] = pr;
+              if constexpr (DO_K) xs[z] = pr * (dp[v] - Dd[v >> 2][v & 3]);
             }
-            wv[e / 2] = pack_bf16x2(x[0], x[1]);
+            if constexpr (DO_V) wp[e / 2] = pack_bf16x2(xp[0], xp[1]);
+            if constexpr (DO_K) ws[e / 2] = pack_bf16x2(xs[0], xs[1]);
           }
-          op[tt] = __builtin_bit_cast(bf16x8, wv);
+          if constexpr (DO_V) op_p[tt] = __builtin_bit_cast(bf16x8, wp);
+          if constexpr (DO_K) op_s[tt] = __builtin_bit_cast(bf16x8, ws);
         }
       };
       if (masked)
@@ -943,7 +965,10 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[cb] = bwd_mfma(op[tt], tb[tt][cb], acc[cb]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          if constexpr (DO_V) acc_v[cb] = bwd_mfma(op_p[tt], td[tt][cb], acc_v[cb]);
+          if constexpr (DO_K) acc_k[cb] = bwd_mfma(op_s[tt], tq[tt][cb], acc_k[cb]);
+        }
     };
     // query block qb sits in buffer qb % 2 ... counted from the top: block NB-1-j in buffer j % 2.
     // Before each block: its copy is in and every wave has finished the previous block; then
@@ -964,72 +989,105 @@ __device__ __forceinline__ void bwd_dkdv_shared_item(const BwdParams &p, const R
     }
   }
   if (!has_kb) return;
-  // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block
-  if constexpr (SPLIT) {
-    float *part = p.part + (((size_t)(DV ? n_hs : 0) + hs) * p.B * p.Hkv + unit) * p.NB * BR * D;
+  // result lane = column 32 cb + l32, register v = key 8(v/4) + 4 hh + v%4 of the block; dk is
+  // rotated back, dv written as is (or, with head splits, both left as fp32 partials)
+  auto finish = [&](auto is_v, f32x16 (&acc)[NCB]) __attribute__((always_inline)) {
+    constexpr bool DV = decltype(is_v)::value;
+    if constexpr (SPLIT) {
+      float *part = p.part + (((size_t)(DV ? n_hs : 0) + hs) * p.B * p.Hkv + unit) * p.NB * BR * D;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kb * BR + res_row(v, hh);
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * BR + res_row(v, hh);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) part[(size_t)key * D + 32 * cb + l32] = acc[cb][v];
-    }
-  } else {
-    if (!DV) {
+        for (int cb = 0; cb < NCB; ++cb) part[(size_t)key * D + 32 * cb + l32] = acc[cb][v];
+      }
+    } else {
+      if (!DV) {
 #pragma unroll
-      for (int cb = 0; cb < NCB / 2; ++cb) {
-        const double rev = tab.rev[32 * cb + l32];
+        for (int cb = 0; cb < NCB / 2; ++cb) {
+          const double rev = tab.rev[32 * cb + l32];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb * BR + res_row(v, hh);
-          const float t = turn_fraction(p.k_pos0 + key, rev);
-          const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
-          const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
-          acc[cb][v] = x * cs + y * sn;
-          acc[cb + NCB / 2][v] = y * cs - x * sn;
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb * BR + res_row(v, hh);
+            const float t = turn_fraction(p.k_pos0 + key, rev);
+            const float sn = __builtin_amdgcn_sinf(t), cs = __builtin_amdgcn_cosf(t);
+            const float x = acc[cb][v], y = acc[cb + NCB / 2][v];
+            acc[cb][v] = x * cs + y * sn;
+            acc[cb + NCB / 2][v] = y * cs - x * sn;
+          }
+        }
+      }
+      __bf16 *dst0 = DV ? p.dv : p.dk;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * BR + res_row(v, hh);
+        if (key < p.S) {
+          const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
+          const int il = DV ? 0 : tab.interleaved;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
         }
       }
     }
-    __bf16 *dst0 = DV ? p.dv : p.dk;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kb * BR + res_row(v, hh);
-      if (key < p.S) {
-        const size_t dst = (((size_t)b * p.S + key) * p.Hkv + g) * D;
-        const int il = DV ? 0 : tab.interleaved;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) dst0[dst + rope_src_dim(32 * cb + l32, D / 2, il)] = (__bf16)acc[cb][v];
-      }
-    }
-  }
+  };
+  if constexpr (DO_V) finish(std::true_type{}, acc_v);
+  if constexpr (DO_K) finish(std::false_type{}, acc_k);
 }
 
-// KINDS 1: dk only; 2: dv only; 3: dk and dv in one launch; 7: dk, dv and dq (the shared dq
-// kernel with KW heads per workgroup) in one launch.  In one launch the work items go by
-// level, heaviest first: level j holds the dk and dv items of key group j and (KINDS 7) the dq
-// items of query blocks NB-1-4j down to NB-4-4j, which see as many key blocks as key group j
-// sees query blocks; within a level the dk items (three products per step) come first.  The
+// KINDS, a set of work-item kinds in one launch: 1 dk, 2 dv, 4 dq (the shared dq kernel with KW
+// heads per workgroup), 8 dk and dv together (head_dim 64).  With more than one kind the work
+// items go by level, heaviest first: level j holds the dk and dv items of key group j and the
+// dq items of query blocks NB-1-4j down to NB-4-4j, which see as many key blocks as key group
+// j sees query blocks; within a level the items with more products per step come first.  The
 // light items of every kind then fill the CUs as the heavy ones end.
+template <int D, int KINDS>
+constexpr int bwd_kv_lds_bytes() {
+  int b = 0;
+  if (KINDS & 1) b = bwd_kv_buf_bytes<D, kKvDk>();
+  if ((KINDS & 8) && bwd_kv_buf_bytes<D, kKvBoth>() > b) b = bwd_kv_buf_bytes<D, kKvBoth>();
+  if ((KINDS & 2) && bwd_kv_buf_bytes<D, kKvDv>() > b) b = bwd_kv_buf_bytes<D, kKvDv>();
+  if ((KINDS & 4) && bwd_dq_buf_bytes<D>() > b) b = bwd_dq_buf_bytes<D>();
+  return b;
+}
+
 template <int D, bool SPLIT, int KINDS>
 __global__ void __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 registers
 bwd_dkdv_shared_kernel(BwdParams p, RopeTable tab) {
-  constexpr int BUF = KINDS == 2 ? bwd_kv_buf_bytes<D, true>() : bwd_kv_buf_bytes<D, false>();
-  static_assert(KINDS != 7 || bwd_dq_buf_bytes<D>() <= BUF, "the dq buffers fit in the dk ones");
+  constexpr int BUF = bwd_kv_lds_bytes<D, KINDS>();
   __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
-  const int blk = (int)blockIdx.x;
-  if constexpr (KINDS == 3 || KINDS == 7) {
-    const int per_kg = p.B * p.Hkv * (SPLIT ? p.HS : 1);
-    const int per_q = KINDS == 7 ? p.B * p.Hkv * ((p.G + KW - 1) / KW) : 0;  // dq items per query block
-    const int L = 2 * per_kg + KW * per_q;                                 // items per level
-    const int lvl = blk / L, r = blk % L;
-    if (r < per_kg)
-      bwd_dkdv_shared_item<D, false, SPLIT>(p, tab, lvl * per_kg + r, lds, lds + bwd_kv_buf_bytes<D, false>());
-    else if (r < 2 * per_kg)
-      bwd_dkdv_shared_item<D, true, SPLIT>(p, tab, lvl * per_kg + r - per_kg, lds, lds + bwd_kv_buf_bytes<D, true>());
-    else if constexpr (KINDS == 7)
-      bwd_dq_shared_item<D, KW>(p, tab, lvl * KW * per_q + r - 2 * per_kg, lds, lds + bwd_dq_buf_bytes<D>());
-  } else {
-    bwd_dkdv_shared_item<D, KINDS == 2, SPLIT>(p, tab, blk, lds, lds + BUF);
+  constexpr int NKV = ((KINDS & 1) ? 1 : 0) + ((KINDS & 2) ? 1 : 0) + ((KINDS & 8) ? 1 : 0);
+  if constexpr (NKV == 1 && (KINDS & 4) == 0) {  // one kind: the block is the item
+    constexpr int KIND = (KINDS & 1) ? kKvDk : (KINDS & 2) ? kKvDv : kKvBoth;
+    bwd_dkdv_shared_item<D, KIND, SPLIT>(p, tab, (int)blockIdx.x, lds, lds + BUF);
+    return;
   }
+  const int per_kg = p.B * p.Hkv * (SPLIT ? p.HS : 1);
+  const int per_q = (KINDS & 4) ? p.B * p.Hkv * ((p.G + KW - 1) / KW) : 0;  // dq items per query block
+  const int L = NKV * per_kg + KW * per_q;                                 // items per level
+  const int lvl = (int)blockIdx.x / L;
+  int r = (int)blockIdx.x % L;
+  if constexpr ((KINDS & 1) != 0) {
+    if (r < per_kg) {
+      bwd_dkdv_shared_item<D, kKvDk, SPLIT>(p, tab, lvl * per_kg + r, lds, lds + bwd_kv_buf_bytes<D, kKvDk>());
+      return;
+    }
+    r -= per_kg;
+  }
+  if constexpr ((KINDS & 8) != 0) {
+    if (r < per_kg) {
+      bwd_dkdv_shared_item<D, kKvBoth, SPLIT>(p, tab, lvl * per_kg + r, lds, lds + bwd_kv_buf_bytes<D, kKvBoth>());
+      return;
+    }
+    r -= per_kg;
+  }
+  if constexpr ((KINDS & 2) != 0) {
+    if (r < per_kg) {
+      bwd_dkdv_shared_item<D, kKvDv, SPLIT>(p, tab, lvl * per_kg + r, lds, lds + bwd_kv_buf_bytes<D, kKvDv>());
+      return;
+    }
+    r -= per_kg;
+  }
+  if constexpr ((KINDS & 4) != 0) bwd_dq_shared_item<D, KW>(p, tab, lvl * KW * per_q + r, lds, lds + bwd_dq_buf_bytes<D>());
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1175,7 +1233,34 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
       if (std::strcmp(ql, "split") == 0) one_q = false;
       if (std::strcmp(ql, "one") == 0) one_q = can_q;
     }
-    if (one_kv) {
+    // head_dim 64: dk and dv from one pass over the query blocks (the probabilities and dS of a
+    // step computed once for both products), dq joining that launch when its items fit
+    // (ATTN_BWD_KVFUSE=off keeps dk and dv apart, a diagnostic)
+    bool fuse_kv = shared_kv && D == 64;
+    if (const char *fz = std::getenv("ATTN_BWD_KVFUSE")) fuse_kv = fuse_kv && std::strcmp(fz, "off") != 0;
+    if constexpr (D == 64) {
+      if (fuse_kv) {
+        one_q = shared_q && p.W == KW && sq_n <= bwd_kv_capacity<D, 12>(p.HS > 1) &&
+                (long long)skv_grid.x <= bwd_kv_capacity<D, 12>(p.HS > 1);
+        if (const char *ql = std::getenv("ATTN_BWD_DQLAUNCH")) {
+          if (std::strcmp(ql, "split") == 0) one_q = false;
+          if (std::strcmp(ql, "one") == 0) one_q = shared_q && p.W == KW;
+        }
+        const dim3 grid2((unsigned)(skv_grid.x + (one_q ? sq_n : 0)));
+        if (one_q && p.HS > 1)
+          hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, true, 12>), grid2, dim3(64 * KW), 0, stream, p, tab);
+        else if (one_q)
+          hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, false, 12>), grid2, dim3(64 * KW), 0, stream, p, tab);
+        else if (p.HS > 1)
+          hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, true, 8>), grid2, dim3(64 * KW), 0, stream, p, tab);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, false, 8>), grid2, dim3(64 * KW), 0, stream, p, tab);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+      }
+    }
+    if (fuse_kv) {
+      // (launched above)
+    } else if (one_kv) {
       const dim3 grid2((unsigned)(2LL * skv_grid.x + (one_q ? sq_n : 0)));
       if (one_q && p.HS > 1)
         hipLaunchKernelGGL((bwd_dkdv_shared_kernel<D, true, 7>), grid2, dim3(64 * KW), 0, stream, p, tab);
