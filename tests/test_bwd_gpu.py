@@ -83,6 +83,35 @@ def test_bwd_parity(shape):
     check("dv", dv, rv, str(w))
 
 
+def _random_shapes(n=12, seed=2024):
+    """Seeded irregular shapes: group sizes 1-8 (MHA, GQA, MQA), head_dim 64 or 128, ragged
+    lengths, causal or not; each picks its own launch forms (one launch or several, one pass or
+    two at head_dim 64, head splits or none)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 3, 4]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 330)), hkv * g, hkv, int(rng.choice([64, 128])),
+                    bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: "B{}S{}H{}/{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_bwd_parity_random_shapes(shape):
+    B, S, Hq, Hkv, d, causal = shape
+    w = w_of(B, S, Hq, Hkv, d, causal, seed=S * 7 + Hq + d)
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    dq, dk, dv = run_case(w, q, k, v, do)
+    rq, rk, rv = attention_backward(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(),
+                                    w.rope_theta, causal)
+    check("dq", dq, rq, str(w))
+    check("dk", dk, rk, str(w))
+    check("dv", dv, rv, str(w))
+
+
 def test_bwd_llama3_full_size_one_group():
     """Llama-3-8B shape (B1 S2048 Hq32 Hkv8 d128, rope_theta 5e5) in the benchmark's launch
     configuration; the oracle evaluates K/V group 3 (query heads 12..15), whose gradients do
