@@ -130,6 +130,27 @@ def test_bwd_llama3_full_size_one_group():
     check("dv", dv[:, :, g:g + 1], rv, "llama3 group 3")
 
 
+@pytest.mark.parametrize("name,heads", [("palm_mqa", slice(0, 8)), ("smollm_mha", slice(5, 7))])
+def test_bwd_full_size_one_batch_row(name, heads):
+    """PaLM MQA (B8 S1024 Hq8 Hkv1 d64) and SmolLM MHA (B4 S1024 Hq32 Hkv32 d64) backward in the
+    benchmark's launch configuration; the oracle evaluates batch row 1 (rows are independent),
+    for SmolLM MHA only query heads 5 and 6 with their own K/V heads (heads are independent)."""
+    from transformer_causal_attention_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    do = dout_of(w)
+    say(w)
+    dq, dk, dv = run_case(w, q, k, v, do)
+    bsl = slice(1, 2)
+    kv = heads if w.Hkv == w.Hq else slice(0, w.Hkv)
+    rq, rk, rv = attention_backward(q[bsl, :, heads].double().numpy(), k[bsl, :, kv].double().numpy(),
+                                    v[bsl, :, kv].double().numpy(), do[bsl, :, heads].double().numpy(),
+                                    w.rope_theta, w.causal)
+    check("dq", dq[bsl, :, heads], rq, f"{name} row 1")
+    check("dk", dk[bsl, :, kv], rk, f"{name} row 1")
+    check("dv", dv[bsl, :, kv], rv, f"{name} row 1")
+
+
 def test_bwd_deterministic():
     w = w_of(2, 150, 8, 2, 128, True, seed=77)
     q, k, v = make_inputs(w)
