@@ -61,7 +61,9 @@ extern "C" {
                                   rope_theta not finite or <= 0, rope_style or causal not
                                   0/1 */
 #define ATTN_EUNSUPPORTED (-2) /* head_dim not supported by the call (see each call), unknown
-                                  dtype, sizes too large */
+                                  dtype, sizes too large (among them S above 2^28, or S rounded
+                                  up to 64 times head_dim times 2 bytes at or above 2^31: one
+                                  head's run of prepared tiles must fit 32-bit offsets) */
 #define ATTN_EHIP (-3)         /* the HIP runtime rejected an event record or kernel launch */
 #define ATTN_EWORKSPACE (-4)   /* workspace pointer null while needed, or workspace too small */
 #define ATTN_ESCRATCH (-5)     /* attn_fwd_noalloc: the call needs more than the library's

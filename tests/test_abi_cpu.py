@@ -104,13 +104,14 @@ def test_invalid_arguments(over):
 
 @pytest.mark.parametrize("over", [
     dict(d=96), dict(d=512), dict(d=256, dtype=1), dict(d=32), dict(d=0), dict(dtype=2), dict(dtype=-1),
-    dict(S=(1 << 28) + 1), dict(d=256, S=(1 << 22) + 1),
+    dict(S=(1 << 28) + 1), dict(d=256, S=(1 << 22) + 1), dict(d=128, S=(1 << 23) - 63), dict(d=64, S=(1 << 24) - 63),
 ])
 def test_unsupported(over):
     assert call(**over) == _lib.ATTN_EUNSUPPORTED
 
 
-@pytest.mark.parametrize("over", [dict(ws=None), dict(wsb=1024), dict(ws=P + 8)])
+@pytest.mark.parametrize("over", [dict(ws=None), dict(wsb=1024), dict(ws=P + 8),
+                                  dict(d=128, S=(1 << 23) - 64)])  # (the longest run 32-bit offsets allow)
 def test_workspace_rejected(over):
     assert call(**over) == _lib.ATTN_EWORKSPACE
 

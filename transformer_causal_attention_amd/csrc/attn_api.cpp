@@ -95,6 +95,9 @@ int check_shape(int B, int S, int Hq, int Hkv, int d, double rope_theta, int cau
   // index arithmetic in the kernels: row/key positions in int, offsets in size_t,
   // workgroup counts below 2^31
   if (S > (1 << 28)) return ATTN_EUNSUPPORTED;
+  // the kernels address one (b, head) run of prepared tiles (S padded to 64 keys, d bf16 per
+  // key) with 32-bit buffer offsets
+  if ((double)padded_len(S) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
   if ((double)Hkv * d > (double)(1 << 24)) return ATTN_EUNSUPPORTED;  // 32-bit offsets within a 64-key tile
   const double elems = (double)B * S * Hq * d;
   if (elems > 4.0e15) return ATTN_EUNSUPPORTED;
@@ -241,8 +244,6 @@ int fwd_impl(const void *q, const void *k, const void *v, int B, int S, int Hq, 
   if (!rope_style_ok(rope_style)) return ATTN_EINVAL;
   const int rc = check_shape(B, S, Hq, Hkv, d, rope_theta, causal, dtype);
   if (rc != ATTN_OK) return rc;
-  // head_dim 256 addresses one (b, K/V head) run of prepared tiles with 32-bit offsets
-  if (d == 256 && (double)padded_len(S) * d * 2 >= 2147483647.0) return ATTN_EUNSUPPORTED;
   const size_t need = attn_fwd_workspace_bytes(B, S, Hkv, d, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_EWORKSPACE;
 
