@@ -60,3 +60,23 @@ def test_cpu_baseline_record():
     assert r["host_cores"] == len(os.sched_getaffinity(0))
     assert r["value"] > 0 and r["seconds"] >= 0.4
     assert "whole passes" in r["sample"] and "tiny" in r["sample"]
+
+
+def test_bench_counts():
+    """The benchmark's algorithmic counts: 2 B Hq S^2 d FLOPs for a causal call (4 B Hq S^2 d
+    without the mask), 4 d FLOPs per visible (row, key) pair for sampled rows (counted by brute
+    force here), and q, k, v, out in bf16 plus an fp32 lse for the bytes."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from transformer_causal_attention_amd.workloads import WORKLOADS, Workload
+
+    w = WORKLOADS["llama3_8b"]
+    assert bench.flops(w) == 2 * 1 * 32 * 2048 * 2048 * 128
+    assert bench.algorithmic_bytes(w) == (2 * 2048 * 32 * 128 + 2 * 2048 * 8 * 128) * 2 + 4 * 32 * 2048
+    t = Workload("t", 2, 37, 6, 3, 64, "bf16", 1.0, 10000.0, True, 1)
+    rows = [0, 5, 36]
+    pairs = sum(1 for i in rows for j in range(t.S) if j <= i)
+    assert bench.flops(t, rows) == 4 * t.d * pairs * t.B * t.Hq
+    tf = Workload("t", 2, 37, 6, 3, 64, "bf16", 1.0, 10000.0, False, 1)
+    assert bench.flops(tf) == 4 * 2 * 6 * 37 * 37 * 64
+    assert bench.flops(tf, rows) == 4 * tf.d * len(rows) * tf.S * tf.B * tf.Hq
