@@ -1168,12 +1168,13 @@ hipError_t launch_bwd(const BwdParams &p, const RopeTable &tab, hipStream_t stre
     if ((err = launch_bwd_d256_main(p, tab, stream)) != hipSuccess) return err;
   } else {
     // The per-wave kernels (diagnostics) take work items of single blocks, heaviest first,
-    // instead of balanced pairs: for dq when the pairs would leave SIMDs idle, when the key range is long (the waves of one round then sweep
-    // nearby key blocks and share them in L2) or when every K/V head serves one query head; for
-    // the per-head dk/dv kernel (ATTN_BWD_KV=waves) in that last case only.  (Measured on the
-    // workloads: single dq blocks 17% faster on PaLM MQA, 13% on SmolLM MHA, 31% on the 32K
-    // shard, 6% slower on Llama-3-8B; single dk/dv blocks 10-19% faster on SmolLM MHA, 5-24%
-    // slower on Llama-3-8B and PaLM MQA.)
+    // instead of balanced pairs: for dq when the pairs would leave SIMDs idle, when the key
+    // range is long (the waves of one round then sweep nearby key blocks and share them in L2)
+    // or when every K/V head serves one query head; for the per-head dk/dv kernel
+    // (ATTN_BWD_KV=waves) in that last case only.  (Measured on the workloads: single dq blocks
+    // 17% faster on PaLM MQA, 13% on SmolLM MHA, 31% on the 32K shard, 6% slower on
+    // Llama-3-8B; single dk/dv blocks 10-19% faster on SmolLM MHA, 5-24% slower on Llama-3-8B
+    // and PaLM MQA.)
     bool single_kv = p.G == 1;
     bool single_q = p.G == 1 || p.NB > 64 || (long long)p.B * p.Hq * p.n_pairs < bwd_dq_capacity<D>();
     // diagnostic: ATTN_BWD_ITEMS=pairs or =single forces one kind for every kernel (both give
